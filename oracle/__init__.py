@@ -1,0 +1,192 @@
+"""fp64 CPU oracle for HSTU attention -- test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product path (the HIP library and its Python binding) never
+does, and this package imports nothing from it.
+
+The arithmetic lives in ``hstu_oracle.c`` (plain C, fp64, libm ``exp``, gcc
+``-O2`` without fast-math, OpenMP over independent output rows).  This module
+only builds and loads that file and marshals numpy arrays into it.  bf16 inputs
+are widened exactly to fp64 here (``widen``); the score scale is passed as the
+fp64 widening of the fp32 value the GPU receives.
+
+Every function takes packed ``(T, H, D)`` arrays and int32 cumulative offsets
+(HSTU Attention page, "Tensor layout") and returns fp64 arrays of the requested
+rows.  ``rows=None`` computes every row.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hstu_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_hstu.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``hstu_oracle.c`` with gcc into ``liboracle_hstu.so``."""
+    global _lib
+    with _lock:
+        if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            tmp = _LIB + f".tmp{os.getpid()}"
+            cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+            subprocess.run(cmd, check=True)
+            os.replace(tmp, _LIB)
+            _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=False)
+        with _lock:
+            lib = ctypes.CDLL(_LIB)
+            i64, i32p, f64p, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), \
+                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+            lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_hstu_fwd.restype = ctypes.c_int
+            lib.oracle_hstu_fwd.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p,
+                                            ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                            i64p, i64, f64p]
+            lib.oracle_hstu_bwd_dq.restype = ctypes.c_int
+            lib.oracle_hstu_bwd_dq.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
+                                               ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                               i64p, i64, f64p]
+            lib.oracle_hstu_bwd_dkdv.restype = ctypes.c_int
+            lib.oracle_hstu_bwd_dkdv.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
+                                                 ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                                 i64p, i64, f64p, f64p]
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on (OMP_NUM_THREADS, else the core count)."""
+    return int(_load().oracle_num_threads())
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of bf16 bit patterns (uint16)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _f64(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint16:
+        return widen(x)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _prep(cu_q, cu_k, q, k, v, rows, total):
+    cu_q = np.ascontiguousarray(cu_q, dtype=np.int32)
+    cu_k = np.ascontiguousarray(cu_k, dtype=np.int32)
+    if cu_q.shape != cu_k.shape or cu_q.ndim != 1 or cu_q.size < 1:
+        raise ValueError("cu_seqlens_q/k must be 1-D of equal length B+1")
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q/k/v must be (T, H, D) with matching H, D")
+    if rows is None:
+        rows_arr = None
+        n = total
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows_arr.size
+        if n and (rows_arr.min() < 0 or rows_arr.max() >= total):
+            raise ValueError("requested row out of range")
+    return cu_q, cu_k, q, k, v, rows_arr, n
+
+
+def fwd(cu_q, cu_k, q, k, v, alpha, scaling_seqlen, causal: bool,
+        rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """O rows (fp64, shape (n, H, D)) of HSTU attention."""
+    cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, q.shape[0])
+    H, D = q.shape[1], q.shape[2]
+    out = np.empty((n, H, D), dtype=np.float64)
+    rc = _load().oracle_hstu_fwd(
+        cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
+        _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+        float(alpha), float(scaling_seqlen), int(bool(causal)),
+        None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
+        _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle: a row lies outside every sequence")
+    return out
+
+
+def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
+           rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """dQ rows (fp64) given the upstream gradient ``dout``."""
+    cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, q.shape[0])
+    dout = _f64(dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    H, D = q.shape[1], q.shape[2]
+    out = np.empty((n, H, D), dtype=np.float64)
+    rc = _load().oracle_hstu_bwd_dq(
+        cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
+        _ptr(dout, ctypes.c_double), _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), int(bool(causal)),
+        None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
+        _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle: a row lies outside every sequence")
+    return out
+
+
+def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
+             rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(dK, dV) rows (fp64) for packed key rows ``rows``."""
+    cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, k.shape[0])
+    dout = _f64(dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    H, D = q.shape[1], q.shape[2]
+    dk = np.empty((n, H, D), dtype=np.float64)
+    dv = np.empty((n, H, D), dtype=np.float64)
+    rc = _load().oracle_hstu_bwd_dkdv(
+        cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
+        _ptr(dout, ctypes.c_double), _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), int(bool(causal)),
+        None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
+        _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle: a row lies outside every sequence")
+    return dk, dv
+
+
+def fwd_workload(wl, rows=None) -> np.ndarray:
+    """Oracle O for a ``Workload`` (its bf16 inputs widened exactly)."""
+    return fwd(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.q, wl.k, wl.v,
+               float(wl.alpha), wl.scaling_seqlen, wl.causal, rows)
+
+
+def bwd_workload(wl, rows_q=None, rows_k=None):
+    """Oracle (dQ, dK, dV) for a ``Workload`` with an upstream gradient."""
+    if wl.do is None:
+        raise ValueError("workload has no upstream gradient")
+    dq = bwd_dq(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, wl.q, wl.k, wl.v,
+                float(wl.alpha), wl.scaling_seqlen, wl.causal, rows_q)
+    dk, dv = bwd_dkdv(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, wl.q, wl.k, wl.v,
+                      float(wl.alpha), wl.scaling_seqlen, wl.causal, rows_k)
+    return dq, dk, dv
+
+
+if __name__ == "__main__":  # pragma: no cover - manual build helper
+    print(build(force=True), file=sys.stderr)
