@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark: HSTU attention forward + backward on one MI355X.
+
+One step = the whole path over one batch of synthetic input: hstu_fwd,
+hstu_bwd_dq, hstu_bwd_dkdv (all three launched through the C ABI on the current
+stream).  Default workload: B=32 sequences with Zipf(1.2) lengths clipped to
+[16, 4096] (T = 23460), H=4, D=128, causal, bf16, plus an upstream gradient.
+
+Metric: useful TFLOP/s = useful flops / time, counting only visible (query,
+key) pairs P: forward 4*D*H*P, backward 10*D*H*P (five matmul-equivalents,
+including the score recompute the backward needs).  Inputs are resident in HBM
+before the timed region starts.
+
+Prints one JSON line.  `--gpus N` with N > 1 is refused: this build measures a
+single GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "zipf_b32_h4_d128_causal_fwdbwd"
+# Algorithmic flops per visible (query, key) pair and head, per unit of D:
+# forward: S (2) + A.V (2); dq kernel: S (2) + dO.V^T (2) + dS.K (2);
+# dk/dv kernel: S (2) + dO.V^T (2) + A^T.dO (2) + dS^T.Q (2).
+FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+USEFUL_PER_PAIR_D = {"fwd": 4, "bwd": 10}
+KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel"}
+
+
+def visible_pairs(lengths_q, lengths_k, causal: bool) -> int:
+    """Count of (query, key) pairs the mask keeps (top-left causal: j <= i)."""
+    total = 0
+    for lq, lk in zip(np.asarray(lengths_q, dtype=np.int64), np.asarray(lengths_k, dtype=np.int64)):
+        if causal:
+            i = np.arange(lq, dtype=np.int64)
+            total += int(np.minimum(i + 1, lk).sum())
+        else:
+            total += int(lq * lk)
+    return total
+
+
+def kernel_source_digest() -> str:
+    csrc = os.path.join(ROOT, "generative_recommender_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from the committed PMC summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != kernel_source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return int(k["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(wl, max_pairs: int):
+    """Time the fp64 oracle (fwd + bwd) on whole sequences of the workload whose
+    visible pairs add up to at most ``max_pairs`` (shortest first)."""
+    import oracle
+
+    oracle.build(force=False)
+    order = np.argsort(wl.lengths_q, kind="stable")
+    chosen, pairs = [], 0
+    for b in order:
+        p = visible_pairs([wl.lengths_q[b]], [wl.lengths_k[b]], wl.causal)
+        if pairs + p > max_pairs and chosen:
+            continue
+        chosen.append(int(b))
+        pairs += p
+    cu_q, cu_k = wl.cu_seqlens_q, wl.cu_seqlens_k
+    rows_q = np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in chosen])
+    rows_k = np.concatenate([np.arange(cu_k[b], cu_k[b + 1]) for b in chosen])
+    t0 = time.perf_counter()
+    oracle.fwd_workload(wl, rows_q)
+    if wl.do is not None:
+        oracle.bwd_workload(wl, rows_q, rows_k)
+    dt = time.perf_counter() - t0
+    per_pair = USEFUL_PER_PAIR_D["fwd"] + (USEFUL_PER_PAIR_D["bwd"] if wl.do is not None else 0)
+    flops = per_pair * wl.head_dim * wl.num_heads * pairs
+    lens = sorted(int(wl.lengths_q[b]) for b in chosen)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle fwd+bwd on {len(chosen)} of {wl.batch} sequences (lengths {lens[0]}..{lens[-1]}, "
+                   f"{pairs} visible pairs x {wl.num_heads} heads = {pairs / visible_pairs(wl.lengths_q, wl.lengths_k, wl.causal):.1%} "
+                   f"of the workload's pairs), {dt:.1f} s"),
+        "seconds": dt,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-max-pairs", type=int, default=10_000_000,
+                    help="bound on the oracle sample (visible pairs per head)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (PMC byte-counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+                                   "(every (sequence, head) pair is independent; see the sharding design notes)"}))
+        return 2
+
+    import torch
+
+    from generative_recommender_attention_amd import hstu
+    from generative_recommender_attention_amd.workloads import named_workload
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": 5}))
+        return 0
+
+    lib = hstu.library()
+    del lib
+    wl = named_workload(args.workload)
+    print(f"[bench] workload {wl.name}: B={wl.batch} T={wl.total_q} H={wl.num_heads} D={wl.head_dim} "
+          f"causal={wl.causal}", file=sys.stderr, flush=True)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = to_dev(wl.q), to_dev(wl.k), to_dev(wl.v)
+    has_bwd = wl.do is not None
+    do = to_dev(wl.do) if has_bwd else None
+    cu_q = torch.from_numpy(wl.cu_seqlens_q).to(dev)
+    cu_k = torch.from_numpy(wl.cu_seqlens_k).to(dev)
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    kw = dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, alpha=float(wl.alpha),
+              scaling_seqlen=wl.scaling_seqlen, causal=wl.causal)
+    stream = torch.cuda.current_stream(dev)
+    kernels = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if has_bwd else [])
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        hstu.hstu_fwd(q, k, v, cu_q, cu_k, out=o, stream=stream, **kw)
+        if events is not None:
+            events[1].record(stream)
+        if has_bwd:
+            hstu.hstu_bwd_dq(do, q, k, v, cu_q, cu_k, dq=dq, stream=stream, **kw)
+            if events is not None:
+                events[2].record(stream)
+            hstu.hstu_bwd_dkdv(do, q, k, v, cu_q, cu_k, dk=dk, dv=dv, stream=stream, **kw)
+            if events is not None:
+                events[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()  # barrier: one rank
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    per_kernel_ms = {}
+    for i, name in enumerate(kernels):
+        per_kernel_ms[name] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    pairs = visible_pairs(wl.lengths_q, wl.lengths_k, wl.causal)
+    unit_pd = wl.head_dim * wl.num_heads * pairs
+    useful = USEFUL_PER_PAIR_D["fwd"] * unit_pd + (USEFUL_PER_PAIR_D["bwd"] * unit_pd if has_bwd else 0)
+    value = useful / (ms_per_step * 1e-3) / 1e12
+
+    dominant = max(per_kernel_ms, key=per_kernel_ms.get)
+    alg_flops = FLOPS_PER_PAIR_D[dominant] * unit_pd
+    achieved = alg_flops / (per_kernel_ms[dominant] * 1e-3) / 1e12
+    traffic = load_traffic(KERNEL_SYMBOL[dominant])
+
+    detail = {}
+    for name in kernels:
+        f = FLOPS_PER_PAIR_D[name] * unit_pd
+        tf = f / (per_kernel_ms[name] * 1e-3) / 1e12
+        detail[name] = {"ms": round(per_kernel_ms[name], 5), "alg_tflops": round(tf, 2),
+                        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    fwd_useful_tf = USEFUL_PER_PAIR_D["fwd"] * unit_pd / (per_kernel_ms["fwd"] * 1e-3) / 1e12
+    result = {
+        "metric": "HSTU attn fwd/bwd useful TFLOP/s @H=4,D=128 causal jagged; % of BF16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "total_tokens": wl.total_q,
+                   "heads": wl.num_heads, "head_dim": wl.head_dim, "mask": "causal" if wl.causal else "none",
+                   "max_seqlen": wl.max_seqlen_q, "visible_pairs_per_head": pairs,
+                   "useful_flops_per_step": useful, "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_useful_tflops": round(fwd_useful_tf, 2),
+        "fwd_frac_of_peak": round(fwd_useful_tf / PEAK_BF16_TFLOPS, 4),
+        "kernels": detail,
+        "roofline": {"bound": "mfma", "kernel": KERNEL_SYMBOL[dominant], "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "alg_flops_per_launch": alg_flops,
+                     "avg_launch_ms": round(per_kernel_ms[dominant], 5)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_max_pairs)
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
+                        "gcn_arch": getattr(props, "gcnArchName", "")}
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,236 @@
+// C ABI of libhstu: host-side validation and dispatch.  Declarations and the
+// full contract are in include/hstu.h.  Nothing here reads device memory,
+// synchronises or allocates; every check is on scalars and pointer values.
+#include "hstu.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hstu_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hstu_status_t fail(hstu_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+hstu_status_t ok() {
+    g_last_error.clear();
+    return HSTU_OK;
+}
+
+// A tensor operand after stride resolution.
+struct Operand {
+    const char* name;
+    const void* ptr;
+    hstu_stride_t stride;
+    int64_t rows;  // T of this tensor
+};
+
+hstu_status_t check_operand(const hstu_args_t& a, Operand& t) {
+    const int64_t H = a.num_heads, D = a.head_dim;
+    if (t.stride.token == 0 && t.stride.head == 0) t.stride = hstu_stride_t{H * D, D};
+    if (t.rows == 0) return HSTU_OK;  // nothing is read or written through it
+    if (t.ptr == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "%s is null", t.name);
+    if (reinterpret_cast<uintptr_t>(t.ptr) % 16 != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", t.name);
+    const int64_t st = t.stride.token, sh = t.stride.head;
+    if (st <= 0 || sh <= 0 || st % 8 != 0 || sh % 8 != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT,
+                    "%s strides (token %lld, head %lld) must be positive multiples of 8 elements", t.name,
+                    (long long)st, (long long)sh);
+    // Non-aliasing: either heads nest inside tokens or tokens nest inside heads.
+    const bool token_major = sh >= D && (H == 1 || st >= sh * H);
+    const bool head_major = st >= D && (t.rows == 1 || sh >= st * t.rows);
+    if (!token_major && !head_major)
+        return fail(HSTU_ERR_INVALID_ARGUMENT,
+                    "%s strides (token %lld, head %lld) map two elements to one address", t.name,
+                    (long long)st, (long long)sh);
+    return HSTU_OK;
+}
+
+// Scalar checks common to every entry point; fills the kernel parameter block.
+hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int32_t* cu_k, hstu::AttnParams& p) {
+    if (a == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args is null");
+    if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+        return fail(HSTU_ERR_UNSUPPORTED, "head_dim %d is not one of 16, 32, 64, 128", a->head_dim);
+    if (a->mask != HSTU_MASK_NONE && a->mask != HSTU_MASK_CAUSAL)
+        return fail(HSTU_ERR_UNSUPPORTED, "mask %d is not HSTU_MASK_NONE or HSTU_MASK_CAUSAL", a->mask);
+    if (a->batch < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "batch %d < 1", a->batch);
+    if (a->num_heads < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_heads %d < 1", a->num_heads);
+    if (a->total_q < 0 || a->total_k < 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "negative total (total_q %d, total_k %d)", a->total_q, a->total_k);
+    if (a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "negative max_seqlen (q %d, k %d)", a->max_seqlen_q,
+                    a->max_seqlen_k);
+    if (a->max_seqlen_q > a->max_seqlen_k)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "max_seqlen_q %d > max_seqlen_k %d", a->max_seqlen_q,
+                    a->max_seqlen_k);
+    if (a->max_seqlen_q > a->total_q || a->max_seqlen_k > a->total_k)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "max_seqlen exceeds the total token count");
+    if (!std::isfinite(a->alpha)) return fail(HSTU_ERR_INVALID_ARGUMENT, "alpha is not finite");
+    if (a->scaling_seqlen < 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "scaling_seqlen %d < 0", a->scaling_seqlen);
+    const int32_t ls = a->scaling_seqlen == 0 ? a->max_seqlen_q : a->scaling_seqlen;
+    if (ls < 1 && a->total_q > 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "scaling_seqlen resolves to %d; it must be positive", ls);
+    if (cu_q == nullptr || cu_k == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "cu_seqlens pointer is null");
+    if (reinterpret_cast<uintptr_t>(cu_q) % 4 != 0 || reinterpret_cast<uintptr_t>(cu_k) % 4 != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "cu_seqlens pointer is not 4-byte aligned");
+
+    std::memset(&p, 0, sizeof(p));
+    p.cu_q = cu_q;
+    p.cu_k = cu_k;
+    p.batch = a->batch;
+    p.heads = a->num_heads;
+    p.alpha = a->alpha;
+    p.exp_c = -a->alpha * 1.4426950408889634f;
+    p.out_scale = ls >= 1 ? a->alpha / (float)ls : 0.0f;
+    return HSTU_OK;
+}
+
+hstu::TensorRef ref(const Operand& t) {
+    return hstu::TensorRef{static_cast<const uint16_t*>(t.ptr), t.stride.token, t.stride.head};
+}
+hstu::TensorOut out(const Operand& t) {
+    return hstu::TensorOut{static_cast<uint16_t*>(const_cast<void*>(t.ptr)), t.stride.token, t.stride.head};
+}
+
+hstu_status_t set_grid(hstu::AttnParams& p, int32_t max_len, int block) {
+    const int64_t nblk = ((int64_t)max_len + block - 1) / block;
+    const int64_t grid = nblk * p.batch * p.heads;
+    if (grid > 0x7fffffffLL)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "problem too large: %lld workgroups", (long long)grid);
+    p.nblk = (int32_t)nblk;
+    return HSTU_OK;
+}
+
+hstu_status_t launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(HSTU_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                     const int32_t* cu_q, const int32_t* cu_k, void* dq, hipStream_t stream) {
+    hstu::AttnParams p;
+    hstu_status_t st = check_common(a, cu_q, cu_k, p);
+    if (st != HSTU_OK) return st;
+    Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q}, {"k", k, a->k, a->total_k},
+                     {"v", v, a->v, a->total_k},          {"dq", dq, a->dq, a->total_q}};
+    for (Operand& o : ops)
+        if ((st = check_operand(*a, o)) != HSTU_OK) return st;
+    p.dout = ref(ops[0]);
+    p.q = ref(ops[1]);
+    p.k = ref(ops[2]);
+    p.v = ref(ops[3]);
+    p.dq = out(ops[4]);
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if (a->total_q == 0) return ok();
+    return launched(hstu::launch_bwd_dq(p, a->head_dim, a->mask == HSTU_MASK_CAUSAL, stream), "hstu_bwd_dq");
+}
+
+hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                       const int32_t* cu_q, const int32_t* cu_k, void* dk, void* dv, hipStream_t stream) {
+    hstu::AttnParams p;
+    hstu_status_t st = check_common(a, cu_q, cu_k, p);
+    if (st != HSTU_OK) return st;
+    Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q},
+                     {"k", k, a->k, a->total_k},          {"v", v, a->v, a->total_k},
+                     {"dk", dk, a->dk, a->total_k},       {"dv", dv, a->dv, a->total_k}};
+    for (Operand& o : ops)
+        if ((st = check_operand(*a, o)) != HSTU_OK) return st;
+    if (a->total_k > 0 && dk == dv) return fail(HSTU_ERR_INVALID_ARGUMENT, "dk and dv are the same buffer");
+    p.dout = ref(ops[0]);
+    p.q = ref(ops[1]);
+    p.k = ref(ops[2]);
+    p.v = ref(ops[3]);
+    p.dk = out(ops[4]);
+    p.dv = out(ops[5]);
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN)) != HSTU_OK) return st;
+    if (a->total_k == 0) return ok();
+    return launched(hstu::launch_bwd_dkdv(p, a->head_dim, a->mask == HSTU_MASK_CAUSAL, stream),
+                    "hstu_bwd_dkdv");
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_fwd(const hstu_args_t* a, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o, hipStream_t stream) {
+    hstu::AttnParams p;
+    hstu_status_t st = check_common(a, cu_seqlens_q, cu_seqlens_k, p);
+    if (st != HSTU_OK) return st;
+    Operand ops[] = {{"q", q, a->q, a->total_q},
+                     {"k", k, a->k, a->total_k},
+                     {"v", v, a->v, a->total_k},
+                     {"o", o, a->o, a->total_q}};
+    for (Operand& op : ops)
+        if ((st = check_operand(*a, op)) != HSTU_OK) return st;
+    p.q = ref(ops[0]);
+    p.k = ref(ops[1]);
+    p.v = ref(ops[2]);
+    p.o = out(ops[3]);
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if (a->total_q == 0) return ok();
+    return launched(hstu::launch_fwd(p, a->head_dim, a->mask == HSTU_MASK_CAUSAL, stream), "hstu_fwd");
+}
+
+hstu_status_t hstu_bwd_dq(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, hipStream_t stream) {
+    return run_dq(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dq, stream);
+}
+
+hstu_status_t hstu_bwd_dkdv(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dk, void* dv,
+                            hipStream_t stream) {
+    return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream);
+}
+
+hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                       hipStream_t stream) {
+    // Validate both halves before enqueueing either, so a failure enqueues nothing.
+    hstu::AttnParams p;
+    hstu_status_t st = check_common(a, cu_seqlens_q, cu_seqlens_k, p);
+    if (st != HSTU_OK) return st;
+    Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q},
+                     {"k", k, a->k, a->total_k},          {"v", v, a->v, a->total_k},
+                     {"dq", dq, a->dq, a->total_q},       {"dk", dk, a->dk, a->total_k},
+                     {"dv", dv, a->dv, a->total_k}};
+    for (Operand& o : ops)
+        if ((st = check_operand(*a, o)) != HSTU_OK) return st;
+    if (a->total_k > 0 && dk == dv) return fail(HSTU_ERR_INVALID_ARGUMENT, "dk and dv are the same buffer");
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN)) != HSTU_OK) return st;
+    st = run_dq(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dq, stream);
+    if (st != HSTU_OK) return st;
+    return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream);
+}
+
+const char* hstu_last_error(void) { return g_last_error.c_str(); }
+
+const char* hstu_status_string(hstu_status_t s) {
+    switch (s) {
+        case HSTU_OK: return "HSTU_OK";
+        case HSTU_ERR_INVALID_ARGUMENT: return "HSTU_ERR_INVALID_ARGUMENT";
+        case HSTU_ERR_UNSUPPORTED: return "HSTU_ERR_UNSUPPORTED";
+        case HSTU_ERR_DEVICE: return "HSTU_ERR_DEVICE";
+    }
+    return "HSTU_ERR_UNKNOWN";
+}
+
+int hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+}  // extern "C"

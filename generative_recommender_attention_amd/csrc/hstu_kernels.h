@@ -1,0 +1,33 @@
+// Launch-side view of the HSTU attention kernels: the parameter block every
+// kernel takes and the per-direction launchers the C ABI calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hstu_device.h"
+
+namespace hstu {
+
+struct AttnParams {
+    const int32_t* cu_q;   // (B + 1) cumulative query lengths, device
+    const int32_t* cu_k;   // (B + 1) cumulative key lengths, device
+    int32_t batch;         // B
+    int32_t heads;         // H
+    int32_t nblk;          // row (or key) blocks per sequence covered by the grid
+    float alpha;           // score scale
+    float exp_c;           // -alpha * log2(e), for sig(alpha x) = 1 / (1 + 2^(x exp_c))
+    float out_scale;       // alpha / L_scale: the epilogue factor of O, dQ, dK and dV
+    TensorRef q, k, v, dout;
+    TensorOut o, dq, dk, dv;
+};
+
+// Tile shapes (rows per workgroup) used to size the grids.
+constexpr int kFwdBlockM = 128;   // query rows per forward / dQ workgroup
+constexpr int kBwdBlockN = 128;   // key rows per dK/dV workgroup
+
+hipError_t launch_fwd(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
+
+}  // namespace hstu

@@ -1,0 +1,279 @@
+"""Python binding of libhstu (HSTU attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libhstu.so``.  PyTorch supplies device memory and the current
+stream.  The functions mirror the HSTU Attention page's allocating functions
+("High-level functions"): ``hstu_fwd`` returns the packed output, ``hstu_bwd``
+returns (dq, dk, dv); caller-owned outputs may be passed in and are
+overwritten.  ``causal=True`` is the page's ``window_size=(-1, 0)`` and
+``causal=False`` its ``(-1, -1)``.  There is no fallback: if the library is
+missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "HstuError",
+    "HstuArgs",
+    "HstuStride",
+    "library",
+    "library_path",
+    "hstu_fwd",
+    "hstu_bwd",
+    "hstu_bwd_dq",
+    "hstu_bwd_dkdv",
+    "HSTU_OK",
+    "HSTU_ERR_INVALID_ARGUMENT",
+    "HSTU_ERR_UNSUPPORTED",
+    "HSTU_ERR_DEVICE",
+    "HSTU_MASK_NONE",
+    "HSTU_MASK_CAUSAL",
+]
+
+HSTU_OK = 0
+HSTU_ERR_INVALID_ARGUMENT = 1
+HSTU_ERR_UNSUPPORTED = 2
+HSTU_ERR_DEVICE = 3
+HSTU_MASK_NONE = 0
+HSTU_MASK_CAUSAL = 1
+ABI_VERSION = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libhstu.so")
+
+
+class HstuStride(ctypes.Structure):
+    _fields_ = [("token", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+class HstuArgs(ctypes.Structure):
+    """Mirror of ``hstu_args_t`` in include/hstu.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("scaling_seqlen", ctypes.c_int32),
+        ("mask", ctypes.c_int32),
+        ("q", HstuStride),
+        ("k", HstuStride),
+        ("v", HstuStride),
+        ("o", HstuStride),
+        ("dout", HstuStride),
+        ("dq", HstuStride),
+        ("dk", HstuStride),
+        ("dv", HstuStride),
+    ]
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    return {0: "HSTU_OK", 1: "HSTU_ERR_INVALID_ARGUMENT", 2: "HSTU_ERR_UNSUPPORTED",
+            3: "HSTU_ERR_DEVICE"}.get(s, f"status {s}")
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libhstu.so`` (built in-tree); raise if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"libhstu.so not found at {path}; build it with "
+                    "`python -m generative_recommender_attention_amd.build` (there is no fallback)")
+            lib = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            argp = ctypes.POINTER(HstuArgs)
+            lib.hstu_fwd.restype = ctypes.c_int
+            lib.hstu_fwd.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_bwd.restype = ctypes.c_int
+            lib.hstu_bwd.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_bwd_dq.restype = ctypes.c_int
+            lib.hstu_bwd_dq.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_bwd_dkdv.restype = ctypes.c_int
+            lib.hstu_bwd_dkdv.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_last_error.restype = ctypes.c_char_p
+            lib.hstu_last_error.argtypes = []
+            lib.hstu_status_string.restype = ctypes.c_char_p
+            lib.hstu_status_string.argtypes = [ctypes.c_int]
+            lib.hstu_abi_version.restype = ctypes.c_int
+            lib.hstu_abi_version.argtypes = []
+            if lib.hstu_abi_version() != ABI_VERSION:
+                raise RuntimeError(f"libhstu ABI {lib.hstu_abi_version()} != binding ABI {ABI_VERSION}")
+            _lib = lib
+        return _lib
+
+
+def _check(status: int) -> None:
+    if status == HSTU_OK:
+        return
+    msg = library().hstu_last_error().decode(errors="replace")
+    if status == HSTU_ERR_UNSUPPORTED:
+        raise NotImplementedError(f"{_status_name(status)}: {msg}")
+    raise HstuError(status, msg)
+
+
+def _thd(name: str, t: torch.Tensor, rows: Optional[int], H: int, D: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dim() != 3 or t.shape[1] != H or t.shape[2] != D or (rows is not None and t.shape[0] != rows):
+        want = f"({rows if rows is not None else 'T'}, {H}, {D})"
+        raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    if t.shape[0] > 0 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+
+
+def _stride(t: torch.Tensor) -> HstuStride:
+    return HstuStride(t.stride(0), t.stride(1))
+
+
+def _cu(name: str, t: torch.Tensor, device: torch.device) -> int:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1:
+        raise TypeError(f"{name} must be a 1-D int32 tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal) -> HstuArgs:
+    a = HstuArgs()
+    a.batch = int(cu_q.shape[0]) - 1
+    a.total_q = int(q.shape[0])
+    a.total_k = int(k.shape[0])
+    a.num_heads = int(q.shape[1])
+    a.head_dim = int(q.shape[2])
+    a.max_seqlen_q = int(max_seqlen_q)
+    a.max_seqlen_k = int(max_seqlen_k)
+    a.alpha = float(alpha)
+    a.scaling_seqlen = 0 if scaling_seqlen is None else int(scaling_seqlen)
+    a.mask = HSTU_MASK_CAUSAL if causal else HSTU_MASK_NONE
+    if scaling_seqlen is not None and int(scaling_seqlen) <= 0:
+        raise ValueError("scaling_seqlen must be positive")
+    return a
+
+
+def _inputs(q, k, v, cu_q, cu_k):
+    if q.dim() != 3:
+        raise ValueError("q must be (T_q, H, D)")
+    H, D = int(q.shape[1]), int(q.shape[2])
+    _thd("q", q, None, H, D)
+    _thd("k", k, None, H, D)
+    _thd("v", v, int(k.shape[0]), H, D)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
+    pq, pk = _cu("cu_seqlens_q", cu_q, q.device), _cu("cu_seqlens_k", cu_k, q.device)
+    if cu_q.shape != cu_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries")
+    return H, D, pq, pk
+
+
+def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+             max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
+             scaling_seqlen: Optional[int] = None, causal: bool = True,
+             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """O = HSTU(q, k, v) on packed (T, H, D) bf16 tensors; returns ``out``."""
+    H, D, pq, pk = _inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _thd("out", out, int(q.shape[0]), H, D)
+    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal)
+    a.q, a.k, a.v, a.o = _stride(q), _stride(k), _stride(v), _stride(out)
+    _check(library().hstu_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(), pq, pk,
+                              out.data_ptr(), _stream(stream, q.device)))
+    return out
+
+
+def _bwd_common(dout, q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal):
+    H, D, pq, pk = _inputs(q, k, v, cu_q, cu_k)
+    _thd("dout", dout, int(q.shape[0]), H, D)
+    a = _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal)
+    a.q, a.k, a.v, a.dout = _stride(q), _stride(k), _stride(v), _stride(dout)
+    return H, D, pq, pk, a
+
+
+def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+             max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
+             scaling_seqlen: Optional[int] = None, causal: bool = True,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, stream=None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``."""
+    H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, alpha, scaling_seqlen, causal)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _thd("dq", dq, int(q.shape[0]), H, D)
+    _thd("dk", dk, int(k.shape[0]), H, D)
+    _thd("dv", dv, int(k.shape[0]), H, D)
+    a.dq, a.dk, a.dv = _stride(dq), _stride(dk), _stride(dv)
+    _check(library().hstu_bwd(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              _stream(stream, q.device)))
+    return dq, dk, dv
+
+
+def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                alpha=1.0, scaling_seqlen=None, causal=True, dq=None, stream=None) -> torch.Tensor:
+    """dq only (the query-major backward kernel)."""
+    H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, alpha, scaling_seqlen, causal)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    _thd("dq", dq, int(q.shape[0]), H, D)
+    a.dq = _stride(dq)
+    _check(library().hstu_bwd_dq(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                 v.data_ptr(), pq, pk, dq.data_ptr(), _stream(stream, q.device)))
+    return dq
+
+
+def hstu_bwd_dkdv(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None):
+    """(dk, dv) only (the key-major backward kernel)."""
+    H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, alpha, scaling_seqlen, causal)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _thd("dk", dk, int(k.shape[0]), H, D)
+    _thd("dv", dv, int(k.shape[0]), H, D)
+    a.dk, a.dv = _stride(dk), _stride(dv)
+    _check(library().hstu_bwd_dkdv(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(),
+                                   _stream(stream, q.device)))
+    return dk, dv

@@ -1,0 +1,165 @@
+/*
+ * libhstu -- HSTU attention over packed variable-length sequences, for AMD
+ * MI355X (gfx950).  C ABI.
+ *
+ * The operation (HSTU Attention page, "Overview", the four displayed equations):
+ * for every packed sequence b and head h,
+ *
+ *     S = alpha * Q K^T,    A = (M (.) SiLU(S)) / L_scale,    O = A V,
+ *
+ * with SiLU(s) = s / (1 + exp(-s)), no softmax and no row normalisation, and the
+ * heads concatenated.  M is the attention mask inside one sequence; no token
+ * ever attends across sequences.  L_scale ("scaling_seqlen") is one positive
+ * scalar for the whole call, not a per-sequence token count.
+ *
+ * Backward (same page, "High-level functions": the backward takes the upstream
+ * gradient dO and q, k, v only -- no saved output or statistics -- so the scores
+ * are recomputed), by the chain rule on the definition above:
+ *
+ *     dV = A^T dO
+ *     dS = (dO V^T) (.) M (.) SiLU'(S) / L_scale,  SiLU'(s) = sig(s)(1 + s(1 - sig(s)))
+ *     dQ = alpha dS K,     dK = alpha dS^T Q
+ *
+ * -- Tensors ("Tensor layout" table) ------------------------------------------
+ *   q, do, o, dq : (T_q, H, D) bf16        k, v, dk, dv : (T_k, H, D) bf16
+ *   cu_seqlens_q, cu_seqlens_k : (B + 1) int32, device memory, starting at 0;
+ *   sequence b owns rows [cu[b], cu[b+1]).  T_q = cu_seqlens_q[B], T_k likewise.
+ *   Every tensor pointer is a device pointer.  Element (t, h, d) of a tensor
+ *   lives at base + t * stride.token + h * stride.head + d (in elements): the
+ *   last dimension is always contiguous.  A zero stride pair selects the packed
+ *   layout (token = H * D, head = D).  Strides must be multiples of 8 elements,
+ *   must not map two elements to one address, and base pointers must be 16-byte
+ *   aligned ("Tensor layout", the alignment paragraph).  Disjoint views of one
+ *   allocation (e.g. dk and dv split from one packed KV gradient buffer) are
+ *   fine; overlap between an output and a live input is not checked.
+ *
+ * -- Masks ("Mask support" table) ---------------------------------------------
+ *   HSTU_MASK_NONE   : window (-1, -1), every key of the sequence is visible.
+ *   HSTU_MASK_CAUSAL : window (-1, 0), key j is visible to query i (both indices
+ *                      local to the sequence) iff j <= i.  The diagonal is
+ *                      aligned top-left; with equal query and key lengths this
+ *                      is the usual causal mask.
+ *
+ * -- Trust and validation ("Tensor layout", the paragraph on metadata) --------
+ *   The library checks every scalar and pointer argument on the host and never
+ *   reads cu_seqlens on the host, never synchronises and never allocates.  The
+ *   values inside cu_seqlens are trusted: they must be non-decreasing, start at
+ *   0, end at T_q / T_k, and no sequence may be longer than max_seqlen_q /
+ *   max_seqlen_k.  Breaking that contract is undefined behaviour on the device.
+ *
+ * -- Outputs --------------------------------------------------------------------
+ *   Every row r < T_q of o / dq and every row r < T_k of dk / dv is overwritten
+ *   (rows with no visible key, or keys no query sees, are written as zeros, the
+ *   page's zero-write rule for empty tiles); nothing is read from them first,
+ *   and rows past T_q / T_k are not touched.  Caller-owned outputs are the only
+ *   outputs: nothing is allocated.
+ *
+ * -- Execution ------------------------------------------------------------------
+ *   Each call validates, enqueues its kernels on `stream` (0 = the null stream)
+ *   and returns; results are ready when the stream reaches that point.  Calls
+ *   are thread-safe and keep no state between them, so they can be captured in
+ *   a HIP graph.  An asynchronous device fault shows up at the caller's next
+ *   synchronisation, not in the returned status.  Both backward kernels are
+ *   deterministic: the same inputs give bit-identical gradients.
+ *
+ * -- Errors -----------------------------------------------------------------------
+ *   Every entry point returns an hstu_status_t; on failure nothing has been
+ *   enqueued and hstu_last_error() returns a message for the calling thread.
+ *   No exception, abort or exit ever crosses this interface.
+ */
+#ifndef LIBHSTU_HSTU_H_
+#define LIBHSTU_HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSTU_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define HSTU_API __attribute__((visibility("default")))
+#else
+#define HSTU_API
+#endif
+
+typedef enum hstu_status {
+    HSTU_OK = 0,
+    HSTU_ERR_INVALID_ARGUMENT = 1, /* a scalar, pointer, stride or size breaks the contract */
+    HSTU_ERR_UNSUPPORTED = 2,      /* head_dim or mask outside what is built               */
+    HSTU_ERR_DEVICE = 3            /* the HIP runtime refused a launch                      */
+} hstu_status_t;
+
+typedef enum hstu_mask {
+    HSTU_MASK_NONE = 0,   /* window (-1, -1) */
+    HSTU_MASK_CAUSAL = 1  /* window (-1, 0), top-left aligned */
+} hstu_mask_t;
+
+/* Strides of one (T, H, D) tensor, in elements.  {0, 0} = packed. */
+typedef struct hstu_stride {
+    int64_t token;
+    int64_t head;
+} hstu_stride_t;
+
+/* Problem description shared by the forward and the backward (the page asks
+ * that both use the same alpha, scaling_seqlen, mask and sequence metadata). */
+typedef struct hstu_args {
+    int32_t batch;          /* B >= 1; cu_seqlens_q/k hold B + 1 int32 each             */
+    int32_t total_q;        /* T_q >= 0: rows of q, do, o, dq                            */
+    int32_t total_k;        /* T_k >= 0: rows of k, v, dk, dv                            */
+    int32_t num_heads;      /* H >= 1, the same for q, k and v (multi-head only)         */
+    int32_t head_dim;       /* D, one of 16, 32, 64, 128                                 */
+    int32_t max_seqlen_q;   /* host-known bound on every query length, >= 0              */
+    int32_t max_seqlen_k;   /* host-known bound on every key length, >= max_seqlen_q     */
+    float alpha;            /* score scale, finite                                        */
+    int32_t scaling_seqlen; /* L_scale > 0; 0 selects max_seqlen_q; < 0 is rejected      */
+    int32_t mask;           /* an hstu_mask_t                                             */
+    hstu_stride_t q, k, v;  /* input strides                                              */
+    hstu_stride_t o;        /* forward output                                             */
+    hstu_stride_t dout;     /* backward upstream gradient                                 */
+    hstu_stride_t dq, dk, dv; /* backward outputs                                         */
+} hstu_args_t;
+
+/* Forward: o = HSTU(q, k, v).  Reads q, k, v, cu_seqlens_q/k; writes o. */
+HSTU_API hstu_status_t hstu_fwd(const hstu_args_t* args,
+                       const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       void* o, hipStream_t stream);
+
+/* Backward, all three gradients: enqueues hstu_bwd_dq then hstu_bwd_dkdv. */
+HSTU_API hstu_status_t hstu_bwd(const hstu_args_t* args, const void* dout,
+                       const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       void* dq, void* dk, void* dv, hipStream_t stream);
+
+/* Backward, dQ only (one query-major kernel: recompute S, dS; dQ = alpha dS K). */
+HSTU_API hstu_status_t hstu_bwd_dq(const hstu_args_t* args, const void* dout,
+                          const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          void* dq, hipStream_t stream);
+
+/* Backward, dK and dV only (one key-major kernel: recompute S, dS;
+ * dV = A^T dO, dK = alpha dS^T Q). */
+HSTU_API hstu_status_t hstu_bwd_dkdv(const hstu_args_t* args, const void* dout,
+                            const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            void* dk, void* dv, hipStream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+HSTU_API const char* hstu_last_error(void);
+
+/* Short name of a status code. */
+HSTU_API const char* hstu_status_string(hstu_status_t status);
+
+/* HSTU_ABI_VERSION of the built library. */
+HSTU_API int hstu_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBHSTU_HSTU_H_ */

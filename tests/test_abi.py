@@ -1,0 +1,133 @@
+"""The C ABI on the host: the library loads, exports what include/hstu.h
+declares, and rejects every contract-breaking argument before touching a device.
+
+No test here launches anything: each call is built to fail host validation, and
+the fake device addresses used are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from generative_recommender_attention_amd import hstu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+FAKE = 0x100000  # a 16-byte-aligned address that is never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"HSTU_API\s+[\w\s\*]*?\b(hstu_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hstu.library_path()):
+        pytest.skip("libhstu.so is not built (run `python -m generative_recommender_attention_amd.build`)")
+    return hstu.library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted([
+        "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dq", "hstu_fwd",
+        "hstu_last_error", "hstu_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.hstu_abi_version() == hstu.ABI_VERSION
+    assert lib.hstu_status_string(0) == b"HSTU_OK"
+    assert lib.hstu_status_string(2) == b"HSTU_ERR_UNSUPPORTED"
+
+
+def test_struct_layout_matches_header():
+    # 7 int32 + float + 2 int32 = 40 bytes, then 8 stride pairs of 16 bytes
+    assert ctypes.sizeof(hstu.HstuArgs) == 40 + 8 * 16
+    assert hstu.HstuArgs.q.offset == 40
+    assert hstu.HstuArgs.dv.offset == 40 + 7 * 16
+
+
+def good_args(**kw):
+    a = hstu.HstuArgs()
+    a.batch, a.total_q, a.total_k, a.num_heads, a.head_dim = 2, 32, 32, 2, 64
+    a.max_seqlen_q, a.max_seqlen_k, a.alpha, a.scaling_seqlen, a.mask = 20, 20, 0.125, 0, 1
+    for k, v in kw.items():
+        if isinstance(v, tuple):
+            setattr(a, k, hstu.HstuStride(*v))
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def fwd(lib, a, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, o=FAKE):
+    return lib.hstu_fwd(ctypes.byref(a), q, k, v, cu_q, cu_k, o, None)
+
+
+REJECT = [
+    # (description, args overrides, expected status)
+    ("head_dim 48", dict(head_dim=48), hstu.HSTU_ERR_UNSUPPORTED),
+    ("head_dim 256", dict(head_dim=256), hstu.HSTU_ERR_UNSUPPORTED),
+    ("mask 2", dict(mask=2), hstu.HSTU_ERR_UNSUPPORTED),
+    ("batch 0", dict(batch=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("heads 0", dict(num_heads=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("negative total", dict(total_q=-1), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("max_q > max_k", dict(max_seqlen_q=21), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("negative max", dict(max_seqlen_k=-3), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("max above total", dict(max_seqlen_q=40, max_seqlen_k=40), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("scaling_seqlen < 0", dict(scaling_seqlen=-1), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("scaling resolves to 0", dict(max_seqlen_q=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("alpha inf", dict(alpha=float("inf")), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("alpha nan", dict(alpha=float("nan")), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("token stride not multiple of 8", dict(q=(132, 64)), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("head stride not multiple of 8", dict(k=(128, 68)), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("aliasing strides", dict(v=(64, 64)), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("negative stride", dict(o=(-128, 64)), hstu.HSTU_ERR_INVALID_ARGUMENT),
+]
+
+
+@pytest.mark.parametrize("desc,over,want", REJECT, ids=[r[0] for r in REJECT])
+def test_scalar_rejections(lib, desc, over, want):
+    st = fwd(lib, good_args(**over))
+    assert st == want, (desc, lib.hstu_last_error())
+    assert lib.hstu_last_error() != b""
+
+
+def test_pointer_rejections(lib):
+    a = good_args()
+    assert fwd(lib, a, q=0) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert b"q is null" in lib.hstu_last_error()
+    assert fwd(lib, a, o=FAKE + 8) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert b"16-byte" in lib.hstu_last_error()
+    assert fwd(lib, a, cu_q=0) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+
+
+def test_backward_rejections(lib):
+    a = good_args()
+    # dk and dv may not be one buffer
+    st = lib.hstu_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == hstu.HSTU_ERR_INVALID_ARGUMENT and b"same buffer" in lib.hstu_last_error()
+    st = lib.hstu_bwd_dkdv(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == hstu.HSTU_ERR_INVALID_ARGUMENT
+    # missing upstream gradient
+    st = lib.hstu_bwd_dq(ctypes.byref(a), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == hstu.HSTU_ERR_INVALID_ARGUMENT and b"dout is null" in lib.hstu_last_error()
+    st = lib.hstu_bwd(ctypes.byref(good_args(head_dim=24)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      FAKE + 16, FAKE + 32, None)
+    assert st == hstu.HSTU_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    q = torch.zeros(4, 1, 16, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        hstu.hstu_fwd(q, q, q, cu, cu, 4, 4)
+    with pytest.raises(TypeError):
+        hstu.hstu_fwd(q.float(), q, q, cu, cu, 4, 4)

@@ -1,0 +1,240 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Small problems are compared element by element in full; the full-size
+workloads on rows the oracle computes one by one (every row of short
+sequences, first/last rows, rows on both sides of tile edges, random rows).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from generative_recommender_attention_amd import hstu
+from generative_recommender_attention_amd.workloads import make_workload, named_workload
+
+from hip_cases import DeviceWorkload, check_close, sample_rows, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    hstu.library()  # no fallback: a missing library fails here
+
+
+def run_fwd_check(wl, rows=None, tag=""):
+    dw = DeviceWorkload(wl)
+    say(f"hstu_fwd {wl.name}{tag}: B={wl.batch} T={wl.total_q} H={wl.num_heads} D={wl.head_dim} causal={wl.causal}")
+    o = dw.fwd()
+    torch.cuda.synchronize()
+    got = to_f64(o)
+    ref = oracle.fwd_workload(wl, rows)
+    if rows is not None:
+        got = got[rows]
+    return check_close("O", got, ref, wl.cu_seqlens_q, rows)
+
+
+def run_bwd_check(wl, rows_q=None, rows_k=None, tag=""):
+    dw = DeviceWorkload(wl)
+    say(f"hstu_bwd {wl.name}{tag}: B={wl.batch} Tq={wl.total_q} Tk={wl.total_k} H={wl.num_heads} "
+        f"D={wl.head_dim} causal={wl.causal}")
+    dq, dk, dv = dw.bwd()
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.bwd_workload(wl, rows_q, rows_k)
+    gq, gk, gv = to_f64(dq), to_f64(dk), to_f64(dv)
+    if rows_q is not None:
+        gq = gq[rows_q]
+    if rows_k is not None:
+        gk, gv = gk[rows_k], gv[rows_k]
+    return (check_close("dQ", gq, rq, wl.cu_seqlens_q, rows_q),
+            check_close("dK", gk, rk, wl.cu_seqlens_k, rows_k),
+            check_close("dV", gv, rv, wl.cu_seqlens_k, rows_k))
+
+
+# ---------------------------------------------------------------- the workloads
+def test_tiny_workload_fwd(oracle_lib):
+    run_fwd_check(named_workload("tiny_b2_h1_d16_causal"))
+
+
+def test_uniform_workload_fwd(oracle_lib):
+    run_fwd_check(named_workload("uniform_b8_h2_d64_full"))
+
+
+def test_zipf_workload_fwd_sampled(oracle_lib):
+    wl = named_workload("zipf_b32_h4_d128_causal")
+    rel, worst = run_fwd_check(wl, sample_rows(wl.cu_seqlens_q, seed=2), " (sampled rows)")
+    print(f"zipf fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
+
+
+def test_long_workload_fwd_sampled(oracle_lib):
+    wl = named_workload("long_b4_h8_d128_causal")
+    rel, worst = run_fwd_check(wl, sample_rows(wl.cu_seqlens_q, per_seq=24, seed=3), " (sampled rows)")
+    print(f"long fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
+
+
+def test_zipf_workload_fwd_bwd_sampled(oracle_lib):
+    wl = named_workload("zipf_b32_h4_d128_causal_fwdbwd")
+    rows = sample_rows(wl.cu_seqlens_q, per_seq=32, seed=4)
+    run_fwd_check(wl, rows, " (sampled rows)")
+    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    print("zipf bwd (err/max, worst per-seq):", res)
+
+
+# ------------------------------------------------------------ shapes and edges
+EDGE_LENGTHS = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 200]
+
+RANDOM_CASES = [
+    # (seed, lengths_q, lengths_k or None, H, D, causal)
+    (100, EDGE_LENGTHS, None, 2, 16, True),
+    (101, EDGE_LENGTHS, None, 2, 32, False),
+    (102, EDGE_LENGTHS, None, 1, 64, True),
+    (103, EDGE_LENGTHS, None, 2, 128, True),
+    (104, EDGE_LENGTHS, None, 2, 128, False),
+    (105, [300, 5, 0, 257], [310, 9, 4, 257], 2, 64, True),     # L_k > L_q, top-left causal
+    (106, [130, 40, 7], [100, 41, 3], 3, 32, False),            # L_k < L_q, full
+    (107, [3] * 40 + [250], None, 1, 128, True),                # many tiny sequences
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"seed{c[0]}_d{c[4]}_{'causal' if c[5] else 'full'}"
+                                                    for c in RANDOM_CASES])
+def test_random_shapes_fwd_bwd(oracle_lib, case):
+    seed, lq, lk, H, D, causal = case
+    wl = make_workload(f"edge{seed}", seed, lq, H, D, causal, 1.0, lengths_k=lk, with_do=True)
+    run_fwd_check(wl)
+    run_bwd_check(wl)
+
+
+def test_explicit_scaling_seqlen_and_alpha(oracle_lib):
+    wl = make_workload("ls", 110, [90, 33], 2, 64, True, 1.0, with_do=True, alpha=0.3, scaling_seqlen=7)
+    run_fwd_check(wl)
+    run_bwd_check(wl)
+
+
+def test_single_long_sequence_full_mask(oracle_lib):
+    wl = make_workload("single", 111, [777], 1, 128, False, 0.5, with_do=True)
+    run_fwd_check(wl)
+    run_bwd_check(wl)
+
+
+# ------------------------------------------------------------------ invariants
+def test_zero_queries_give_exact_zeros():
+    wl = make_workload("zq", 120, [70, 150], 2, 128, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    dw.q.zero_()
+    say("hstu_fwd/bwd zero queries")
+    o = dw.fwd()
+    dq, dk, dv = dw.bwd()
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+    assert torch.any(dq != 0)
+
+
+def test_alpha_folds_into_queries_bitwise():
+    wl = make_workload("alpha2", 121, [100, 31, 260], 2, 64, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    say("hstu_fwd/bwd alpha=2 vs doubled q")
+    o1 = dw.fwd(alpha=2.0)
+    g1 = dw.bwd(alpha=2.0)
+    q2 = dw.q * 2  # exact in bf16
+    o2 = hstu.hstu_fwd(q2, dw.k, dw.v, dw.cu_q, dw.cu_k, wl.max_seqlen_q, wl.max_seqlen_k, alpha=1.0,
+                       scaling_seqlen=wl.scaling_seqlen, causal=True)
+    g2 = hstu.hstu_bwd(dw.do, q2, dw.k, dw.v, dw.cu_q, dw.cu_k, wl.max_seqlen_q, wl.max_seqlen_k, alpha=1.0,
+                       scaling_seqlen=wl.scaling_seqlen, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(g1[0], g2[0] * 2)   # dQ(alpha=2, Q) = 2 dQ(alpha=1, 2Q)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+
+
+def test_outputs_written_exactly_on_real_rows():
+    """Canary: outputs start as NaN; every real row is overwritten, the guard rows past T are not."""
+    wl = make_workload("canary", 122, [5, 0, 129, 64], 2, 32, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    T, H, D, guard = wl.total_q, wl.num_heads, wl.head_dim, 40
+    nan = torch.full((T + guard, H, D), float("nan"), device="cuda", dtype=torch.bfloat16)
+    o_buf, dq_buf, dk_buf, dv_buf = (nan.clone() for _ in range(4))
+    kw = dw.kw()
+    say("canary fwd/bwd")
+    hstu.hstu_fwd(dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, out=o_buf[:T], **kw)
+    hstu.hstu_bwd(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, dq=dq_buf[:T], dk=dk_buf[:T], dv=dv_buf[:T], **kw)
+    torch.cuda.synchronize()
+    for name, buf in (("o", o_buf), ("dq", dq_buf), ("dk", dk_buf), ("dv", dv_buf)):
+        assert not torch.any(torch.isnan(buf[:T])), name
+        assert torch.all(torch.isnan(buf[T:])), name
+
+
+def test_strided_views():
+    """dk/dv split from one packed KV gradient buffer, head-major q, padded-token v."""
+    wl = make_workload("views", 123, [80, 200, 33], 2, 64, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    T, H, D = wl.total_q, wl.num_heads, wl.head_dim
+    kw = dw.kw()
+    say("strided views")
+    o_ref = dw.fwd()
+    dq_ref, dk_ref, dv_ref = dw.bwd()
+    q_hm = dw.q.permute(1, 0, 2).contiguous().permute(1, 0, 2)         # (T, H, D) view of (H, T, D)
+    v_pad = torch.zeros(T, H, D + 64, device="cuda", dtype=torch.bfloat16)
+    v_pad[:, :, :D] = dw.v
+    v_view = v_pad[:, :, :D]                                              # token stride H*(D+64)
+    kv_grad = torch.empty(T, 2, H, D, device="cuda", dtype=torch.bfloat16)
+    o = hstu.hstu_fwd(q_hm, dw.k, v_view, dw.cu_q, dw.cu_k, **kw)
+    dq, dk, dv = hstu.hstu_bwd(dw.do, q_hm, dw.k, v_view, dw.cu_q, dw.cu_k, dk=kv_grad[:, 0], dv=kv_grad[:, 1], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    assert torch.equal(dq, dq_ref) and torch.equal(kv_grad[:, 0], dk_ref) and torch.equal(kv_grad[:, 1], dv_ref)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    wl = named_workload("zipf_b32_h4_d128_causal_fwdbwd")
+    dw = DeviceWorkload(wl)
+    say("determinism: zipf fwd+bwd twice")
+    o1, g1 = dw.fwd(), dw.bwd()
+    o2, g2 = dw.fwd(), dw.bwd()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_permuting_sequences_permutes_outputs_bitwise():
+    wl = make_workload("perm", 124, [130, 7, 300, 64], 2, 128, True, with_do=True)
+    perm = [2, 0, 3, 1]
+    cu = wl.cu_seqlens_q
+    rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in perm])
+    wl_p = make_workload("perm_p", 124, [int(wl.lengths_q[b]) for b in perm], 2, 128, True, with_do=True)
+    wl_p.q, wl_p.k, wl_p.v, wl_p.do = wl.q[rows], wl.k[rows], wl.v[rows], wl.do[rows]
+    wl_p.scaling_seqlen = wl.scaling_seqlen
+    a, b = DeviceWorkload(wl), DeviceWorkload(wl_p)
+    say("permutation")
+    oa, ga = a.fwd(), a.bwd()
+    ob, gb = b.fwd(), b.bwd()
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).cuda()
+    assert torch.equal(ob, oa[idx])
+    for x, y in zip(gb, ga):
+        assert torch.equal(x, y[idx])
+
+
+def test_runs_on_caller_stream(oracle_lib):
+    wl = make_workload("stream", 125, [100, 60], 2, 64, False, with_do=True)
+    dw = DeviceWorkload(wl)
+    s = torch.cuda.Stream()
+    say("non-default stream")
+    with torch.cuda.stream(s):
+        o = dw.fwd()
+    s.synchronize()
+    check_close("O", to_f64(o), oracle.fwd_workload(wl), wl.cu_seqlens_q)
+
+
+def test_unsupported_raise():
+    wl = make_workload("unsup", 126, [10], 1, 16, True)
+    dw = DeviceWorkload(wl)
+    q48 = torch.zeros(10, 1, 48, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(NotImplementedError):
+        hstu.hstu_fwd(q48, q48, q48, dw.cu_q, dw.cu_k, 10, 10)
+    with pytest.raises(hstu.HstuError):
+        hstu.hstu_fwd(dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, 11, 10)  # max_seqlen_q > max_seqlen_k
