@@ -94,7 +94,7 @@ RANDOM_CASES = [
     (103, EDGE_LENGTHS, None, 2, 128, True),
     (104, EDGE_LENGTHS, None, 2, 128, False),
     (105, [300, 5, 0, 257], [310, 9, 4, 257], 2, 64, True),     # L_k > L_q, top-left causal
-    (106, [130, 40, 7], [100, 41, 3], 3, 32, False),            # L_k < L_q, full
+    (106, [130, 40, 7], [131, 38, 3], 3, 32, False),            # L_k < L_q in two sequences, full
     (107, [3] * 40 + [250], None, 1, 128, True),                # many tiny sequences
 ]
 
