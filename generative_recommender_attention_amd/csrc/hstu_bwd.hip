@@ -11,73 +11,81 @@
 // alpha) and fold alpha / L_scale into the final store, as the forward does.
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
-// same tile walk as the forward.  Per 64-key tile, K is staged row-major and
-// transposed and V row-major; each wave computes S^T = K Q^T and dA^T = V dO^T,
-// forms dS^T in registers and accumulates dQ^T += K^T dS^T.
+// same tile walk as the forward.  Per 64-key tile K and V are staged row-major
+// in LDS; each wave computes S^T = K Q^T and dA^T = V dO^T (A operands: K, V
+// rows), forms dS^T in registers and accumulates dQ^T += K^T dS^T (A operand:
+// K read transposed).
 //
 // dk/dv kernel: key-major, one workgroup per (128-key block, sequence, head),
 // each wave owning 32 keys held in registers.  Causal blocks walk query tiles
 // from the block's first key to the end of the sequence (rows before it see
-// none of these keys).  Per 64-row query tile, Q and dO are staged row-major and
-// transposed; each wave computes S = Q K^T and dA = dO V^T, forms A' and dS in
-// registers and accumulates dV^T += dO^T A' and dK^T += Q^T dS.
+// none of these keys).  Per 64-row query tile Q and dO are staged row-major;
+// each wave computes S = Q K^T and dA = dO V^T (A operands: Q, dO rows), forms
+// A' and dS in registers and accumulates dV^T += dO^T A' and dK^T += Q^T dS
+// (A operands: dO, Q read transposed).
 //
-// Splitting the gradients over two kernels executes 14 D flops per visible pair
-// against 10 D for a single pass, but needs no atomics and no dQ workspace and is
-// bit-for-bit reproducible.
+// Tiles are staged by direct global->LDS loads into two buffers per operand:
+// tile t+1 loads while tile t is computed.  Splitting the gradients over two
+// kernels executes 14 D flops per visible pair against 10 D for a single pass,
+// but needs no atomics and no workspace and is bit-for-bit reproducible.
 #include "hstu_kernels.h"
 
 namespace hstu {
 namespace {
 
-constexpr int BM = kFwdBlockM;  // dq kernel: query rows per workgroup (32 per wave)
-constexpr int BN = 64;          // dq kernel: keys per tile
-constexpr int BNK = kBwdBlockN; // dk/dv kernel: keys per workgroup (32 per wave)
-constexpr int BMQ = 64;         // dk/dv kernel: query rows per tile
+constexpr int BM = kFwdBlockM;   // dq kernel: query rows per workgroup (32 per wave)
+constexpr int BN = kTileRows;    // dq kernel: keys per tile
+constexpr int BNK = kBwdBlockN;  // dk/dv kernel: keys per workgroup (32 per wave)
+constexpr int BMQ = kTileRows;   // dk/dv kernel: query rows per tile
 
 // SiLU'(alpha x) given sig = sig(alpha x).
 __device__ __forceinline__ float dsilu(float x, float sig, float alpha) {
     return sig * (1.0f + alpha * x * (1.0f - sig));
 }
 
-// Stage one 8-row x 8-column block of a (rows, D) bf16 tile into LDS twice:
-// row-major at rows group_row(c, e) and transposed at column group c.  Rows at
-// or past `valid_end` (local) are zero.  `src` points at local row 0, column 0.
-template <int D, int RSTR, int NC, int TSTR>
-__device__ __forceinline__ void stage_block_both(const uint16_t* src, int64_t tok, int row_base, int valid_end,
-                                                 int c, int c8, uint16_t* rm, uint16_t* tr) {
-    uint4 in[8], out[8];
+// One key tile of the dq kernel for one wave.
+template <int D>
+__device__ __forceinline__ void dq_tile(const uint16_t* ks, const uint16_t* vs, const uint4 (&qf)[D / 16],
+                                        const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32], int n0,
+                                        int lim, float exp_c, float alpha, int lane) {
+    constexpr int DM = D < 32 ? 32 : D;
+    const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int r = group_row(c, e);
-        in[e] = make_uint4(0, 0, 0, 0);
-        if (row_base + r < valid_end) in[e] = ld_global16(src + (int64_t)(row_base + r) * tok + 8 * c8);
-        st_lds16(rm + r * RSTR + 8 * c8, in[e]);
-    }
-    transpose8x8(in, out);
+    for (int kb = 0; kb < BN / 32; ++kb) {
+        f32x16 sacc = f32x16{}, dacc = f32x16{};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int d = 8 * c8 + e;
-        st_lds16(tr + d * TSTR + 8 * swz<NC>(c, d), out[e]);
+        for (int kk = 0; kk < D / 16; ++kk) {
+            sacc = mfma32x32x16(lds_read16(ks, kb * 32 + l32, 16 * kk + 8 * g), qf[kk], sacc);
+            dacc = mfma32x32x16(lds_read16(vs, kb * 32 + l32, 16 * kk + 8 * g), dof[kk], dacc);
+        }
+        float dv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float x = sacc[r];
+            const float d = dacc[r] * dsilu(x, sigmoid_scaled(x, exp_c), alpha);
+            dv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? d : 0.0f;
+        }
+        const uint4 d0 = pack_operand(dv), d1 = pack_operand(dv + 8);
+#pragma unroll
+        for (int db = 0; db < DM / 32; ++db) {
+            acc[db] = mfma32x32x16(lds_read_transposed(ks, 2 * kb, db * 32, lane), d0, acc[db]);
+            acc[db] = mfma32x32x16(lds_read_transposed(ks, 2 * kb + 1, db * 32, lane), d1, acc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
     constexpr int DM = D < 32 ? 32 : D;
-    constexpr int D8 = D / 8;
-    constexpr int KSTR = D + 8;
-    constexpr int NCK = BN / 8;
-    constexpr int TSTR = BN + 8;
     constexpr int KSTEPS = D / 16;
-    constexpr int NSTEPS = BN / 16;
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t kt[DM * TSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t ks0[kTileElems], ks1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t vs0[kTileElems], vs1[kTileElems];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
     int idx = blockIdx.x;
     const int h = idx % p.heads;
@@ -93,92 +101,51 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     const int row0 = m0 + 32 * wave;
     const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
+    const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
 
     uint4 qf[KSTEPS], dof[KSTEPS];
-    if (my_row < sb.lq) {
-        const uint16_t* qs = p.q.base + (int64_t)(sb.q0 + my_row) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
-        const uint16_t* ds = p.dout.base + (int64_t)(sb.q0 + my_row) * p.dout.tok + (int64_t)h * p.dout.head + 8 * g;
+    {
+        const int r = min(my_row, sb.lq - 1);
+        const uint16_t* qsrc = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
+        const uint16_t* dsrc = p.dout.base + (int64_t)(sb.q0 + r) * p.dout.tok + (int64_t)h * p.dout.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            qf[kk] = ld_global16(qs + 16 * kk);
-            dof[kk] = ld_global16(ds + 16 * kk);
+            qf[kk] = ld_global16(qsrc + 16 * kk);
+            dof[kk] = ld_global16(dsrc + 16 * kk);
         }
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = dof[kk] = make_uint4(0, 0, 0, 0);
-    }
-    if (DM > D) {
-        for (int i = tid; i < (DM - D) * TSTR / 8; i += 256)
-            st_lds16(kt + D * TSTR + 8 * i, make_uint4(0, 0, 0, 0));
     }
 
-    f32x16 dqacc[DM / 32];
+    f32x16 acc[DM / 32];
 #pragma unroll
-    for (int db = 0; db < DM / 32; ++db) dqacc[db] = f32x16{};
+    for (int db = 0; db < DM / 32; ++db) acc[db] = f32x16{};
 
-    const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
-    const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int n0 = t * BN;
-        __syncthreads();
-        if (tid < 128) {
-            for (int bi = tid; bi < NCK * D8; bi += 128) {
-                const int c8 = bi % D8, c = bi / D8;
-                stage_block_both<D, KSTR, NCK, TSTR>(kbase, p.k.tok, n0, kv_end, c, c8, ks, kt);
-            }
-        } else {
-            for (int c = tid - 128; c < BN * D8; c += 128) {
-                const int r = c / D8, c8 = c % D8;
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (n0 + r < kv_end) val = ld_global16(vbase + (int64_t)(n0 + r) * p.v.tok + 8 * c8);
-                st_lds16(vs + r * KSTR + 8 * c8, val);
-            }
-        }
+    if (ntiles > 0) {
+        const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
+        const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
+        TileDma<D> kdma, vdma;
+        kdma.init(wave, lane, p.k.tok);
+        vdma.init(wave, lane, p.v.tok);
+        zero_tile_tail<D>(ks0, tid);
+        zero_tile_tail<D>(ks1, tid);
+        kdma.issue(ks0, kbase, p.k.tok, 0, kv_end);
+        vdma.issue(vs0, vbase, p.v.tok, 0, kv_end);
+        wait_global_loads();
         __syncthreads();
 
-        if (!wave_live) continue;
-        if (CAUSAL && n0 > row0 + 31) continue;
-
-        f32x16 sacc[BN / 32], dacc[BN / 32];
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            sacc[kb] = f32x16{};
-            dacc[kb] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                const int off = (kb * 32 + l32) * KSTR + 16 * kk + 8 * g;
-                sacc[kb] = mfma32x32x16(ld_lds16(ks + off), qf[kk], sacc[kb]);
-                dacc[kb] = mfma32x32x16(ld_lds16(vs + off), dof[kk], dacc[kb]);
+        auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn, int t) {
+            const int n0 = t * BN;
+            if (t + 1 < ntiles) {
+                kdma.issue(kn, kbase, p.k.tok, n0 + BN, kv_end);
+                vdma.issue(vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
-        }
-
-        const bool diag = CAUSAL && (n0 + BN - 1 > row0);
-        uint4 dsf[NSTEPS];
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            float dv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = sacc[kb][r];
-                const float sg = sigmoid_scaled(x, p.exp_c);
-                float v = dacc[kb][r] * dsilu(x, sg, p.alpha);
-                if (diag) {
-                    const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key > my_row) v = 0.0f;
-                }
-                dv[r] = v;
-            }
-            dsf[2 * kb] = pack_operand(dv);
-            dsf[2 * kb + 1] = pack_operand(dv + 8);
-        }
-
-#pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-            const int d = db * 32 + l32;
-#pragma unroll
-            for (int s = 0; s < NSTEPS; ++s)
-                dqacc[db] = mfma32x32x16(ld_lds16(kt + d * TSTR + 8 * swz<NCK>(2 * s + g, d)), dsf[s], dqacc[db]);
+            if (wave_live && !(CAUSAL && n0 > row0 + 31))
+                dq_tile<D>(kc, vc, qf, dof, acc, n0, lim, p.exp_c, p.alpha, lane);
+            wait_global_loads();
+            __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(ks0, vs0, ks1, vs1, t);
+            if (t + 1 < ntiles) step(ks1, vs1, ks0, vs0, t + 1);
         }
     }
 
@@ -191,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
             for (int rq = 0; rq < 4; ++rq) {
                 const int d0 = db * 32 + 8 * rq + 4 * g;
                 if (d0 < D) {
-                    const f32x16& a = dqacc[db];
+                    const f32x16& a = acc[db];
                     *reinterpret_cast<uint2*>(dst + d0) =
                         make_uint2(pack_bf16x2(a[4 * rq] * sc, a[4 * rq + 1] * sc),
                                    pack_bf16x2(a[4 * rq + 2] * sc, a[4 * rq + 3] * sc));
@@ -201,23 +168,56 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     }
 }
 
+// One query tile of the dk/dv kernel for one wave; rows outside [lo, hi) are masked.
+template <int D>
+__device__ __forceinline__ void dkdv_tile(const uint16_t* qs, const uint16_t* dos, const uint4 (&kf)[D / 16],
+                                          const uint4 (&vf)[D / 16], f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
+                                          f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], int qt0, int lo, int hi,
+                                          float exp_c, float alpha, int lane) {
+    constexpr int DM = D < 32 ? 32 : D;
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) {
+        f32x16 sacc = f32x16{}, dacc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            sacc = mfma32x32x16(lds_read16(qs, qb * 32 + l32, 16 * kk + 8 * g), kf[kk], sacc);
+            dacc = mfma32x32x16(lds_read16(dos, qb * 32 + l32, 16 * kk + 8 * g), vf[kk], dacc);
+        }
+        float av[16], dv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float x = sacc[r];
+            const float sg = sigmoid_scaled(x, exp_c);
+            const int row = qt0 + qb * 32 + acc_row(r, g);
+            const bool ok = row >= lo && row < hi;
+            av[r] = ok ? x * sg : 0.0f;
+            dv[r] = ok ? dacc[r] * dsilu(x, sg, alpha) : 0.0f;
+        }
+        const uint4 a0 = pack_operand(av), a1 = pack_operand(av + 8);
+        const uint4 d0 = pack_operand(dv), d1 = pack_operand(dv + 8);
+#pragma unroll
+        for (int db = 0; db < DM / 32; ++db) {
+            dvacc[db] = mfma32x32x16(lds_read_transposed(dos, 2 * qb, db * 32, lane), a0, dvacc[db]);
+            dvacc[db] = mfma32x32x16(lds_read_transposed(dos, 2 * qb + 1, db * 32, lane), a1, dvacc[db]);
+            dkacc[db] = mfma32x32x16(lds_read_transposed(qs, 2 * qb, db * 32, lane), d0, dkacc[db]);
+            dkacc[db] = mfma32x32x16(lds_read_transposed(qs, 2 * qb + 1, db * 32, lane), d1, dkacc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr int DM = D < 32 ? 32 : D;
-    constexpr int D8 = D / 8;
-    constexpr int QSTR = D + 8;
-    constexpr int NCQ = BMQ / 8;
-    constexpr int TSTR = BMQ + 8;
     constexpr int KSTEPS = D / 16;
-    constexpr int NSTEPS = BMQ / 16;
 
-    __shared__ __attribute__((aligned(16))) uint16_t qs[BMQ * QSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t dos[BMQ * QSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t qt[DM * TSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t dot[DM * TSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t qs0[kTileElems], qs1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t ds0[kTileElems], ds1[kTileElems];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
     // (key block n, sequence b, head h), key block 0 (the most query tiles) first
     int idx = blockIdx.x;
@@ -234,22 +234,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     const bool wave_live = key0 < sb.lk;
 
     uint4 kf[KSTEPS], vf[KSTEPS];
-    if (my_key < sb.lk) {
-        const uint16_t* ks = p.k.base + (int64_t)(sb.k0 + my_key) * p.k.tok + (int64_t)h * p.k.head + 8 * g;
-        const uint16_t* vs = p.v.base + (int64_t)(sb.k0 + my_key) * p.v.tok + (int64_t)h * p.v.head + 8 * g;
+    {
+        const int r = min(my_key, sb.lk - 1);
+        const uint16_t* ksrc = p.k.base + (int64_t)(sb.k0 + r) * p.k.tok + (int64_t)h * p.k.head + 8 * g;
+        const uint16_t* vsrc = p.v.base + (int64_t)(sb.k0 + r) * p.v.tok + (int64_t)h * p.v.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            kf[kk] = ld_global16(ks + 16 * kk);
-            vf[kk] = ld_global16(vs + 16 * kk);
-        }
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) kf[kk] = vf[kk] = make_uint4(0, 0, 0, 0);
-    }
-    if (DM > D) {
-        for (int i = tid; i < (DM - D) * TSTR / 8; i += 256) {
-            st_lds16(qt + D * TSTR + 8 * i, make_uint4(0, 0, 0, 0));
-            st_lds16(dot + D * TSTR + 8 * i, make_uint4(0, 0, 0, 0));
+            kf[kk] = ld_global16(ksrc + 16 * kk);
+            vf[kk] = ld_global16(vsrc + 16 * kk);
         }
     }
 
@@ -259,74 +251,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
 
     const int q_begin = CAUSAL ? n0 : 0;  // causal: rows before the block's first key see none of it
     const int ntiles = sb.lq > q_begin ? (sb.lq - q_begin + BMQ - 1) / BMQ : 0;
-    const uint16_t* qbase = p.q.base + (int64_t)sb.q0 * p.q.tok + (int64_t)h * p.q.head;
-    const uint16_t* dbase = p.dout.base + (int64_t)sb.q0 * p.dout.tok + (int64_t)h * p.dout.head;
+    // rows this lane's key is visible to: [lo, sb.lq)
+    const int lo = CAUSAL ? my_key : 0;
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int qt0 = q_begin + t * BMQ;
+    if (ntiles > 0) {
+        const uint16_t* qbase = p.q.base + (int64_t)sb.q0 * p.q.tok + (int64_t)h * p.q.head;
+        const uint16_t* dbase = p.dout.base + (int64_t)sb.q0 * p.dout.tok + (int64_t)h * p.dout.head;
+        TileDma<D> qdma, ddma;
+        qdma.init(wave, lane, p.q.tok);
+        ddma.init(wave, lane, p.dout.tok);
+        zero_tile_tail<D>(qs0, tid);
+        zero_tile_tail<D>(qs1, tid);
+        zero_tile_tail<D>(ds0, tid);
+        zero_tile_tail<D>(ds1, tid);
+        qdma.issue(qs0, qbase, p.q.tok, q_begin, sb.lq);
+        ddma.issue(ds0, dbase, p.dout.tok, q_begin, sb.lq);
+        wait_global_loads();
         __syncthreads();
-        if (tid < 128) {
-            for (int bi = tid; bi < NCQ * D8; bi += 128) {
-                const int c8 = bi % D8, c = bi / D8;
-                stage_block_both<D, QSTR, NCQ, TSTR>(qbase, p.q.tok, qt0, sb.lq, c, c8, qs, qt);
-            }
-        } else {
-            for (int bi = tid - 128; bi < NCQ * D8; bi += 128) {
-                const int c8 = bi % D8, c = bi / D8;
-                stage_block_both<D, QSTR, NCQ, TSTR>(dbase, p.dout.tok, qt0, sb.lq, c, c8, dos, dot);
-            }
-        }
-        __syncthreads();
 
-        if (!wave_live) continue;
-        if (CAUSAL && qt0 + BMQ - 1 < key0) continue;  // every row of the tile precedes every key of the wave
-
-        f32x16 sacc[BMQ / 32], dacc[BMQ / 32];
-#pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb) {
-            sacc[qb] = f32x16{};
-            dacc[qb] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                const int off = (qb * 32 + l32) * QSTR + 16 * kk + 8 * g;
-                sacc[qb] = mfma32x32x16(ld_lds16(qs + off), kf[kk], sacc[qb]);
-                dacc[qb] = mfma32x32x16(ld_lds16(dos + off), vf[kk], dacc[qb]);
+        auto step = [&](const uint16_t* qc, const uint16_t* dc, uint16_t* qn, uint16_t* dn, int t) {
+            const int qt0 = q_begin + t * BMQ;
+            if (t + 1 < ntiles) {
+                qdma.issue(qn, qbase, p.q.tok, qt0 + BMQ, sb.lq);
+                ddma.issue(dn, dbase, p.dout.tok, qt0 + BMQ, sb.lq);
             }
-        }
-
-        const bool diag = CAUSAL && (qt0 < key0 + 31);
-        uint4 af[NSTEPS], dsf[NSTEPS];
-#pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb) {
-            float av[16], dv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = sacc[qb][r];
-                const float sg = sigmoid_scaled(x, p.exp_c);
-                float a = x * sg;
-                float d = dacc[qb][r] * dsilu(x, sg, p.alpha);
-                if (diag) {
-                    const int row = qt0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (my_key > row) a = d = 0.0f;
-                }
-                av[r] = a;
-                dv[r] = d;
-            }
-            af[2 * qb] = pack_operand(av);
-            af[2 * qb + 1] = pack_operand(av + 8);
-            dsf[2 * qb] = pack_operand(dv);
-            dsf[2 * qb + 1] = pack_operand(dv + 8);
-        }
-
-#pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-            const int d = db * 32 + l32;
-#pragma unroll
-            for (int s = 0; s < NSTEPS; ++s) {
-                const int off = d * TSTR + 8 * swz<NCQ>(2 * s + g, d);
-                dvacc[db] = mfma32x32x16(ld_lds16(dot + off), af[s], dvacc[db]);
-                dkacc[db] = mfma32x32x16(ld_lds16(qt + off), dsf[s], dkacc[db]);
-            }
+            // waves whose keys all follow every row of the tile, or lie past the sequence, skip it
+            if (wave_live && !(CAUSAL && qt0 + BMQ - 1 < key0))
+                dkdv_tile<D>(qc, dc, kf, vf, dvacc, dkacc, qt0, lo, sb.lq, p.exp_c, p.alpha, lane);
+            wait_global_loads();
+            __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(qs0, ds0, qs1, ds1, t);
+            if (t + 1 < ntiles) step(qs1, ds1, qs0, ds0, t + 1);
         }
     }
 

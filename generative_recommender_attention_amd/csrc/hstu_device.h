@@ -7,15 +7,25 @@
 //   A (32 rows x 16 k):  lane holds row l32, k = 8g .. 8g+7   (one 16-byte value)
 //   B (16 k x 32 cols):  lane holds col l32, k = 8g .. 8g+7   (one 16-byte value)
 //   C (32 x 32, fp32):   lane holds col l32, rows 8(r/4) + 4g + r%4, r = 0..15
-// An accumulator C[m][n] therefore keeps its column index in the lane and its
-// row index in the register.  The kernels exploit that: the fp32 tile of one
-// product, rounded to bf16 in registers, is directly the B operand of the next
-// product that contracts over C's row index, with no trip through LDS.  The
-// order of the 16 contraction slots is free as long as both operands agree; the
-// B operand built from an accumulator takes, for contraction step s (16 rows of
-// C), slot t <- row 16s + 4g + (t%4) + 8(t/4), i.e. registers 8(s%2)+t of the
-// 32-row block s/2.  The A operand for such a product is read from a transposed
-// LDS tile whose 16-byte column groups hold the same rows in the same order.
+// An accumulator C[m][n] keeps its column index in the lane and its row index
+// in the register.  The kernels exploit that: the fp32 tile of one product,
+// rounded to bf16 in registers, is directly the B operand of the next product
+// that contracts over C's row index, with no trip through LDS.  The order of
+// the 16 contraction slots is free as long as both operands agree; a B operand
+// built from an accumulator takes, for contraction step s (16 rows of C),
+// slot t <- row 16s + 4g + (t%4) + 8(t/4), i.e. registers 8(s%2)+t of the
+// 32-row block s/2.  The matching A operand is read from a row-major LDS tile
+// with the gfx950 transposing read ds_read_b64_tr_b16: within each 16-lane
+// group, lane i receives element i%4 of the 8-byte pieces addressed by lanes
+// i/4, i/4+4, i/4+8 and i/4+12, so 16 lanes addressing 4 rows x 16 columns
+// receive those 16 columns x 4 rows.  Two such reads give the 8 slots.
+//
+// LDS tiles: 64 rows of 256 bytes (128 bf16; head dims below 128 leave the
+// rest of the row unused).  The 16-byte unit c of row r is stored at unit
+// c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3).  With that swizzle both
+// access patterns are free of bank conflicts on gfx950's 64-bank LDS (measured
+// with SQ_LDS_BANK_CONFLICT): 16-byte row reads by 16 consecutive rows, and
+// transposing reads of 4 consecutive rows x 32 bytes by each 16-lane group.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,8 +37,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
 
 constexpr int kWave = 64;
+constexpr int kTileRows = 64;             // rows per staged LDS tile
+constexpr int kRowElems = 128;            // bf16 per LDS tile row (256 bytes)
+constexpr int kTileElems = kTileRows * kRowElems;
 
 // One (T, H, D) bf16 tensor: element (t, h, d) at base + t*tok + h*head + d.
 struct TensorRef {
@@ -54,7 +69,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// bf16 B operand from registers r0..r0+7 of an fp32 accumulator-shaped array.
+// bf16 B operand from eight consecutive accumulator registers x[0..7].
 __device__ __forceinline__ uint4 pack_operand(const float* x) {
     return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
@@ -63,43 +78,105 @@ __device__ __forceinline__ uint4 pack_operand(const float* x) {
 __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
-__device__ __forceinline__ uint4 ld_lds16(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-__device__ __forceinline__ void st_lds16(uint16_t* p, uint4 v) {
-    *reinterpret_cast<uint4*>(p) = v;
+
+// ---- swizzled LDS tiles ------------------------------------------------------
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Element offset of (row r, column d) inside a tile; d % 8 is kept.
+__device__ __forceinline__ int tile_off(int r, int d) {
+    return r * kRowElems + 8 * ((d >> 3) ^ tile_swz(r)) + (d & 7);
 }
 
-// 8 x 8 transpose of bf16 held as eight 16-byte rows: out[e] element t =
-// in[t] element e.
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+__device__ __forceinline__ uint4 lds_read16(const uint16_t* tile, int r, int d) {
+    return *reinterpret_cast<const uint4*>(tile + tile_off(r, d));
+}
+
+__device__ __forceinline__ void lds_write16(uint16_t* tile, int r, int d, uint4 v) {
+    *reinterpret_cast<uint4*>(tile + tile_off(r, d)) = v;
+}
+
+// A operand of a product contracting over tile rows: rows of the operand are
+// columns d0 + 0..31 of the tile, contraction step s covers tile rows
+// 16s .. 16s+15 in the accumulator slot order (see the header comment).
+__device__ __forceinline__ uint4 lds_read_transposed(const uint16_t* tile, int s, int d0, int lane) {
+    const int grp = lane >> 4, j = lane & 15;
+    const int r = 16 * s + 4 * (grp >> 1) + (j >> 2);
+    const int d = d0 + 16 * (grp & 1) + 4 * (j & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off(r, d)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off(r + 8, d)));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_void;
+
+// Wait for this wave's outstanding global loads (including loads into LDS):
+// s_waitcnt vmcnt(0), leaving the other counters unconstrained.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Direct global -> LDS staging of one 64-row tile of a (T, H, D) tensor by the
+// 4 waves of a 256-thread workgroup, with global_load_lds_dwordx4: each wave
+// instruction fills one contiguous 1 KB chunk (4 tile rows), lane l writing
+// the 16 bytes at chunk + 16 l.  The swizzle is applied on the global side:
+// lane l fetches the logical unit that belongs at its physical slot.  Rows at
+// or past `valid_end` (local) are clamped to the last valid row, so the data
+// stays finite; the kernels mask those rows out.  Completion is awaited with
+// wait_global_loads() and published with a workgroup barrier.
+template <int D>
+struct TileDma {
+    static constexpr int kChunks = 4;  // 1 KB chunks per wave per tile
+    uint32_t off[kChunks];             // element offset of this lane's source from the tile's row 0
+    int wave;                          // wave index (wave-uniform)
+    int lane;
+
+    __device__ __forceinline__ static int chunk_row(int wave, int i, int lane) { return 4 * (wave * kChunks + i) + (lane >> 4); }
+    __device__ __forceinline__ static int chunk_col(int r, int lane) { return (lane & 15) ^ tile_swz(r); }
+
+    __device__ __forceinline__ void init(int wave_, int lane_, int64_t tok) {
+        wave = wave_;
+        lane = lane_;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        uint32_t w[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t* a = reinterpret_cast<const uint32_t*>(&in[2 * c]);
-            const uint32_t* b = reinterpret_cast<const uint32_t*>(&in[2 * c + 1]);
-            const uint32_t x = a[e >> 1], y = b[e >> 1];
-            w[c] = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        for (int i = 0; i < kChunks; ++i) {
+            const int r = chunk_row(wave, i, lane);
+            off[i] = (uint32_t)(r * tok + 8 * chunk_col(r, lane));
         }
-        out[e] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-}
+    // Fill `tile` with local rows row0 .. row0+63 of the tensor at `base`.
+    __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, int64_t tok, int row0,
+                                          int valid_end) const {
+        uint16_t* dst = tile + wave * kChunks * 4 * kRowElems;
+        if (row0 + kTileRows <= valid_end) {
+            const uint16_t* src = base + (int64_t)row0 * tok;
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i)
+                if (D == 128 || chunk_col(chunk_row(wave, i, lane), lane) < D / 8)
+                    __builtin_amdgcn_global_load_lds((global_void*)(src + off[i]), (lds_void*)(dst + i * 4 * kRowElems),
+                                                     16, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) {
+                const int r = chunk_row(wave, i, lane), c = chunk_col(r, lane);
+                if (D == 128 || c < D / 8) {
+                    const int row = min(row0 + r, valid_end - 1);
+                    __builtin_amdgcn_global_load_lds((global_void*)(base + (int64_t)row * tok + 8 * c),
+                                                     (lds_void*)(dst + i * 4 * kRowElems), 16, 0, 0);
+                }
+            }
+        }
+    }
+};
 
-// Row (within a tile) of element t of 16-byte column group c of a transposed
-// tile: the contraction-slot order of an accumulator-built B operand.
-__device__ __forceinline__ int group_row(int c, int t) {
-    return 16 * (c >> 1) + 4 * (c & 1) + (t & 3) + 8 * (t >> 2);
-}
-
-// Transposed tiles: row d (a head-dim index) of NC 16-byte column groups, with
-// the group index XOR-swizzled by d/8 so that both the staging writes (eight
-// lanes = eight consecutive d/8 at one group) and the MFMA reads (eight lanes =
-// eight consecutive d at one group) spread over all LDS banks.
-template <int NC>
-__device__ __forceinline__ int swz(int c, int d) {
-    return c ^ ((d >> 3) & (NC - 1));
+// Zero the unused columns D..127 of a tile (only needed below D = 32, where a
+// 32-row MFMA block reads past D; the results of those rows are discarded).
+template <int D>
+__device__ __forceinline__ void zero_tile_tail(uint16_t* tile, int tid) {
+    if (D < 32) {
+        for (int u = tid; u < kTileRows * (32 - D) / 8; u += 256) {
+            const int r = u / ((32 - D) / 8), c = u % ((32 - D) / 8);
+            lds_write16(tile, r, D + 8 * c, make_uint4(0, 0, 0, 0));
+        }
+    }
 }
 
 // Sequence bounds of batch entry b.
@@ -115,11 +192,14 @@ __device__ __forceinline__ SeqBounds seq_bounds(const int32_t* cu_q, const int32
     return s;
 }
 
-// SiLU(alpha x) / alpha = x * sig(alpha x), with sig(y) = 1 / (1 + 2^(-y log2 e)).
-// `c` = -alpha * log2(e).  v_exp_f32 and v_rcp_f32 (about 1 ulp each); large
-// |x| saturate cleanly: 2^+big = inf -> rcp = 0, 2^-big = 0 -> rcp = 1.
+// sig(alpha x) = 1 / (1 + 2^(x c)) with c = -alpha log2(e), on v_exp_f32 and
+// v_rcp_f32 (about 1 ulp each).  Large |x| saturate cleanly: 2^+big = inf ->
+// rcp = 0, 2^-big = 0 -> rcp = 1.
 __device__ __forceinline__ float sigmoid_scaled(float x, float c) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * c));
 }
+
+// Row of accumulator register r (0..15) inside a 32-row block, for lane half g.
+__device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 }  // namespace hstu

@@ -12,39 +12,71 @@
 // block past its sequence's end exits at once; the host never reads the
 // cumulative lengths.
 //
-// Per key tile of 64 keys: K is staged row-major and V transposed in LDS
-// (16-byte coalesced global loads; V is transposed in registers on the way in).
-// Each wave then runs
-//   S^T (64 x 32)  = K Q^T      on MFMA (A = K from LDS, B = Q from registers)
+// Key tiles of 64 rows are staged row-major in swizzled LDS by direct
+// global->LDS loads, double-buffered: the loads of tile t+1 are issued before
+// tile t is computed, so their latency hides behind it and one barrier per
+// tile suffices.  Each wave runs
+//   S^T (64 x 32)  = K Q^T      on MFMA (A = K rows from LDS, B = Q from registers)
 //   P^T            = bf16(S^T (.) sig(alpha S^T)), masked, in registers
-//   O^T (D x 32)  += V^T P^T    on MFMA (A = V^T from LDS, B = P^T from registers)
+//   O^T (D x 32)  += V^T P^T    on MFMA (A = V read transposed from LDS, B = P^T)
 // and the epilogue writes O = (alpha / L_scale) O^T^T in bf16.  Causal: only
-// key tiles up to the block's last row are visited, and the per-element mask is
-// applied only on tiles that cross the diagonal.  Key rows past the tile's end
-// are staged as zeros, so they add exactly zero without a mask.
+// key tiles up to the block's last row are visited, waves skip tiles entirely
+// after their rows, and the per-element mask runs only on tiles that cross the
+// diagonal or the sequence end.
 #include "hstu_kernels.h"
 
 namespace hstu {
 namespace {
 
 constexpr int BM = kFwdBlockM;  // 128 query rows per workgroup
-constexpr int BN = 64;          // keys per tile
+constexpr int BN = kTileRows;   // 64 keys per tile
+
+// One key tile for one wave: S^T = K Q^T, P^T = bf16(S^T sig(alpha S^T)) masked
+// to keys below `lim`, O^T += V^T P^T.  The mask is applied on every tile (a
+// compare and a select per score): a second, unmasked copy of this body for
+// interior tiles costs more registers than the 256 the two-waves-per-SIMD
+// occupancy allows.
+template <int D>
+__device__ __forceinline__ void fwd_tile(const uint16_t* ks, const uint16_t* vs, const uint4 (&qf)[D / 16],
+                                         f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], int n0, int lim, float exp_c,
+                                         int lane) {
+    constexpr int DM = D < 32 ? 32 : D;
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            sacc = mfma32x32x16(lds_read16(ks, kb * 32 + l32, 16 * kk + 8 * g), qf[kk], sacc);
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float a = sacc[r] * sigmoid_scaled(sacc[r], exp_c);
+            pv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? a : 0.0f;
+        }
+        const uint4 p0 = pack_operand(pv), p1 = pack_operand(pv + 8);
+#pragma unroll
+        for (int db = 0; db < DM / 32; ++db) {
+            oacc[db] = mfma32x32x16(lds_read_transposed(vs, 2 * kb, db * 32, lane), p0, oacc[db]);
+            oacc[db] = mfma32x32x16(lds_read_transposed(vs, 2 * kb + 1, db * 32, lane), p1, oacc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
+    }
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
-    constexpr int DM = D < 32 ? 32 : D;  // rows of the transposed V tile (32-row MFMA blocks)
-    constexpr int D8 = D / 8;            // 16-byte groups per head-dim row
-    constexpr int KSTR = D + 8;          // K tile row stride (elements); pad spreads banks
-    constexpr int NCV = BN / 8;          // 16-byte column groups of a transposed row
-    constexpr int VSTR = BN + 8;         // transposed V row stride (elements)
+    constexpr int DM = D < 32 ? 32 : D;  // rows of the O^T accumulator (32-row MFMA blocks)
     constexpr int KSTEPS = D / 16;       // contraction steps of K Q^T
-    constexpr int NSTEPS = BN / 16;      // contraction steps of V^T P^T
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[DM * VSTR];
+    // two separate buffers per operand, so the compiler can tell the tile being
+    // read from the tile being filled and need not wait for the fill
+    __shared__ __attribute__((aligned(16))) uint16_t ks0[kTileElems], ks1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t vs0[kTileElems], vs1[kTileElems];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
     int idx = blockIdx.x;
     const int h = idx % p.heads;
@@ -61,98 +93,50 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     const int row0 = m0 + 32 * wave;  // first (local) query row of this wave
     const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
+    // keys at or past `lim` contribute nothing to this lane's row
+    const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
 
     uint4 qf[KSTEPS];
-    if (my_row < sb.lq) {
-        const uint16_t* src = p.q.base + (int64_t)(sb.q0 + my_row) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
+    {
+        const int r = min(my_row, sb.lq - 1);
+        const uint16_t* src = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = ld_global16(src + 16 * kk);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = make_uint4(0, 0, 0, 0);
-    }
-
-    if (DM > D) {  // padding rows of the transposed tile feed only discarded outputs; keep them finite
-        for (int i = tid; i < (DM - D) * VSTR / 8; i += 256)
-            st_lds16(vt + D * VSTR + 8 * i, make_uint4(0, 0, 0, 0));
     }
 
     f32x16 oacc[DM / 32];
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) oacc[db] = f32x16{};
 
-    const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
-    const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int n0 = t * BN;
-        __syncthreads();  // every wave is done reading the previous tile
-        if (tid >= 128) {
-            // K, row-major: consecutive threads take consecutive 16-byte groups of a row
-            for (int c = tid - 128; c < BN * D8; c += 128) {
-                const int r = c / D8, c8 = c % D8;
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (n0 + r < kv_end) val = ld_global16(kbase + (int64_t)(n0 + r) * p.k.tok + 8 * c8);
-                st_lds16(ks + r * KSTR + 8 * c8, val);
-            }
-        } else {
-            // V, transposed: a thread moves an 8 key x 8 dim block, keys in operand-slot order
-            for (int bi = tid; bi < NCV * D8; bi += 128) {
-                const int c8 = bi % D8, kg = bi / D8;
-                uint4 in[8], out[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = n0 + group_row(kg, e);
-                    in[e] = make_uint4(0, 0, 0, 0);
-                    if (key < kv_end) in[e] = ld_global16(vbase + (int64_t)key * p.v.tok + 8 * c8);
-                }
-                transpose8x8(in, out);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = 8 * c8 + e;
-                    st_lds16(vt + d * VSTR + 8 * swz<NCV>(kg, d), out[e]);
-                }
-            }
-        }
+    if (ntiles > 0) {
+        const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
+        const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
+        TileDma<D> kdma, vdma;
+        kdma.init(wave, lane, p.k.tok);
+        vdma.init(wave, lane, p.v.tok);
+        zero_tile_tail<D>(ks0, tid);
+        zero_tile_tail<D>(ks1, tid);
+        zero_tile_tail<D>(vs0, tid);
+        zero_tile_tail<D>(vs1, tid);
+        kdma.issue(ks0, kbase, p.k.tok, 0, kv_end);
+        vdma.issue(vs0, vbase, p.v.tok, 0, kv_end);
+        wait_global_loads();
         __syncthreads();
 
-        if (!wave_live) continue;
-        if (CAUSAL && n0 > row0 + 31) continue;  // every key of the tile is after every row of the wave
-
-        f32x16 sacc[BN / 32];
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            sacc[kb] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                sacc[kb] = mfma32x32x16(ld_lds16(ks + (kb * 32 + l32) * KSTR + 16 * kk + 8 * g), qf[kk], sacc[kb]);
-        }
-
-        const bool diag = CAUSAL && (n0 + BN - 1 > row0);
-        uint4 pf[NSTEPS];
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            float pv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = sacc[kb][r];
-                float a = x * sigmoid_scaled(x, p.exp_c);
-                if (diag) {
-                    const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key > my_row) a = 0.0f;
-                }
-                pv[r] = a;
+        auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn, int t) {
+            const int n0 = t * BN;
+            if (t + 1 < ntiles) {  // the other buffers were last read before the previous barrier
+                kdma.issue(kn, kbase, p.k.tok, n0 + BN, kv_end);
+                vdma.issue(vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
-            pf[2 * kb] = pack_operand(pv);
-            pf[2 * kb + 1] = pack_operand(pv + 8);
-        }
-
-#pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-            const int d = db * 32 + l32;
-#pragma unroll
-            for (int s = 0; s < NSTEPS; ++s)
-                oacc[db] = mfma32x32x16(ld_lds16(vt + d * VSTR + 8 * swz<NCV>(2 * s + g, d)), pf[s], oacc[db]);
+            // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
+            if (wave_live && !(CAUSAL && n0 > row0 + 31)) fwd_tile<D>(kc, vc, qf, oacc, n0, lim, p.exp_c, lane);
+            wait_global_loads();
+            __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(ks0, vs0, ks1, vs1, t);
+            if (t + 1 < ntiles) step(ks1, vs1, ks0, vs0, t + 1);
         }
     }
 
