@@ -31,36 +31,48 @@ namespace {
 constexpr int BM = kFwdBlockM;  // 128 query rows per workgroup
 constexpr int BN = kTileRows;   // 64 keys per tile
 
-// One key tile for one wave: S^T = K Q^T, P^T = bf16(S^T sig(alpha S^T)) masked
-// to keys below `lim`, O^T += V^T P^T.  The mask is applied on every tile (a
-// compare and a select per score): a second, unmasked copy of this body for
-// interior tiles costs more registers than the 256 the two-waves-per-SIMD
-// occupancy allows.
+// One key tile for one wave: S^T = K Q^T for both 32-key blocks (two
+// independent MFMA chains), then per block P^T = bf16(S^T sig(alpha S^T))
+// masked to keys below `lim` and O^T += V^T P^T.  The mask is applied on every
+// tile (a compare and a select per score): a second, unmasked copy of this
+// body for interior tiles costs more registers than the 256 the
+// two-waves-per-SIMD occupancy allows.
+// bf16 P^T operand from accumulator registers r0..r0+7: SiLU(alpha x) / alpha,
+// zero for keys at or past `lim`.
+__device__ __forceinline__ uint4 fwd_scores_op(const f32x16& sacc, int r0, int key0, int lim, float exp_c, int g) {
+    float pv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float a = sacc[r0 + r] * sigmoid_scaled(sacc[r0 + r], exp_c);
+        pv[r] = key0 + acc_row(r0 + r, g) < lim ? a : 0.0f;
+    }
+    return pack_operand(pv);
+}
+
 template <int D>
 __device__ __forceinline__ void fwd_tile(const uint16_t* ks, const uint16_t* vs, const uint4 (&qf)[D / 16],
                                          f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], int n0, int lim, float exp_c,
                                          int lane) {
     constexpr int DM = D < 32 ? 32 : D;
     const int l32 = lane & 31, g = lane >> 5;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-        f32x16 sacc = f32x16{};
+    for (int kk = 0; kk < D / 16; ++kk) s0 = mfma32x32x16(lds_read16(ks, l32, 16 * kk + 8 * g), qf[kk], s0);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            sacc = mfma32x32x16(lds_read16(ks, kb * 32 + l32, 16 * kk + 8 * g), qf[kk], sacc);
-        float pv[16];
+    for (int kk = 0; kk < D / 16; ++kk) s1 = mfma32x32x16(lds_read16(ks, 32 + l32, 16 * kk + 8 * g), qf[kk], s1);
+    const uint4 p0 = fwd_scores_op(s0, 0, n0, lim, exp_c, g);
+    const uint4 p1 = fwd_scores_op(s0, 8, n0, lim, exp_c, g);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float a = sacc[r] * sigmoid_scaled(sacc[r], exp_c);
-            pv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? a : 0.0f;
-        }
-        const uint4 p0 = pack_operand(pv), p1 = pack_operand(pv + 8);
+    for (int db = 0; db < DM / 32; ++db) {
+        oacc[db] = mfma32x32x16(lds_read_transposed(vs, 0, db * 32, lane), p0, oacc[db]);
+        oacc[db] = mfma32x32x16(lds_read_transposed(vs, 1, db * 32, lane), p1, oacc[db]);
+    }
+    const uint4 p2 = fwd_scores_op(s1, 0, n0 + 32, lim, exp_c, g);
+    const uint4 p3 = fwd_scores_op(s1, 8, n0 + 32, lim, exp_c, g);
 #pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-            oacc[db] = mfma32x32x16(lds_read_transposed(vs, 2 * kb, db * 32, lane), p0, oacc[db]);
-            oacc[db] = mfma32x32x16(lds_read_transposed(vs, 2 * kb + 1, db * 32, lane), p1, oacc[db]);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
+    for (int db = 0; db < DM / 32; ++db) {
+        oacc[db] = mfma32x32x16(lds_read_transposed(vs, 2, db * 32, lane), p2, oacc[db]);
+        oacc[db] = mfma32x32x16(lds_read_transposed(vs, 3, db * 32, lane), p3, oacc[db]);
     }
 }
 
