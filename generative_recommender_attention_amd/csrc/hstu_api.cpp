@@ -97,6 +97,7 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
     p.alpha = a->alpha;
     p.exp_c = -a->alpha * 1.4426950408889634f;
     p.out_scale = ls >= 1 ? a->alpha / (float)ls : 0.0f;
+    p.pre_scale = p.exp_c != 0.0f ? p.out_scale / p.exp_c : 0.0f;
     return HSTU_OK;
 }
 

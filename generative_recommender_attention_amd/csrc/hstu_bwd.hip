@@ -7,8 +7,11 @@
 //     dV_j = sum_i M_ij a_ij dO_i
 //     dQ_i = alpha sum_j M_ij dA_ij SiLU'(s_ij) / L_scale k_j
 //     dK_j = alpha sum_i M_ij dA_ij SiLU'(s_ij) / L_scale q_i
-// SiLU'(s) = sig(s) (1 + s (1 - sig(s))).  Both kernels carry x = q_i.k_j (no
-// alpha) and fold alpha / L_scale into the final store, as the forward does.
+// SiLU'(s) = sig(s) (1 + s (1 - sig(s))).  As in the forward, the score MFMAs
+// run on Q (dq kernel) or K (dk/dv kernel) pre-multiplied by c = -alpha log2 e,
+// so they produce y = c x (x = q_i.k_j): sig(s) = 1 / (1 + 2^y) and
+// s = alpha x = -y / log2 e; alpha / L_scale (and 1/c for dV) is applied at the
+// final store.
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
 // same tile walk as the forward.  Per 64-key tile K and V are staged row-major
@@ -38,16 +41,19 @@ constexpr int BN = kTileRows;    // dq kernel: keys per tile
 constexpr int BNK = kBwdBlockN;  // dk/dv kernel: keys per workgroup (32 per wave)
 constexpr int BMQ = kTileRows;   // dk/dv kernel: query rows per tile
 
-// SiLU'(alpha x) given sig = sig(alpha x).
-__device__ __forceinline__ float dsilu(float x, float sig, float alpha) {
-    return sig * (1.0f + alpha * x * (1.0f - sig));
+constexpr float kNegLn2 = -0.69314718055994531f;  // s = y * kNegLn2 for y = c x
+
+// sig(s) and SiLU'(s) = sig (1 + s (1 - sig)) from a pre-scaled score y.
+__device__ __forceinline__ float sig_pre(float y) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y)); }
+__device__ __forceinline__ float dsilu_pre(float y, float sig) {
+    return sig * __builtin_fmaf(y * kNegLn2, 1.0f - sig, 1.0f);
 }
 
 // One key tile of the dq kernel for one wave.
 template <int D>
 __device__ __forceinline__ void dq_tile(const uint16_t* ks, const uint16_t* vs, const uint4 (&qf)[D / 16],
                                         const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32], int n0,
-                                        int lim, float exp_c, float alpha, int lane) {
+                                        int lim, int wlim, int lane) {
     constexpr int DM = D < 32 ? 32 : D;
     const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -60,10 +66,10 @@ __device__ __forceinline__ void dq_tile(const uint16_t* ks, const uint16_t* vs, 
         }
         float dv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float x = sacc[r];
-            const float d = dacc[r] * dsilu(x, sigmoid_scaled(x, exp_c), alpha);
-            dv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? d : 0.0f;
+        for (int r = 0; r < 16; ++r) dv[r] = dacc[r] * dsilu_pre(sacc[r], sig_pre(sacc[r]));
+        if (n0 + kb * 32 + 32 > wlim) {  // only blocks crossing the mask pay for the selects
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? dv[r] : 0.0f;
         }
         const uint4 d0 = pack_operand(dv), d1 = pack_operand(dv + 8);
 #pragma unroll
@@ -102,6 +108,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
     const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
     const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
+    const int wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;  // smallest lim in the wave
 
     uint4 qf[KSTEPS], dof[KSTEPS];
     {
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
         const uint16_t* dsrc = p.dout.base + (int64_t)(sb.q0 + r) * p.dout.tok + (int64_t)h * p.dout.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            qf[kk] = ld_global16(qsrc + 16 * kk);
+            qf[kk] = scale_bf16x8(ld_global16(qsrc + 16 * kk), p.exp_c);  // fold c into Q
             dof[kk] = ld_global16(dsrc + 16 * kk);
         }
     }
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
                 vdma.issue(vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
             if (wave_live && !(CAUSAL && n0 > row0 + 31))
-                dq_tile<D>(kc, vc, qf, dof, acc, n0, lim, p.exp_c, p.alpha, lane);
+                dq_tile<D>(kc, vc, qf, dof, acc, n0, lim, wlim, lane);
             wait_global_loads();
             __syncthreads();
         };
@@ -168,12 +175,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
     }
 }
 
-// One query tile of the dk/dv kernel for one wave; rows outside [lo, hi) are masked.
+// One query tile of the dk/dv kernel for one wave; rows outside [lo, hi) are
+// masked (lo is per lane); only blocks with rows below `wlo` (the largest lo of
+// the wave) or at or past hi pay for the selects.
 template <int D>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qs, const uint16_t* dos, const uint4 (&kf)[D / 16],
                                           const uint4 (&vf)[D / 16], f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
-                                          f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], int qt0, int lo, int hi,
-                                          float exp_c, float alpha, int lane) {
+                                          f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], int qt0, int lo, int wlo,
+                                          int hi, int lane) {
     constexpr int DM = D < 32 ? 32 : D;
     const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -187,12 +196,19 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qs, const uint16_t* do
         float av[16], dv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float x = sacc[r];
-            const float sg = sigmoid_scaled(x, exp_c);
-            const int row = qt0 + qb * 32 + acc_row(r, g);
-            const bool ok = row >= lo && row < hi;
-            av[r] = ok ? x * sg : 0.0f;
-            dv[r] = ok ? dacc[r] * dsilu(x, sg, alpha) : 0.0f;
+            const float y = sacc[r], sg = sig_pre(y);
+            av[r] = y * sg;
+            dv[r] = dacc[r] * dsilu_pre(y, sg);
+        }
+        const int row0 = qt0 + qb * 32;
+        if (row0 < wlo || row0 + 32 > hi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + acc_row(r, g);
+                const bool ok = row >= lo && row < hi;
+                av[r] = ok ? av[r] : 0.0f;
+                dv[r] = ok ? dv[r] : 0.0f;
+            }
         }
         const uint4 a0 = pack_operand(av), a1 = pack_operand(av + 8);
         const uint4 d0 = pack_operand(dv), d1 = pack_operand(dv + 8);
@@ -240,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
         const uint16_t* vsrc = p.v.base + (int64_t)(sb.k0 + r) * p.v.tok + (int64_t)h * p.v.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            kf[kk] = ld_global16(ksrc + 16 * kk);
+            kf[kk] = scale_bf16x8(ld_global16(ksrc + 16 * kk), p.exp_c);  // fold c into K
             vf[kk] = ld_global16(vsrc + 16 * kk);
         }
     }
@@ -253,6 +269,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int ntiles = sb.lq > q_begin ? (sb.lq - q_begin + BMQ - 1) / BMQ : 0;
     // rows this lane's key is visible to: [lo, sb.lq)
     const int lo = CAUSAL ? my_key : 0;
+    const int wlo = CAUSAL ? key0 + 31 : 0;  // largest lo in the wave
 
     if (ntiles > 0) {
         const uint16_t* qbase = p.q.base + (int64_t)sb.q0 * p.q.tok + (int64_t)h * p.q.head;
@@ -277,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
             }
             // waves whose keys all follow every row of the tile, or lie past the sequence, skip it
             if (wave_live && !(CAUSAL && qt0 + BMQ - 1 < key0))
-                dkdv_tile<D>(qc, dc, kf, vf, dvacc, dkacc, qt0, lo, sb.lq, p.exp_c, p.alpha, lane);
+                dkdv_tile<D>(qc, dc, kf, vf, dvacc, dkacc, qt0, lo, wlo, sb.lq, lane);
             wait_global_loads();
             __syncthreads();
         };
@@ -290,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     if (my_key < sb.lk) {
         uint16_t* dk = p.dk.base + (int64_t)(sb.k0 + my_key) * p.dk.tok + (int64_t)h * p.dk.head;
         uint16_t* dv = p.dv.base + (int64_t)(sb.k0 + my_key) * p.dv.tok + (int64_t)h * p.dv.head;
-        const float sc = p.out_scale;
+        const float sc = p.out_scale, scv = p.pre_scale;
 #pragma unroll
         for (int db = 0; db < DM / 32; ++db) {
 #pragma unroll
@@ -303,8 +320,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
                         make_uint2(pack_bf16x2(a[4 * rq] * sc, a[4 * rq + 1] * sc),
                                    pack_bf16x2(a[4 * rq + 2] * sc, a[4 * rq + 3] * sc));
                     *reinterpret_cast<uint2*>(dv + d0) =
-                        make_uint2(pack_bf16x2(c[4 * rq] * sc, c[4 * rq + 1] * sc),
-                                   pack_bf16x2(c[4 * rq + 2] * sc, c[4 * rq + 3] * sc));
+                        make_uint2(pack_bf16x2(c[4 * rq] * scv, c[4 * rq + 1] * scv),
+                                   pack_bf16x2(c[4 * rq + 2] * scv, c[4 * rq + 3] * scv));
                 }
             }
         }

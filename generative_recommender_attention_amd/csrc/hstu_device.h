@@ -75,6 +75,18 @@ __device__ __forceinline__ uint4 pack_operand(const float* x) {
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
 }
 
+// Eight bf16 values times an fp32 factor, rounded back to bf16 (nearest-even).
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float c) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+        o[i] = pack_bf16x2(lo * c, hi * c);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
@@ -123,9 +135,9 @@ __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt
 // or past `valid_end` (local) are clamped to the last valid row, so the data
 // stays finite; the kernels mask those rows out.  Completion is awaited with
 // wait_global_loads() and published with a workgroup barrier.
-template <int D>
+template <int D, int ROWS = kTileRows>
 struct TileDma {
-    static constexpr int kChunks = 4;  // 1 KB chunks per wave per tile
+    static constexpr int kChunks = ROWS / 16;  // 1 KB chunks per wave per tile
     uint32_t off[kChunks];             // element offset of this lane's source from the tile's row 0
     int wave;                          // wave index (wave-uniform)
     int lane;
@@ -146,7 +158,7 @@ struct TileDma {
     __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, int64_t tok, int row0,
                                           int valid_end) const {
         uint16_t* dst = tile + wave * kChunks * 4 * kRowElems;
-        if (row0 + kTileRows <= valid_end) {
+        if (row0 + ROWS <= valid_end) {
             const uint16_t* src = base + (int64_t)row0 * tok;
 #pragma unroll
             for (int i = 0; i < kChunks; ++i)
@@ -169,10 +181,10 @@ struct TileDma {
 
 // Zero the unused columns D..127 of a tile (only needed below D = 32, where a
 // 32-row MFMA block reads past D; the results of those rows are discarded).
-template <int D>
+template <int D, int ROWS = kTileRows>
 __device__ __forceinline__ void zero_tile_tail(uint16_t* tile, int tid) {
     if (D < 32) {
-        for (int u = tid; u < kTileRows * (32 - D) / 8; u += 256) {
+        for (int u = tid; u < ROWS * (32 - D) / 8; u += 256) {
             const int r = u / ((32 - D) / 8), c = u % ((32 - D) / 8);
             lds_write16(tile, r, D + 8 * c, make_uint4(0, 0, 0, 0));
         }
@@ -197,6 +209,12 @@ __device__ __forceinline__ SeqBounds seq_bounds(const int32_t* cu_q, const int32
 // rcp = 0, 2^-big = 0 -> rcp = 1.
 __device__ __forceinline__ float sigmoid_scaled(float x, float c) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * c));
+}
+
+// y / (1 + 2^y): SiLU(s) / alpha times c for a score pre-multiplied by
+// c = -alpha log2(e), i.e. y = c x, s = alpha x (x = q.k).
+__device__ __forceinline__ float silu_pre(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
 }
 
 // Row of accumulator register r (0..15) inside a 32-row block, for lane half g.

@@ -16,8 +16,9 @@
 // global->LDS loads, double-buffered: the loads of tile t+1 are issued before
 // tile t is computed, so their latency hides behind it and one barrier per
 // tile suffices.  Each wave runs
-//   S^T (64 x 32)  = K Q^T      on MFMA (A = K rows from LDS, B = Q from registers)
-//   P^T            = bf16(S^T (.) sig(alpha S^T)), masked, in registers
+//   S^T (64 x 32)  = K (cQ)^T   on MFMA (A = K rows from LDS, B = Q from registers,
+//                                scaled once by c = -alpha log2 e so the exponent is free)
+//   P^T            = bf16(y / (1 + 2^y)), masked, in registers
 //   O^T (D x 32)  += V^T P^T    on MFMA (A = V read transposed from LDS, B = P^T)
 // and the epilogue writes O = (alpha / L_scale) O^T^T in bf16.  Causal: only
 // key tiles up to the block's last row are visited, waves skip tiles entirely
@@ -28,30 +29,32 @@
 namespace hstu {
 namespace {
 
-constexpr int BM = kFwdBlockM;  // 128 query rows per workgroup
+constexpr int BM = kFwdBlockM;  // 128 query rows per workgroup, 32 per wave
 constexpr int BN = kTileRows;   // 64 keys per tile
 
-// One key tile for one wave: S^T = K Q^T for both 32-key blocks (two
-// independent MFMA chains), then per block P^T = bf16(S^T sig(alpha S^T))
-// masked to keys below `lim` and O^T += V^T P^T.  The mask is applied on every
-// tile (a compare and a select per score): a second, unmasked copy of this
-// body for interior tiles costs more registers than the 256 the
-// two-waves-per-SIMD occupancy allows.
-// bf16 P^T operand from accumulator registers r0..r0+7: SiLU(alpha x) / alpha,
-// zero for keys at or past `lim`.
-__device__ __forceinline__ uint4 fwd_scores_op(const f32x16& sacc, int r0, int key0, int lim, float exp_c, int g) {
+// bf16 P^T operand from accumulator registers r0..r0+7.  The scores arrive as
+// y = c x with c = -alpha log2(e) folded into Q (x = q.k), so
+// y sig(alpha x) = y / (1 + 2^y) costs one exp, one add, one rcp and one
+// multiply; the factor 1/c is folded into the output scale.  Keys at or past
+// `lim` are zeroed; only blocks reaching `wlim` (the smallest `lim` of the
+// wave) pay for the selects.
+__device__ __forceinline__ uint4 fwd_scores_op(const f32x16& sacc, int r0, int key0, int lim, int wlim, int g) {
     float pv[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const float a = sacc[r0 + r] * sigmoid_scaled(sacc[r0 + r], exp_c);
-        pv[r] = key0 + acc_row(r0 + r, g) < lim ? a : 0.0f;
+    for (int r = 0; r < 8; ++r) pv[r] = silu_pre(sacc[r0 + r]);
+    if (key0 + 32 > wlim) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) pv[r] = key0 + acc_row(r0 + r, g) < lim ? pv[r] : 0.0f;
     }
     return pack_operand(pv);
 }
 
+// One key tile for one wave: S^T = K Q^T for both 32-key blocks (two
+// independent MFMA chains), then per block P^T = bf16(y sig(alpha x)) masked to
+// keys below `lim` and O^T += V^T P^T.
 template <int D>
 __device__ __forceinline__ void fwd_tile(const uint16_t* ks, const uint16_t* vs, const uint4 (&qf)[D / 16],
-                                         f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], int n0, int lim, float exp_c,
+                                         f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], int n0, int lim, int wlim,
                                          int lane) {
     constexpr int DM = D < 32 ? 32 : D;
     const int l32 = lane & 31, g = lane >> 5;
@@ -60,15 +63,15 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* ks, const uint16_t* vs,
     for (int kk = 0; kk < D / 16; ++kk) s0 = mfma32x32x16(lds_read16(ks, l32, 16 * kk + 8 * g), qf[kk], s0);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) s1 = mfma32x32x16(lds_read16(ks, 32 + l32, 16 * kk + 8 * g), qf[kk], s1);
-    const uint4 p0 = fwd_scores_op(s0, 0, n0, lim, exp_c, g);
-    const uint4 p1 = fwd_scores_op(s0, 8, n0, lim, exp_c, g);
+    const uint4 p0 = fwd_scores_op(s0, 0, n0, lim, wlim, g);
+    const uint4 p1 = fwd_scores_op(s0, 8, n0, lim, wlim, g);
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) {
         oacc[db] = mfma32x32x16(lds_read_transposed(vs, 0, db * 32, lane), p0, oacc[db]);
         oacc[db] = mfma32x32x16(lds_read_transposed(vs, 1, db * 32, lane), p1, oacc[db]);
     }
-    const uint4 p2 = fwd_scores_op(s1, 0, n0 + 32, lim, exp_c, g);
-    const uint4 p3 = fwd_scores_op(s1, 8, n0 + 32, lim, exp_c, g);
+    const uint4 p2 = fwd_scores_op(s1, 0, n0 + 32, lim, wlim, g);
+    const uint4 p3 = fwd_scores_op(s1, 8, n0 + 32, lim, wlim, g);
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) {
         oacc[db] = mfma32x32x16(lds_read_transposed(vs, 2, db * 32, lane), p2, oacc[db]);
@@ -107,13 +110,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     const bool wave_live = row0 < sb.lq;
     // keys at or past `lim` contribute nothing to this lane's row
     const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
+    const int wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;  // smallest lim in the wave
 
     uint4 qf[KSTEPS];
     {
         const int r = min(my_row, sb.lq - 1);
         const uint16_t* src = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = ld_global16(src + 16 * kk);
+        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = scale_bf16x8(ld_global16(src + 16 * kk), p.exp_c);
     }
 
     f32x16 oacc[DM / 32];
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
                 vdma.issue(vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
             // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
-            if (wave_live && !(CAUSAL && n0 > row0 + 31)) fwd_tile<D>(kc, vc, qf, oacc, n0, lim, p.exp_c, lane);
+            if (wave_live && !(CAUSAL && n0 > row0 + 31)) fwd_tile<D>(kc, vc, qf, oacc, n0, lim, wlim, lane);
             wait_global_loads();
             __syncthreads();
         };
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
 
     if (my_row < sb.lq) {
         uint16_t* dst = p.o.base + (int64_t)(sb.q0 + my_row) * p.o.tok + (int64_t)h * p.o.head;
-        const float sc = p.out_scale;
+        const float sc = p.pre_scale;  // alpha / L_scale, and undo the c folded into the scores
 #pragma unroll
         for (int db = 0; db < DM / 32; ++db) {
 #pragma unroll

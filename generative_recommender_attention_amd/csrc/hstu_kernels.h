@@ -17,7 +17,9 @@ struct AttnParams {
     int32_t nblk;          // row (or key) blocks per sequence covered by the grid
     float alpha;           // score scale
     float exp_c;           // -alpha * log2(e), for sig(alpha x) = 1 / (1 + 2^(x exp_c))
-    float out_scale;       // alpha / L_scale: the epilogue factor of O, dQ, dK and dV
+    float out_scale;       // alpha / L_scale: the epilogue factor of dQ and dK
+    float pre_scale;       // alpha / (L_scale c): the factor of O and dV, whose sums run over
+                           // scores pre-multiplied by c = exp_c (0 when alpha = 0)
     TensorRef q, k, v, dout;
     TensorOut o, dq, dk, dv;
 };
