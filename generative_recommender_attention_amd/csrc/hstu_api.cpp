@@ -50,6 +50,10 @@ hstu_status_t check_operand(const hstu_args_t& a, Operand& t) {
         return fail(HSTU_ERR_INVALID_ARGUMENT,
                     "%s strides (token %lld, head %lld) must be positive multiples of 8 elements", t.name,
                     (long long)st, (long long)sh);
+    // Staged tiles are addressed by 32-bit byte offsets from a tile's first row.
+    if (st > hstu::kMaxTokenStride)
+        return fail(HSTU_ERR_UNSUPPORTED, "%s token stride %lld exceeds %lld elements", t.name, (long long)st,
+                    (long long)hstu::kMaxTokenStride);
     // Non-aliasing: either heads nest inside tokens or tokens nest inside heads.
     const bool token_major = sh >= D && (H == 1 || st >= sh * H);
     const bool head_major = st >= D && (t.rows == 1 || sh >= st * t.rows);
@@ -114,6 +118,7 @@ hstu_status_t set_grid(hstu::AttnParams& p, int32_t max_len, int block) {
     if (grid > 0x7fffffffLL)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "problem too large: %lld workgroups", (long long)grid);
     p.nblk = (int32_t)nblk;
+    p.max_len = max_len;
     return HSTU_OK;
 }
 

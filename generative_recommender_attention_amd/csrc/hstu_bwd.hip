@@ -68,6 +68,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* ks, const uint16_t* vs, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) dv[r] = dacc[r] * dsilu_pre(sacc[r], sig_pre(sacc[r]));
         if (n0 + kb * 32 + 32 > wlim) {  // only blocks crossing the mask pay for the selects
+            keep_branch();
 #pragma unroll
             for (int r = 0; r < 16; ++r) dv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? dv[r] : 0.0f;
         }
@@ -202,6 +203,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qs, const uint16_t* do
         }
         const int row0 = qt0 + qb * 32;
         if (row0 < wlo || row0 + 32 > hi) {
+            keep_branch();
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + acc_row(r, g);

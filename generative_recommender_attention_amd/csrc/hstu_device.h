@@ -191,6 +191,115 @@ __device__ __forceinline__ void zero_tile_tail(uint16_t* tile, int tid) {
     }
 }
 
+// ---- LDS by byte address ------------------------------------------------------
+// Kernels that keep all their tiles in one LDS array address them by byte
+// offset, so that constant parts (slot, row block, contraction step) fold into
+// the instructions' immediate offsets and only a few lane-dependent offsets
+// stay in registers.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
+__device__ __forceinline__ uint4 ds_read16(uint32_t a) {
+    const u32x4 v = *(lds_u32x4*)(uintptr_t)a;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void ds_write16(uint32_t a, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    *(lds_u32x4*)(uintptr_t)a = w;
+}
+
+// Byte offset of (row r, 16-byte unit c) inside a swizzled tile.
+__device__ __forceinline__ uint32_t tile_byte(int r, int c) { return (uint32_t)(r * 256 + 16 * (c ^ tile_swz(r))); }
+
+// Transposing read (see the header comment) from two byte addresses: rows r
+// and r + 8 of the same 16-row contraction step.
+__device__ __forceinline__ uint4 ds_read_tr16x2(uint32_t lo, uint32_t hi) {
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lo);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)hi);
+    const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+    return make_uint4(x.x, x.y, y.x, y.y);
+}
+
+// Byte offsets of the transposing reads of lane `lane` for the 32-column block
+// starting at column d0, rows 0..15 of a step (add 4096 bytes per further step):
+// .x for the rows r, .y for the rows r + 8.
+__device__ __forceinline__ uint2 tr_offsets(int d0, int lane) {
+    const int grp = lane >> 4, j = lane & 15;
+    const int r = 4 * (grp >> 1) + (j >> 2);
+    const int d = d0 + 16 * (grp & 1) + 4 * (j & 3);
+    return make_uint2((uint32_t)(2 * tile_off(r, d)), (uint32_t)(2 * tile_off(r + 8, d)));
+}
+
+// A wave-uniform pointer, asserted to the compiler so that it sits in SGPRs.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One 1 KB global -> LDS copy (global_load_lds_dwordx4, saddr form): lane l
+// fetches 16 bytes at gbase + voff and the hardware stores them at LDS byte
+// M0 + 16 l.  Issued from inline assembly so that the compiler does not track
+// it: it inserts no waits of its own, and the caller orders the copy with
+// wait_global_loads() and a barrier.  `lds` and `gbase` must be wave-uniform.
+__device__ __forceinline__ void dma16_lds(uint32_t lds, const void* gbase, uint32_t voff) {
+    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase)));
+}
+
+// Workgroup barrier that leaves global loads in flight (__syncthreads() also
+// drains vmcnt).  LDS accesses are drained first, so that a tile slot may be
+// refilled once every wave has passed; a staged tile is published by its
+// loaders' wait_global_loads() before the barrier.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Staging of 64-row tiles of a (T, H, D) tensor by 4 waves with dma16_lds,
+// swizzled as above; the same chunk layout as TileDma.
+template <int D>
+struct TileDmaAsm {
+    uint32_t off[4];  // byte offset of this lane's source from the tile's row 0
+    int wave;         // 0..3 among the loading waves (wave-uniform)
+    int lane;
+
+    __device__ __forceinline__ static int chunk_row(int wave, int i, int lane) { return 4 * (wave * 4 + i) + (lane >> 4); }
+    __device__ __forceinline__ static int chunk_col(int r, int lane) { return (lane & 15) ^ tile_swz(r); }
+
+    __device__ __forceinline__ void init(int wave_, int lane_, int64_t tok) {
+        wave = wave_;
+        lane = lane_;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = chunk_row(wave, i, lane);
+            off[i] = (uint32_t)(2 * (r * tok + 8 * chunk_col(r, lane)));
+        }
+    }
+    // Fill the tile at LDS byte `tile` with local rows row0 .. row0+63 of the
+    // tensor at `base`; rows at or past valid_end repeat row valid_end - 1.
+    __device__ __forceinline__ void issue(uint32_t tile, const uint16_t* base, int64_t tok, int row0,
+                                          int valid_end) const {
+        const uint16_t* src = base + (int64_t)row0 * tok;
+        const uint32_t dst = tile + (uint32_t)wave * 4096u;
+        if (row0 + kTileRows <= valid_end) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (D == 128 || chunk_col(chunk_row(wave, i, lane), lane) < D / 8) dma16_lds(dst + 1024 * i, src, off[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = chunk_row(wave, i, lane), c = chunk_col(r, lane);
+                if (D == 128 || c < D / 8) {
+                    const int rr = min(r, valid_end - 1 - row0);
+                    dma16_lds(dst + 1024 * i, src, (uint32_t)(2 * (rr * tok + 8 * c)));
+                }
+            }
+        }
+    }
+};
+
 // Sequence bounds of batch entry b.
 struct SeqBounds {
     int q0, lq, k0, lk;
@@ -216,6 +325,11 @@ __device__ __forceinline__ float sigmoid_scaled(float x, float c) {
 __device__ __forceinline__ float silu_pre(float y) {
     return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
 }
+
+// Marks a branch body the optimizer must not speculate: the mask selects sit
+// behind a uniform branch so that interior tiles skip them, and an if-converted
+// (always executed) version would cost two VALU instructions per score.
+__device__ __forceinline__ void keep_branch() { __asm__ volatile(""); }
 
 // Row of accumulator register r (0..15) inside a 32-row block, for lane half g.
 __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }

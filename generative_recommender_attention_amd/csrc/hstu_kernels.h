@@ -15,6 +15,7 @@ struct AttnParams {
     int32_t batch;         // B
     int32_t heads;         // H
     int32_t nblk;          // row (or key) blocks per sequence covered by the grid
+    int32_t max_len;       // max_seqlen_q (forward, dq) or max_seqlen_k (dk/dv): sizes the grid
     float alpha;           // score scale
     float exp_c;           // -alpha * log2(e), for sig(alpha x) = 1 / (1 + 2^(x exp_c))
     float out_scale;       // alpha / L_scale: the epilogue factor of dQ and dK
@@ -27,6 +28,10 @@ struct AttnParams {
 // Tile shapes (rows per workgroup) used to size the grids.
 constexpr int kFwdBlockM = 128;   // query rows per forward / dQ workgroup
 constexpr int kBwdBlockN = 128;   // key rows per dK/dV workgroup
+
+// Largest token stride (elements) the kernels accept: a 64-row tile spans at
+// most 64 strides, addressed by unsigned 32-bit byte offsets.
+constexpr int64_t kMaxTokenStride = int64_t(1) << 24;
 
 hipError_t launch_fwd(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);

@@ -29,7 +29,9 @@
  *   last dimension is always contiguous.  A zero stride pair selects the packed
  *   layout (token = H * D, head = D).  Strides must be multiples of 8 elements,
  *   must not map two elements to one address, and base pointers must be 16-byte
- *   aligned ("Tensor layout", the alignment paragraph).  Disjoint views of one
+ *   aligned ("Tensor layout", the alignment paragraph).  A token stride above
+ *   2^24 elements is refused with HSTU_ERR_UNSUPPORTED (tiles of 64 tokens are
+ *   addressed with 32-bit byte offsets).  Disjoint views of one
  *   allocation (e.g. dk and dv split from one packed KV gradient buffer) are
  *   fine; overlap between an output and a live input is not checked.
  *
@@ -90,7 +92,7 @@ extern "C" {
 typedef enum hstu_status {
     HSTU_OK = 0,
     HSTU_ERR_INVALID_ARGUMENT = 1, /* a scalar, pointer, stride or size breaks the contract */
-    HSTU_ERR_UNSUPPORTED = 2,      /* head_dim or mask outside what is built               */
+    HSTU_ERR_UNSUPPORTED = 2,      /* head_dim, mask or token stride outside what is built */
     HSTU_ERR_DEVICE = 3            /* the HIP runtime refused a launch                      */
 } hstu_status_t;
 

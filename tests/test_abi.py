@@ -87,6 +87,7 @@ REJECT = [
     ("head stride not multiple of 8", dict(k=(128, 68)), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("aliasing strides", dict(v=(64, 64)), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("negative stride", dict(o=(-128, 64)), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("token stride above 2^24", dict(k=((1 << 24) + 8, 64)), hstu.HSTU_ERR_UNSUPPORTED),
 ]
 
 
