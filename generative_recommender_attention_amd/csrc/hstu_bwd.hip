@@ -14,7 +14,8 @@
 // final store.
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
-// same tile walk as the forward.  Per 64-key tile K and V are staged row-major
+// same tile walk as the forward, two workgroups per CU (so the exponent work of
+// one overlaps the products of the other).  Per 64-key tile K and V are staged row-major
 // in LDS; each wave computes S^T = K Q^T and dA^T = V dO^T (A operands: K, V
 // rows), forms dS^T in registers and accumulates dQ^T += K^T dS^T (A operand:
 // K read transposed).
@@ -27,8 +28,11 @@
 // A' and dS in registers and accumulates dV^T += dO^T A' and dK^T += Q^T dS
 // (A operands: dO, Q read transposed).
 //
-// Tiles are staged by direct global->LDS loads into two buffers per operand:
-// tile t+1 loads while tile t is computed.  Splitting the gradients over two
+// Tiles are staged as in the forward: one LDS array with two slots per operand,
+// direct global->LDS loads issued from inline assembly (tile t+1 loads while
+// tile t is computed), byte-addressed reads issued a few products ahead of their
+// MFMAs, and the elementwise work of one 32-row or 32-key block placed between
+// the products of the other.  Splitting the gradients over two
 // kernels executes 14 D flops per visible pair against 10 D for a single pass,
 // but needs no atomics and no workspace and is bit-for-bit reproducible.
 #include "hstu_kernels.h"
@@ -49,46 +53,85 @@ __device__ __forceinline__ float dsilu_pre(float y, float sig) {
     return sig * __builtin_fmaf(y * kNegLn2, 1.0f - sig, 1.0f);
 }
 
-// One key tile of the dq kernel for one wave.
+constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
+
+// dS^T operands of one 32-key block from its score and dA accumulators, masked
+// to keys below `lim` when the block reaches `wlim`.
+__device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc, int key0, int lim, int wlim, int g,
+                                         uint4& d0, uint4& d1) {
+    float dv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[r] = dacc[r] * dsilu_pre(sacc[r], sig_pre(sacc[r]));
+    if (key0 + 32 > wlim) {
+        keep_branch();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dv[r] = key0 + acc_row(r, g) < lim ? dv[r] : 0.0f;
+    }
+    d0 = pack_operand(dv);
+    d1 = pack_operand(dv + 8);
+}
+
+// One key tile of the dq kernel for one wave, on byte-addressed LDS slots `kt`
+// (K) and `vt` (V).  Products run S^T and dA^T of both 32-key blocks, then dQ^T
+// of the first block (while dS^T of the second is formed), then of the second;
+// every LDS read is issued PF products ahead of its MFMA.
 template <int D>
-__device__ __forceinline__ void dq_tile(const uint16_t* ks, const uint16_t* vs, const uint4 (&qf)[D / 16],
-                                        const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32], int n0,
-                                        int lim, int wlim, int lane) {
-    constexpr int DM = D < 32 ? 32 : D;
-    const int l32 = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-        f32x16 sacc = f32x16{}, dacc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            sacc = mfma32x32x16(lds_read16(ks, kb * 32 + l32, 16 * kk + 8 * g), qf[kk], sacc);
-            dacc = mfma32x32x16(lds_read16(vs, kb * 32 + l32, 16 * kk + 8 * g), dof[kk], dacc);
+__device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&qf)[D / 16],
+                                           const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
+                                           const uint32_t (&koff)[D / 16], const uint2 (&toff)[(D < 32 ? 32 : D) / 32],
+                                           int n0, int lim, int wlim, int g) {
+    constexpr int NDB = (D < 32 ? 32 : D) / 32;
+    constexpr int NS = D / 16;
+    constexpr int NA = 4 * NS;   // S and dA products: block kb, step kk, operand (K, V)
+    constexpr int NQ = 4 * NDB;  // dQ products: block kb = i / (2 NDB), step s = i / NDB, column block i % NDB
+    constexpr int PF = 4;
+    uint4 rd[NA + NQ];
+    auto read = [&](int r) {
+        if (r < NA) {
+            const int kb = r / (2 * NS), kk = (r / 2) % NS;
+            rd[r] = ds_read16(koff[kk] + ((r & 1) ? vt : kt) + kb * 8192);
+        } else if (r < NA + NQ) {
+            const int i = r - NA, s4 = i / NDB, db = i % NDB;
+            rd[r] = ds_read_tr16x2(toff[db].x + kt + 4096 * s4, toff[db].y + kt + 4096 * s4);
         }
-        float dv[16];
+    };
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dv[r] = dacc[r] * dsilu_pre(sacc[r], sig_pre(sacc[r]));
-        if (n0 + kb * 32 + 32 > wlim) {  // only blocks crossing the mask pay for the selects
-            keep_branch();
+    for (int r = 0; r < PF; ++r) read(r);
+    f32x16 sa[2], da[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dv[r] = n0 + kb * 32 + acc_row(r, g) < lim ? dv[r] : 0.0f;
+    for (int kb = 0; kb < 2; ++kb) {
+        sa[kb] = f32x16{};
+        da[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NS; ++kk) {
+            const int r = kb * 2 * NS + 2 * kk;
+            sa[kb] = mfma32x32x16(rd[r], qf[kk], sa[kb]);
+            read(r + PF);
+            da[kb] = mfma32x32x16(rd[r + 1], dof[kk], da[kb]);
+            read(r + 1 + PF);
         }
-        const uint4 d0 = pack_operand(dv), d1 = pack_operand(dv + 8);
+    }
 #pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-            acc[db] = mfma32x32x16(lds_read_transposed(ks, 2 * kb, db * 32, lane), d0, acc[db]);
-            acc[db] = mfma32x32x16(lds_read_transposed(ks, 2 * kb + 1, db * 32, lane), d1, acc[db]);
+    for (int kb = 0; kb < 2; ++kb) {
+        uint4 d0, d1;
+        dq_ds_op(sa[kb], da[kb], n0 + 32 * kb, lim, wlim, g, d0, d1);
+#pragma unroll
+        for (int j = 0; j < 2 * NDB; ++j) {
+            const int i = kb * 2 * NDB + j;
+            acc[i % NDB] = mfma32x32x16(rd[NA + i], j < NDB ? d0 : d1, acc[i % NDB]);
+            read(NA + i + PF);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
-
-    __shared__ __attribute__((aligned(16))) uint16_t ks0[kTileElems], ks1[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t vs0[kTileElems], vs1[kTileElems];
+    // [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile t lives in slot t % 2
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
+    const uint32_t lds0 = lds_addr(smem);
+    constexpr uint32_t K0 = 0, K1 = kTileBytes, V0 = 2 * kTileBytes, V1 = 3 * kTileBytes;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
     const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
     const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
-    const int wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;  // smallest lim in the wave
+    const int wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;
 
     uint4 qf[KSTEPS], dof[KSTEPS];
     {
@@ -122,7 +165,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
             dof[kk] = ld_global16(dsrc + 16 * kk);
         }
     }
-
+    uint32_t koff[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = lds0 + tile_byte(l32, 2 * kk + g);
+    uint2 toff[DM / 32];
+#pragma unroll
+    for (int db = 0; db < DM / 32; ++db) {
+        toff[db] = tr_offsets(32 * db, lane);
+        toff[db].x += lds0;
+        toff[db].y += lds0;
+    }
     f32x16 acc[DM / 32];
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) acc[db] = f32x16{};
@@ -133,27 +185,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
         TileDma<D> kdma, vdma;
         kdma.init(wave, lane, p.k.tok);
         vdma.init(wave, lane, p.v.tok);
-        zero_tile_tail<D>(ks0, tid);
-        zero_tile_tail<D>(ks1, tid);
-        kdma.issue(ks0, kbase, p.k.tok, 0, kv_end);
-        vdma.issue(vs0, vbase, p.v.tok, 0, kv_end);
+        if constexpr (D < 32) {
+            // columns D..31 of the K slots are read by the 32-wide transposed blocks
+            for (int u = tid; u < 2 * kTileRows * (32 - D) / 8; u += 256) {
+                const int sl = u / (kTileRows * (32 - D) / 8), v = u % (kTileRows * (32 - D) / 8);
+                const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
+                ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
+            }
+        }
+        kdma.issue(lds0 + K0, kbase, p.k.tok, 0, kv_end);
+        vdma.issue(lds0 + V0, vbase, p.v.tok, 0, kv_end);
         wait_global_loads();
         __syncthreads();
 
-        auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn, int t) {
+        auto step = [&](uint32_t kc, uint32_t vc, uint32_t kn, uint32_t vn, int t) {
             const int n0 = t * BN;
             if (t + 1 < ntiles) {
-                kdma.issue(kn, kbase, p.k.tok, n0 + BN, kv_end);
-                vdma.issue(vn, vbase, p.v.tok, n0 + BN, kv_end);
+                kdma.issue(lds0 + kn, kbase, p.k.tok, n0 + BN, kv_end);
+                vdma.issue(lds0 + vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
             if (wave_live && !(CAUSAL && n0 > row0 + 31))
-                dq_tile<D>(kc, vc, qf, dof, acc, n0, lim, wlim, lane);
+                dq_tile<D>(kc, vc, qf, dof, acc, koff, toff, n0, lim, wlim, g);
             wait_global_loads();
             __syncthreads();
         };
         for (int t = 0; t < ntiles; t += 2) {
-            step(ks0, vs0, ks1, vs1, t);
-            if (t + 1 < ntiles) step(ks1, vs1, ks0, vs0, t + 1);
+            step(K0, V0, K1, V1, t);
+            if (t + 1 < ntiles) step(K1, V1, K0, V0, t + 1);
         }
     }
 
@@ -176,52 +234,86 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnParams p) {
     }
 }
 
-// One query tile of the dk/dv kernel for one wave; rows outside [lo, hi) are
-// masked (lo is per lane); only blocks with rows below `wlo` (the largest lo of
-// the wave) or at or past hi pay for the selects.
-template <int D>
-__device__ __forceinline__ void dkdv_tile(const uint16_t* qs, const uint16_t* dos, const uint4 (&kf)[D / 16],
-                                          const uint4 (&vf)[D / 16], f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
-                                          f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], int qt0, int lo, int wlo,
-                                          int hi, int lane) {
-    constexpr int DM = D < 32 ? 32 : D;
-    const int l32 = lane & 31, g = lane >> 5;
+// A' and dS operands of one 32-row block of the dk/dv kernel, masked to rows in
+// [lo, hi) when the block reaches below `wlo` or past `hi`.
+__device__ __forceinline__ void dkdv_ops(const f32x16& sacc, const f32x16& dacc, int row0, int lo, int wlo, int hi,
+                                         int g, uint4 (&a)[2], uint4 (&d)[2]) {
+    float av[16], dv[16];
 #pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
-        f32x16 sacc = f32x16{}, dacc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            sacc = mfma32x32x16(lds_read16(qs, qb * 32 + l32, 16 * kk + 8 * g), kf[kk], sacc);
-            dacc = mfma32x32x16(lds_read16(dos, qb * 32 + l32, 16 * kk + 8 * g), vf[kk], dacc);
-        }
-        float av[16], dv[16];
+    for (int r = 0; r < 16; ++r) {
+        const float y = sacc[r], sg = sig_pre(y);
+        av[r] = y * sg;
+        dv[r] = dacc[r] * dsilu_pre(y, sg);
+    }
+    if (row0 < wlo || row0 + 32 > hi) {
+        keep_branch();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float y = sacc[r], sg = sig_pre(y);
-            av[r] = y * sg;
-            dv[r] = dacc[r] * dsilu_pre(y, sg);
+            const int row = row0 + acc_row(r, g);
+            const bool ok = row >= lo && row < hi;
+            av[r] = ok ? av[r] : 0.0f;
+            dv[r] = ok ? dv[r] : 0.0f;
         }
-        const int row0 = qt0 + qb * 32;
-        if (row0 < wlo || row0 + 32 > hi) {
-            keep_branch();
+    }
+    a[0] = pack_operand(av);
+    a[1] = pack_operand(av + 8);
+    d[0] = pack_operand(dv);
+    d[1] = pack_operand(dv + 8);
+}
+
+// One query tile of the dk/dv kernel for one wave, on byte-addressed LDS slots
+// `qt` (Q) and `dt` (dO).  Products run S and dA of both 32-row blocks, then dV^T
+// and dK^T of the first block (while A' and dS of the second are formed), then
+// of the second; every LDS read is issued PF products ahead of its MFMA.
+template <int D>
+__device__ __forceinline__ void dkdv_tile(uint32_t qt, uint32_t dt, const uint4 (&kf)[D / 16],
+                                             const uint4 (&vf)[D / 16], f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
+                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
+                                             const uint2 (&toff)[(D < 32 ? 32 : D) / 32], int qt0, int lo, int wlo,
+                                             int hi, int g) {
+    constexpr int NDB = (D < 32 ? 32 : D) / 32;
+    constexpr int NS = D / 16;
+    constexpr int NA = 4 * NS;   // S and dA products: block qb, step kk, operand (Q, dO)
+    constexpr int NG = 8 * NDB;  // gradient products: block qb, step s (2), column block db, (dV, dK)
+    constexpr int PF = 4;
+    uint4 rd[NA + NG];
+    auto read = [&](int r) {
+        if (r < NA) {
+            const int qb = r / (2 * NS), kk = (r / 2) % NS;
+            rd[r] = ds_read16(roff[kk] + ((r & 1) ? dt : qt) + qb * 8192);
+        } else if (r < NA + NG) {
+            const int i = r - NA, qb = i / (4 * NDB), s4 = 2 * qb + (i / (2 * NDB)) % 2, db = (i / 2) % NDB;
+            const uint32_t base = (i & 1) ? qt : dt;  // even: dO^T for dV, odd: Q^T for dK
+            rd[r] = ds_read_tr16x2(toff[db].x + base + 4096 * s4, toff[db].y + base + 4096 * s4);
+        }
+    };
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + acc_row(r, g);
-                const bool ok = row >= lo && row < hi;
-                av[r] = ok ? av[r] : 0.0f;
-                dv[r] = ok ? dv[r] : 0.0f;
-            }
-        }
-        const uint4 a0 = pack_operand(av), a1 = pack_operand(av + 8);
-        const uint4 d0 = pack_operand(dv), d1 = pack_operand(dv + 8);
+    for (int r = 0; r < PF; ++r) read(r);
+    f32x16 sa[2], da[2];
 #pragma unroll
-        for (int db = 0; db < DM / 32; ++db) {
-            dvacc[db] = mfma32x32x16(lds_read_transposed(dos, 2 * qb, db * 32, lane), a0, dvacc[db]);
-            dvacc[db] = mfma32x32x16(lds_read_transposed(dos, 2 * qb + 1, db * 32, lane), a1, dvacc[db]);
-            dkacc[db] = mfma32x32x16(lds_read_transposed(qs, 2 * qb, db * 32, lane), d0, dkacc[db]);
-            dkacc[db] = mfma32x32x16(lds_read_transposed(qs, 2 * qb + 1, db * 32, lane), d1, dkacc[db]);
+    for (int qb = 0; qb < 2; ++qb) {
+        sa[qb] = f32x16{};
+        da[qb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NS; ++kk) {
+            const int r = qb * 2 * NS + 2 * kk;
+            sa[qb] = mfma32x32x16(rd[r], kf[kk], sa[qb]);
+            read(r + PF);
+            da[qb] = mfma32x32x16(rd[r + 1], vf[kk], da[qb]);
+            read(r + 1 + PF);
         }
-        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        uint4 a[2], d[2];
+        dkdv_ops(sa[qb], da[qb], qt0 + 32 * qb, lo, wlo, hi, g, a, d);
+#pragma unroll
+        for (int j = 0; j < 4 * NDB; ++j) {
+            const int i = qb * 4 * NDB + j, half = j / (2 * NDB), db = (j / 2) % NDB;
+            if (j & 1) dkacc[db] = mfma32x32x16(rd[NA + i], d[half], dkacc[db]);
+            else dvacc[db] = mfma32x32x16(rd[NA + i], a[half], dvacc[db]);
+            read(NA + i + PF);
+        }
     }
 }
 
@@ -229,15 +321,15 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
-
-    __shared__ __attribute__((aligned(16))) uint16_t qs0[kTileElems], qs1[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t ds0[kTileElems], ds1[kTileElems];
+    // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1]; tile t lives in slot t % 2
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
+    const uint32_t lds0 = lds_addr(smem);
+    constexpr uint32_t Q0 = 0, Q1 = kTileBytes, D0 = 2 * kTileBytes, D1 = 3 * kTileBytes;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
-    // (key block n, sequence b, head h), key block 0 (the most query tiles) first
     int idx = blockIdx.x;
     const int h = idx % p.heads;
     idx /= p.heads;
@@ -247,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int n0 = n * BNK;
     if (n0 >= sb.lk) return;
 
-    const int key0 = n0 + 32 * wave;  // first (local) key of this wave
+    const int key0 = n0 + 32 * wave;
     const int my_key = key0 + l32;
     const bool wave_live = key0 < sb.lk;
 
@@ -262,16 +354,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
             vf[kk] = ld_global16(vsrc + 16 * kk);
         }
     }
-
+    uint32_t roff[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) roff[kk] = lds0 + tile_byte(l32, 2 * kk + g);
+    uint2 toff[DM / 32];
+#pragma unroll
+    for (int db = 0; db < DM / 32; ++db) {
+        toff[db] = tr_offsets(32 * db, lane);
+        toff[db].x += lds0;
+        toff[db].y += lds0;
+    }
     f32x16 dvacc[DM / 32], dkacc[DM / 32];
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) dvacc[db] = dkacc[db] = f32x16{};
 
-    const int q_begin = CAUSAL ? n0 : 0;  // causal: rows before the block's first key see none of it
+    const int q_begin = CAUSAL ? n0 : 0;
     const int ntiles = sb.lq > q_begin ? (sb.lq - q_begin + BMQ - 1) / BMQ : 0;
-    // rows this lane's key is visible to: [lo, sb.lq)
     const int lo = CAUSAL ? my_key : 0;
-    const int wlo = CAUSAL ? key0 + 31 : 0;  // largest lo in the wave
+    const int wlo = CAUSAL ? key0 + 31 : 0;
 
     if (ntiles > 0) {
         const uint16_t* qbase = p.q.base + (int64_t)sb.q0 * p.q.tok + (int64_t)h * p.q.head;
@@ -279,30 +379,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
         TileDma<D> qdma, ddma;
         qdma.init(wave, lane, p.q.tok);
         ddma.init(wave, lane, p.dout.tok);
-        zero_tile_tail<D>(qs0, tid);
-        zero_tile_tail<D>(qs1, tid);
-        zero_tile_tail<D>(ds0, tid);
-        zero_tile_tail<D>(ds1, tid);
-        qdma.issue(qs0, qbase, p.q.tok, q_begin, sb.lq);
-        ddma.issue(ds0, dbase, p.dout.tok, q_begin, sb.lq);
+        if constexpr (D < 32) {
+            for (int u = tid; u < 4 * kTileRows * (32 - D) / 8; u += 256) {
+                const int sl = u / (kTileRows * (32 - D) / 8), v = u % (kTileRows * (32 - D) / 8);
+                const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
+                ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
+            }
+        }
+        qdma.issue(lds0 + Q0, qbase, p.q.tok, q_begin, sb.lq);
+        ddma.issue(lds0 + D0, dbase, p.dout.tok, q_begin, sb.lq);
         wait_global_loads();
         __syncthreads();
 
-        auto step = [&](const uint16_t* qc, const uint16_t* dc, uint16_t* qn, uint16_t* dn, int t) {
+        auto step = [&](uint32_t qc, uint32_t dc, uint32_t qn, uint32_t dn, int t) {
             const int qt0 = q_begin + t * BMQ;
             if (t + 1 < ntiles) {
-                qdma.issue(qn, qbase, p.q.tok, qt0 + BMQ, sb.lq);
-                ddma.issue(dn, dbase, p.dout.tok, qt0 + BMQ, sb.lq);
+                qdma.issue(lds0 + qn, qbase, p.q.tok, qt0 + BMQ, sb.lq);
+                ddma.issue(lds0 + dn, dbase, p.dout.tok, qt0 + BMQ, sb.lq);
             }
-            // waves whose keys all follow every row of the tile, or lie past the sequence, skip it
             if (wave_live && !(CAUSAL && qt0 + BMQ - 1 < key0))
-                dkdv_tile<D>(qc, dc, kf, vf, dvacc, dkacc, qt0, lo, wlo, sb.lq, lane);
+                dkdv_tile<D>(qc, dc, kf, vf, dvacc, dkacc, roff, toff, qt0, lo, wlo, sb.lq, g);
             wait_global_loads();
             __syncthreads();
         };
         for (int t = 0; t < ntiles; t += 2) {
-            step(qs0, ds0, qs1, ds1, t);
-            if (t + 1 < ntiles) step(qs1, ds1, qs0, ds0, t + 1);
+            step(Q0, D0, Q1, D1, t);
+            if (t + 1 < ntiles) step(Q1, D1, Q0, D0, t + 1);
         }
     }
 

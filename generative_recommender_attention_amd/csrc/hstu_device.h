@@ -40,7 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
 
-constexpr int kWave = 64;
 constexpr int kTileRows = 64;             // rows per staged LDS tile
 constexpr int kRowElems = 128;            // bf16 per LDS tile row (256 bytes)
 constexpr int kTileElems = kTileRows * kRowElems;
@@ -99,97 +98,11 @@ __device__ __forceinline__ int tile_off(int r, int d) {
     return r * kRowElems + 8 * ((d >> 3) ^ tile_swz(r)) + (d & 7);
 }
 
-__device__ __forceinline__ uint4 lds_read16(const uint16_t* tile, int r, int d) {
-    return *reinterpret_cast<const uint4*>(tile + tile_off(r, d));
-}
-
-__device__ __forceinline__ void lds_write16(uint16_t* tile, int r, int d, uint4 v) {
-    *reinterpret_cast<uint4*>(tile + tile_off(r, d)) = v;
-}
-
-// A operand of a product contracting over tile rows: rows of the operand are
-// columns d0 + 0..31 of the tile, contraction step s covers tile rows
-// 16s .. 16s+15 in the accumulator slot order (see the header comment).
-__device__ __forceinline__ uint4 lds_read_transposed(const uint16_t* tile, int s, int d0, int lane) {
-    const int grp = lane >> 4, j = lane & 15;
-    const int r = 16 * s + 4 * (grp >> 1) + (j >> 2);
-    const int d = d0 + 16 * (grp & 1) + 4 * (j & 3);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off(r, d)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off(r + 8, d)));
-    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
-    return make_uint4(a.x, a.y, b.x, b.y);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_void;
 
 // Wait for this wave's outstanding global loads (including loads into LDS):
 // s_waitcnt vmcnt(0), leaving the other counters unconstrained.
 __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-
-// Direct global -> LDS staging of one 64-row tile of a (T, H, D) tensor by the
-// 4 waves of a 256-thread workgroup, with global_load_lds_dwordx4: each wave
-// instruction fills one contiguous 1 KB chunk (4 tile rows), lane l writing
-// the 16 bytes at chunk + 16 l.  The swizzle is applied on the global side:
-// lane l fetches the logical unit that belongs at its physical slot.  Rows at
-// or past `valid_end` (local) are clamped to the last valid row, so the data
-// stays finite; the kernels mask those rows out.  Completion is awaited with
-// wait_global_loads() and published with a workgroup barrier.
-template <int D, int ROWS = kTileRows>
-struct TileDma {
-    static constexpr int kChunks = ROWS / 16;  // 1 KB chunks per wave per tile
-    uint32_t off[kChunks];             // element offset of this lane's source from the tile's row 0
-    int wave;                          // wave index (wave-uniform)
-    int lane;
-
-    __device__ __forceinline__ static int chunk_row(int wave, int i, int lane) { return 4 * (wave * kChunks + i) + (lane >> 4); }
-    __device__ __forceinline__ static int chunk_col(int r, int lane) { return (lane & 15) ^ tile_swz(r); }
-
-    __device__ __forceinline__ void init(int wave_, int lane_, int64_t tok) {
-        wave = wave_;
-        lane = lane_;
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int r = chunk_row(wave, i, lane);
-            off[i] = (uint32_t)(r * tok + 8 * chunk_col(r, lane));
-        }
-    }
-    // Fill `tile` with local rows row0 .. row0+63 of the tensor at `base`.
-    __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, int64_t tok, int row0,
-                                          int valid_end) const {
-        uint16_t* dst = tile + wave * kChunks * 4 * kRowElems;
-        if (row0 + ROWS <= valid_end) {
-            const uint16_t* src = base + (int64_t)row0 * tok;
-#pragma unroll
-            for (int i = 0; i < kChunks; ++i)
-                if (D == 128 || chunk_col(chunk_row(wave, i, lane), lane) < D / 8)
-                    __builtin_amdgcn_global_load_lds((global_void*)(src + off[i]), (lds_void*)(dst + i * 4 * kRowElems),
-                                                     16, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kChunks; ++i) {
-                const int r = chunk_row(wave, i, lane), c = chunk_col(r, lane);
-                if (D == 128 || c < D / 8) {
-                    const int row = min(row0 + r, valid_end - 1);
-                    __builtin_amdgcn_global_load_lds((global_void*)(base + (int64_t)row * tok + 8 * c),
-                                                     (lds_void*)(dst + i * 4 * kRowElems), 16, 0, 0);
-                }
-            }
-        }
-    }
-};
-
-// Zero the unused columns D..127 of a tile (only needed below D = 32, where a
-// 32-row MFMA block reads past D; the results of those rows are discarded).
-template <int D, int ROWS = kTileRows>
-__device__ __forceinline__ void zero_tile_tail(uint16_t* tile, int tid) {
-    if (D < 32) {
-        for (int u = tid; u < ROWS * (32 - D) / 8; u += 256) {
-            const int r = u / ((32 - D) / 8), c = u % ((32 - D) / 8);
-            lds_write16(tile, r, D + 8 * c, make_uint4(0, 0, 0, 0));
-        }
-    }
-}
 
 // ---- LDS by byte address ------------------------------------------------------
 // Kernels that keep all their tiles in one LDS array address them by byte
@@ -251,16 +164,14 @@ __device__ __forceinline__ void dma16_lds(uint32_t lds, const void* gbase, uint3
                      : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase)));
 }
 
-// Workgroup barrier that leaves global loads in flight (__syncthreads() also
-// drains vmcnt).  LDS accesses are drained first, so that a tile slot may be
-// refilled once every wave has passed; a staged tile is published by its
-// loaders' wait_global_loads() before the barrier.
-__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Staging of 64-row tiles of a (T, H, D) tensor by 4 waves with dma16_lds,
-// swizzled as above; the same chunk layout as TileDma.
+// Staging of one 64-row tile of a (T, H, D) tensor by the 4 waves of a
+// workgroup with dma16_lds: each instruction fills one contiguous 1 KB chunk
+// (4 tile rows), lane l writing the 16 bytes at chunk + 16 l.  The swizzle is
+// applied on the global side: lane l fetches the logical unit that belongs at
+// its physical slot.  Rows at or past `valid_end` repeat the last valid row, so
+// the data stays finite; the kernels mask those rows out.
 template <int D>
-struct TileDmaAsm {
+struct TileDma {
     uint32_t off[4];  // byte offset of this lane's source from the tile's row 0
     int wave;         // 0..3 among the loading waves (wave-uniform)
     int lane;
@@ -311,13 +222,6 @@ __device__ __forceinline__ SeqBounds seq_bounds(const int32_t* cu_q, const int32
     s.k0 = cu_k[b];
     s.lk = cu_k[b + 1] - s.k0;
     return s;
-}
-
-// sig(alpha x) = 1 / (1 + 2^(x c)) with c = -alpha log2(e), on v_exp_f32 and
-// v_rcp_f32 (about 1 ulp each).  Large |x| saturate cleanly: 2^+big = inf ->
-// rcp = 0, 2^-big = 0 -> rcp = 1.
-__device__ __forceinline__ float sigmoid_scaled(float x, float c) {
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * c));
 }
 
 // y / (1 + 2^y): SiLU(s) / alpha times c for a score pre-multiplied by

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     if (ntiles > 0) {
         const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
         const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
-        TileDmaAsm<D> kdma, vdma;
+        TileDma<D> kdma, vdma;
         kdma.init(wave, lane, p.k.tok);
         vdma.init(wave, lane, p.v.tok);
         if constexpr (D < 32) {
