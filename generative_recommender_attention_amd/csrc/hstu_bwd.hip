@@ -15,26 +15,29 @@
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
 // same tile walk as the forward, two workgroups per CU (so the exponent work of
-// one overlaps the products of the other).  Per 64-key tile K and V are staged row-major
-// in LDS; each wave computes S^T = K Q^T and dA^T = V dO^T (A operands: K, V
-// rows), forms dS^T in registers and accumulates dQ^T += K^T dS^T (A operand:
-// K read transposed).
+// one overlaps the products of the other).  Per 64-key tile K and V are staged
+// row-major in LDS; each wave computes S^T = K Q^T and dA^T = V dO^T (A operands:
+// K, V rows), forms dS^T in registers and accumulates dQ^T += K^T dS^T (A
+// operand: K read transposed).
 //
-// dk/dv kernel: key-major, one workgroup per (128-key block, sequence, head),
-// each wave owning 32 keys held in registers.  Causal blocks walk query tiles
-// from the block's first key to the end of the sequence (rows before it see
-// none of these keys).  Per 64-row query tile Q and dO are staged row-major;
-// each wave computes S = Q K^T and dA = dO V^T (A operands: Q, dO rows), forms
-// A' and dS in registers and accumulates dV^T += dO^T A' and dK^T += Q^T dS
-// (A operands: dO, Q read transposed).
+// dk/dv kernel: key-major, one 8-wave workgroup per (128-key block, sequence,
+// head).  The block's K (times c) and V rows sit in LDS for the whole walk;
+// waves w and w + 4 own the same 32 keys and take the first and second 32 rows
+// of every query tile, so each wave holds only its dK^T and dV^T accumulators
+// and two waves fit per SIMD; their partial sums are added through LDS at the
+// end.  Causal blocks walk query tiles from the block's first key to the end of
+// the sequence (rows before it see none of these keys).  Per 64-row query tile
+// Q and dO are staged row-major; each wave computes S = Q K^T and dA = dO V^T
+// (A operands: Q, dO rows; B operands: K, V rows), forms A' and dS in registers
+// and accumulates dV^T += dO^T A' and dK^T += Q^T dS (A operands: dO, Q read
+// transposed).
 //
 // Tiles are staged as in the forward: one LDS array with two slots per operand,
 // direct global->LDS loads issued from inline assembly (tile t+1 loads while
-// tile t is computed), byte-addressed reads issued a few products ahead of their
-// MFMAs, and the elementwise work of one 32-row or 32-key block placed between
-// the products of the other.  Splitting the gradients over two
-// kernels executes 14 D flops per visible pair against 10 D for a single pass,
-// but needs no atomics and no workspace and is bit-for-bit reproducible.
+// tile t is computed) and byte-addressed reads issued a few products ahead of
+// their MFMAs.  Splitting the gradients over two kernels executes 14 D flops
+// per visible pair against 10 D for a single pass, but needs no atomics and no
+// workspace and is bit-for-bit reproducible.
 #include "hstu_kernels.h"
 
 namespace hstu {
@@ -42,7 +45,7 @@ namespace {
 
 constexpr int BM = kFwdBlockM;   // dq kernel: query rows per workgroup (32 per wave)
 constexpr int BN = kTileRows;    // dq kernel: keys per tile
-constexpr int BNK = kBwdBlockN;  // dk/dv kernel: keys per workgroup (32 per wave)
+constexpr int BNK = kBwdBlockN;  // dk/dv kernel: keys per workgroup (32 per wave pair)
 constexpr int BMQ = kTileRows;   // dk/dv kernel: query rows per tile
 
 constexpr float kNegLn2 = -0.69314718055994531f;  // s = y * kNegLn2 for y = c x
@@ -234,18 +237,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     }
 }
 
-// A' and dS operands of one 32-row block of the dk/dv kernel, masked to rows in
-// [lo, hi) when the block reaches below `wlo` or past `hi`.
-__device__ __forceinline__ void dkdv_ops(const f32x16& sacc, const f32x16& dacc, int row0, int lo, int wlo, int hi,
-                                         int g, uint4 (&a)[2], uint4 (&d)[2]) {
+// One 32-row block for one wave: S = Q K^T and dA = dO V^T (A operands: Q, dO
+// rows of the block; B operands: the wave's K, V rows), then dV^T += dO^T A' and
+// dK^T += Q^T dS over the block's two contraction steps.
+template <int D>
+__device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t drow, uint32_t krow, uint32_t vrow, uint32_t qtr,
+                                            uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
+                                            f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
+                                            const uint2 (&toff)[(D < 32 ? 32 : D) / 32], int row0, int lo, int hi,
+                                            int g) {
+    constexpr int NDB = (D < 32 ? 32 : D) / 32;
+    constexpr int NS = D / 16;
+    constexpr int NA = 4 * NS;   // reads for S and dA: step kk, (Q, K, dO, V)
+    constexpr int NG = 4 * NDB;  // reads for dV, dK: half, column block, (dO^T, Q^T)
+    constexpr int PF = 6;
+    uint4 rd[NA + NG];
+    auto read = [&](int r) {
+        if (r < NA) {
+            const int kk = r / 4, w = r % 4;
+            const uint32_t base = w == 0 ? qrow : w == 1 ? krow : w == 2 ? drow : vrow;
+            rd[r] = ds_read16(roff[kk] + base);
+        } else if (r < NA + NG) {
+            const int i = r - NA, half = i / (2 * NDB), db = (i / 2) % NDB;
+            const uint32_t base = ((i & 1) ? qtr : dtr) + 4096 * half;
+            rd[r] = ds_read_tr16x2(toff[db].x + base, toff[db].y + base);
+        }
+    };
+#pragma unroll
+    for (int r = 0; r < PF; ++r) read(r);
+    f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NS; ++kk) {
+        sa = mfma32x32x16(rd[4 * kk], rd[4 * kk + 1], sa);
+        read(4 * kk + PF);
+        read(4 * kk + 1 + PF);
+        da = mfma32x32x16(rd[4 * kk + 2], rd[4 * kk + 3], da);
+        read(4 * kk + 2 + PF);
+        read(4 * kk + 3 + PF);
+    }
     float av[16], dv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float y = sacc[r], sg = sig_pre(y);
+        const float y = sa[r], sg = sig_pre(y);
         av[r] = y * sg;
-        dv[r] = dacc[r] * dsilu_pre(y, sg);
+        dv[r] = da[r] * dsilu_pre(y, sg);
     }
-    if (row0 < wlo || row0 + 32 > hi) {
+    if (mask) {
         keep_branch();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -255,79 +292,30 @@ __device__ __forceinline__ void dkdv_ops(const f32x16& sacc, const f32x16& dacc,
             dv[r] = ok ? dv[r] : 0.0f;
         }
     }
-    a[0] = pack_operand(av);
-    a[1] = pack_operand(av + 8);
-    d[0] = pack_operand(dv);
-    d[1] = pack_operand(dv + 8);
-}
-
-// One query tile of the dk/dv kernel for one wave, on byte-addressed LDS slots
-// `qt` (Q) and `dt` (dO).  Products run S and dA of both 32-row blocks, then dV^T
-// and dK^T of the first block (while A' and dS of the second are formed), then
-// of the second; every LDS read is issued PF products ahead of its MFMA.
-template <int D>
-__device__ __forceinline__ void dkdv_tile(uint32_t qt, uint32_t dt, const uint4 (&kf)[D / 16],
-                                             const uint4 (&vf)[D / 16], f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
-                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
-                                             const uint2 (&toff)[(D < 32 ? 32 : D) / 32], int qt0, int lo, int wlo,
-                                             int hi, int g) {
-    constexpr int NDB = (D < 32 ? 32 : D) / 32;
-    constexpr int NS = D / 16;
-    constexpr int NA = 4 * NS;   // S and dA products: block qb, step kk, operand (Q, dO)
-    constexpr int NG = 8 * NDB;  // gradient products: block qb, step s (2), column block db, (dV, dK)
-    constexpr int PF = 4;
-    uint4 rd[NA + NG];
-    auto read = [&](int r) {
-        if (r < NA) {
-            const int qb = r / (2 * NS), kk = (r / 2) % NS;
-            rd[r] = ds_read16(roff[kk] + ((r & 1) ? dt : qt) + qb * 8192);
-        } else if (r < NA + NG) {
-            const int i = r - NA, qb = i / (4 * NDB), s4 = 2 * qb + (i / (2 * NDB)) % 2, db = (i / 2) % NDB;
-            const uint32_t base = (i & 1) ? qt : dt;  // even: dO^T for dV, odd: Q^T for dK
-            rd[r] = ds_read_tr16x2(toff[db].x + base + 4096 * s4, toff[db].y + base + 4096 * s4);
-        }
-    };
+    const uint4 a[2] = {pack_operand(av), pack_operand(av + 8)};
+    const uint4 d[2] = {pack_operand(dv), pack_operand(dv + 8)};
 #pragma unroll
-    for (int r = 0; r < PF; ++r) read(r);
-    f32x16 sa[2], da[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        sa[qb] = f32x16{};
-        da[qb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NS; ++kk) {
-            const int r = qb * 2 * NS + 2 * kk;
-            sa[qb] = mfma32x32x16(rd[r], kf[kk], sa[qb]);
-            read(r + PF);
-            da[qb] = mfma32x32x16(rd[r + 1], vf[kk], da[qb]);
-            read(r + 1 + PF);
-        }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        uint4 a[2], d[2];
-        dkdv_ops(sa[qb], da[qb], qt0 + 32 * qb, lo, wlo, hi, g, a, d);
-#pragma unroll
-        for (int j = 0; j < 4 * NDB; ++j) {
-            const int i = qb * 4 * NDB + j, half = j / (2 * NDB), db = (j / 2) % NDB;
-            if (j & 1) dkacc[db] = mfma32x32x16(rd[NA + i], d[half], dkacc[db]);
-            else dvacc[db] = mfma32x32x16(rd[NA + i], a[half], dvacc[db]);
-            read(NA + i + PF);
-        }
+    for (int j = 0; j < NG; ++j) {
+        const int half = j / (2 * NDB), db = (j / 2) % NDB;
+        if (j & 1) dkacc[db] = mfma32x32x16(rd[NA + j], d[half], dkacc[db]);
+        else dvacc[db] = mfma32x32x16(rd[NA + j], a[half], dvacc[db]);
+        read(NA + j + PF);
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
-    // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1]; tile t lives in slot t % 2
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
+    // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1 | K rows of the block | V rows of the block]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[8 * kTileElems];
     const uint32_t lds0 = lds_addr(smem);
     constexpr uint32_t Q0 = 0, Q1 = kTileBytes, D0 = 2 * kTileBytes, D1 = 3 * kTileBytes;
+    constexpr uint32_t KB = 4 * kTileBytes, VB = 6 * kTileBytes;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kw = wave & 3, qh = wave >> 2;  // key sub-block, row half of each tile
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
     int idx = blockIdx.x;
@@ -339,19 +327,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int n0 = n * BNK;
     if (n0 >= sb.lk) return;
 
-    const int key0 = n0 + 32 * wave;
+    const int key0 = n0 + 32 * kw;
     const int my_key = key0 + l32;
     const bool wave_live = key0 < sb.lk;
 
-    uint4 kf[KSTEPS], vf[KSTEPS];
-    {
-        const int r = min(my_key, sb.lk - 1);
-        const uint16_t* ksrc = p.k.base + (int64_t)(sb.k0 + r) * p.k.tok + (int64_t)h * p.k.head + 8 * g;
-        const uint16_t* vsrc = p.v.base + (int64_t)(sb.k0 + r) * p.v.tok + (int64_t)h * p.v.head + 8 * g;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            kf[kk] = scale_bf16x8(ld_global16(ksrc + 16 * kk), p.exp_c);  // fold c into K
-            vf[kk] = ld_global16(vsrc + 16 * kk);
+    // the block's K (times c) and V rows into LDS; rows past the sequence repeat its last row
+    for (int u = tid; u < BNK * 16; u += 512) {
+        const int r = u >> 4, c = u & 15;
+        if (c < D / 8) {
+            const int64_t row = sb.k0 + min(n0 + r, sb.lk - 1);
+            const uint4 kv = ld_global16(p.k.base + row * p.k.tok + (int64_t)h * p.k.head + 8 * c);
+            const uint4 vv = ld_global16(p.v.base + row * p.v.tok + (int64_t)h * p.v.head + 8 * c);
+            ds_write16(lds0 + KB + tile_byte(r, c), scale_bf16x8(kv, p.exp_c));
+            ds_write16(lds0 + VB + tile_byte(r, c), vv);
         }
     }
     uint32_t roff[KSTEPS];
@@ -371,34 +359,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int q_begin = CAUSAL ? n0 : 0;
     const int ntiles = sb.lq > q_begin ? (sb.lq - q_begin + BMQ - 1) / BMQ : 0;
     const int lo = CAUSAL ? my_key : 0;
-    const int wlo = CAUSAL ? key0 + 31 : 0;
+    const int wlo = CAUSAL ? key0 + 31 : 0;  // largest lo in the wave
+    const uint32_t krow = KB + 8192u * kw, vrow = VB + 8192u * kw;
 
     if (ntiles > 0) {
-        const uint16_t* qbase = p.q.base + (int64_t)sb.q0 * p.q.tok + (int64_t)h * p.q.head;
-        const uint16_t* dbase = p.dout.base + (int64_t)sb.q0 * p.dout.tok + (int64_t)h * p.dout.head;
-        TileDma<D> qdma, ddma;
-        qdma.init(wave, lane, p.q.tok);
-        ddma.init(wave, lane, p.dout.tok);
+        // waves 0-3 stage the Q tiles, waves 4-7 the dO tiles
+        const bool qgrp = qh == 0;
+        const int64_t stok = qgrp ? p.q.tok : p.dout.tok;
+        const uint16_t* sbase = qgrp ? p.q.base + (int64_t)sb.q0 * p.q.tok + (int64_t)h * p.q.head
+                                     : p.dout.base + (int64_t)sb.q0 * p.dout.tok + (int64_t)h * p.dout.head;
+        TileDma<D> dma;
+        dma.init(kw, lane, stok);
         if constexpr (D < 32) {
-            for (int u = tid; u < 4 * kTileRows * (32 - D) / 8; u += 256) {
+            // columns D..31 of the Q and dO slots are read by the 32-wide transposed blocks
+            for (int u = tid; u < 4 * kTileRows * (32 - D) / 8; u += 512) {
                 const int sl = u / (kTileRows * (32 - D) / 8), v = u % (kTileRows * (32 - D) / 8);
                 const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
                 ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
             }
         }
-        qdma.issue(lds0 + Q0, qbase, p.q.tok, q_begin, sb.lq);
-        ddma.issue(lds0 + D0, dbase, p.dout.tok, q_begin, sb.lq);
+        dma.issue(lds0 + (qgrp ? Q0 : D0), sbase, stok, q_begin, sb.lq);
         wait_global_loads();
         __syncthreads();
 
         auto step = [&](uint32_t qc, uint32_t dc, uint32_t qn, uint32_t dn, int t) {
             const int qt0 = q_begin + t * BMQ;
-            if (t + 1 < ntiles) {
-                qdma.issue(lds0 + qn, qbase, p.q.tok, qt0 + BMQ, sb.lq);
-                ddma.issue(lds0 + dn, dbase, p.dout.tok, qt0 + BMQ, sb.lq);
+            if (t + 1 < ntiles) dma.issue(lds0 + (qgrp ? qn : dn), sbase, stok, qt0 + BMQ, sb.lq);
+            const int row0 = qt0 + 32 * qh;
+            // waves whose keys all follow every row of the block, or lie past the sequence, skip it
+            if (wave_live && !(CAUSAL && row0 + 31 < key0) && row0 < sb.lq) {
+                const uint32_t qr = qc + 8192u * qh, dr = dc + 8192u * qh;
+                // rows below the wave's largest first visible row, or past the sequence, need the mask
+                dkdv_block<D>(row0 < wlo || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff,
+                               row0, lo, sb.lq, g);
             }
-            if (wave_live && !(CAUSAL && qt0 + BMQ - 1 < key0))
-                dkdv_tile<D>(qc, dc, kf, vf, dvacc, dkacc, roff, toff, qt0, lo, wlo, sb.lq, g);
             wait_global_loads();
             __syncthreads();
         };
@@ -407,6 +401,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnParams p) {
             if (t + 1 < ntiles) step(Q1, D1, Q0, D0, t + 1);
         }
     }
+
+    // add the row-half partial sums: waves 4-7 hand theirs to waves 0-3 through LDS
+    __syncthreads();
+    constexpr int NREG = DM / 32 * 16;  // accumulator registers per tensor
+    const uint32_t red = lds0 + (uint32_t)kw * (2 * NREG * 256) + 4u * lane;
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < DM / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                *(__attribute__((address_space(3))) float*)(uintptr_t)(red + 256u * (db * 16 + r)) = dvacc[db][r];
+                *(__attribute__((address_space(3))) float*)(uintptr_t)(red + 256u * (NREG + db * 16 + r)) = dkacc[db][r];
+            }
+    }
+    __syncthreads();
+    if (qh == 1) return;
+#pragma unroll
+    for (int db = 0; db < DM / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dvacc[db][r] += *(__attribute__((address_space(3))) float*)(uintptr_t)(red + 256u * (db * 16 + r));
+            dkacc[db][r] += *(__attribute__((address_space(3))) float*)(uintptr_t)(red + 256u * (NREG + db * 16 + r));
+        }
 
     if (my_key < sb.lk) {
         uint16_t* dk = p.dk.base + (int64_t)(sb.k0 + my_key) * p.dk.tok + (int64_t)h * p.dk.head;
@@ -444,7 +461,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
