@@ -55,11 +55,14 @@ def visible_pairs(lengths_q, lengths_k, causal: bool) -> int:
 
 
 def kernel_source_digest() -> str:
-    csrc = os.path.join(ROOT, "generative_recommender_attention_amd", "csrc")
+    """Digest of the kernel sources and of the build script that sets their compile flags."""
+    pkg = os.path.join(ROOT, "generative_recommender_attention_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = [os.path.join(csrc, name) for name in sorted(os.listdir(csrc))] + [os.path.join(pkg, "build.py")]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
