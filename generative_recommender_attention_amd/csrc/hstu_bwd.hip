@@ -50,10 +50,12 @@ constexpr int BMQ = kTileRows;   // dk/dv kernel: query rows per tile
 
 constexpr float kNegLn2 = -0.69314718055994531f;  // s = y * kNegLn2 for y = c x
 
-// sig(s) and SiLU'(s) = sig (1 + s (1 - sig)) from a pre-scaled score y.
+// sig(s) from a pre-scaled score y.
 __device__ __forceinline__ float sig_pre(float y) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y)); }
-__device__ __forceinline__ float dsilu_pre(float y, float sig) {
-    return sig * __builtin_fmaf(y * kNegLn2, 1.0f - sig, 1.0f);
+// SiLU'(s) = sig (1 + s (1 - sig)) from a = y sig: with s = y (-ln 2),
+// SiLU'(s) = sig + s sig (1 - sig) = sig + (-ln 2)(a - a sig), two fused multiply-adds.
+__device__ __forceinline__ float dsilu_from(float a, float sig) {
+    return __builtin_fmaf(kNegLn2, __builtin_fmaf(-a, sig, a), sig);
 }
 
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
@@ -64,7 +66,10 @@ __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc,
                                          uint4& d0, uint4& d1) {
     float dv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dv[r] = dacc[r] * dsilu_pre(sacc[r], sig_pre(sacc[r]));
+    for (int r = 0; r < 16; ++r) {
+        const float sg = sig_pre(sacc[r]);
+        dv[r] = dacc[r] * dsilu_from(sacc[r] * sg, sg);
+    }
     if (key0 + 32 > wlim) {
         keep_branch();
 #pragma unroll
@@ -280,7 +285,7 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     for (int r = 0; r < 16; ++r) {
         const float y = sa[r], sg = sig_pre(y);
         av[r] = y * sg;
-        dv[r] = da[r] * dsilu_pre(y, sg);
+        dv[r] = da[r] * dsilu_from(av[r], sg);
     }
     if (mask) {
         keep_branch();
