@@ -204,13 +204,25 @@ hstu_status_t hstu_bwd_dkdv(const hstu_args_t* a, const void* dout, const void* 
     return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream);
 }
 
+hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* a, size_t* bytes) {
+    if (a == nullptr || bytes == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args or bytes is null");
+    *bytes = 0;  // the two-kernel backward keeps everything in registers and LDS
+    return ok();
+}
+
 hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
-                       hipStream_t stream) {
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
     // Validate both halves before enqueueing either, so a failure enqueues nothing.
     hstu::AttnParams p;
     hstu_status_t st = check_common(a, cu_seqlens_q, cu_seqlens_k, p);
     if (st != HSTU_OK) return st;
+    size_t need = 0;
+    if ((st = hstu_bwd_workspace_size(a, &need)) != HSTU_OK) return st;
+    if (workspace_bytes < need)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (need > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is null or not 256-byte aligned");
     Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q},
                      {"k", k, a->k, a->total_k},          {"v", v, a->v, a->total_k},
                      {"dq", dq, a->dq, a->total_q},       {"dk", dk, a->dk, a->total_k},

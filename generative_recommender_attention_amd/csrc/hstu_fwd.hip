@@ -71,7 +71,7 @@ __device__ __forceinline__ void fwd_tile(uint32_t kt, uint32_t vt, const uint4 (
     constexpr int NS = D / 16;  // contraction steps per key block
     constexpr int NK = 2 * NS;  // K reads: block-major, step-minor
     constexpr int NO = 4 * NDB; // V reads / O products: step-major, column-block-minor
-        constexpr int PF = 4;
+    constexpr int PF = 4;
     // one read per product, issued in product order: r < NK reads K for S, r >= NK reads V for O
     uint4 rd[NK + NO];
     auto read = [&](int r) {

@@ -27,6 +27,7 @@ __all__ = [
     "library_path",
     "hstu_fwd",
     "hstu_bwd",
+    "hstu_bwd_workspace_size",
     "hstu_bwd_dq",
     "hstu_bwd_dkdv",
     "HSTU_OK",
@@ -43,7 +44,7 @@ HSTU_ERR_UNSUPPORTED = 2
 HSTU_ERR_DEVICE = 3
 HSTU_MASK_NONE = 0
 HSTU_MASK_CAUSAL = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -110,7 +111,9 @@ def library() -> ctypes.CDLL:
             lib.hstu_fwd.restype = ctypes.c_int
             lib.hstu_fwd.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_bwd.restype = ctypes.c_int
-            lib.hstu_bwd.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_bwd.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            lib.hstu_bwd_workspace_size.restype = ctypes.c_int
+            lib.hstu_bwd_workspace_size.argtypes = [argp, ctypes.POINTER(ctypes.c_size_t)]
             lib.hstu_bwd_dq.restype = ctypes.c_int
             lib.hstu_bwd_dq.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_bwd_dkdv.restype = ctypes.c_int
@@ -232,9 +235,11 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
              scaling_seqlen: Optional[int] = None, causal: bool = True,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None, stream=None
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``."""
+    """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.  ``workspace``
+    (a device byte tensor) is allocated here when the library asks for one and
+    none is given."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
@@ -244,10 +249,26 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     _thd("dk", dk, int(k.shape[0]), H, D)
     _thd("dv", dv, int(k.shape[0]), H, D)
     a.dq, a.dk, a.dv = _stride(dq), _stride(dk), _stride(dv)
+    need = ctypes.c_size_t(0)
+    _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().hstu_bwd(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
                               _stream(stream, q.device)))
     return dq, dk, dv
+
+
+def hstu_bwd_workspace_size(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                            alpha=1.0, scaling_seqlen=None, causal=True) -> int:
+    """Bytes of device workspace ``hstu_bwd`` needs for this problem."""
+    _, _, _, _, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, alpha,
+                                scaling_seqlen, causal)
+    need = ctypes.c_size_t(0)
+    _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    return int(need.value)
 
 
 def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define HSTU_API __attribute__((visibility("default")))
@@ -132,11 +132,21 @@ HSTU_API hstu_status_t hstu_fwd(const hstu_args_t* args,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                        void* o, hipStream_t stream);
 
-/* Backward, all three gradients: enqueues hstu_bwd_dq then hstu_bwd_dkdv. */
+/* Device workspace, in bytes, that hstu_bwd needs for the problem in `args`
+ * (written to *bytes).  Reads scalars only.  The backward built here (two
+ * kernels, no atomics) needs none and reports 0; the call exists so that
+ * callers size and pass a workspace the same way for every backward variant. */
+HSTU_API hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* args, size_t* bytes);
+
+/* Backward, all three gradients: enqueues hstu_bwd_dq then hstu_bwd_dkdv.
+ * `workspace` is caller-owned device memory of at least
+ * hstu_bwd_workspace_size() bytes, 256-byte aligned; it may be null when that
+ * size is 0.  A smaller `workspace_bytes` is HSTU_ERR_INVALID_ARGUMENT. */
 HSTU_API hstu_status_t hstu_bwd(const hstu_args_t* args, const void* dout,
                        const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                       void* dq, void* dk, void* dv, hipStream_t stream);
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward, dQ only (one query-major kernel: recompute S, dS; dQ = alpha dS K). */
 HSTU_API hstu_status_t hstu_bwd_dq(const hstu_args_t* args, const void* dout,

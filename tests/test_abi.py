@@ -33,7 +33,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
-        "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dq", "hstu_fwd",
+        "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dq", "hstu_bwd_workspace_size", "hstu_fwd",
         "hstu_last_error", "hstu_status_string"])
 
 
@@ -111,7 +111,7 @@ def test_pointer_rejections(lib):
 def test_backward_rejections(lib):
     a = good_args()
     # dk and dv may not be one buffer
-    st = lib.hstu_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    st = lib.hstu_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
     assert st == hstu.HSTU_ERR_INVALID_ARGUMENT and b"same buffer" in lib.hstu_last_error()
     st = lib.hstu_bwd_dkdv(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == hstu.HSTU_ERR_INVALID_ARGUMENT
@@ -119,8 +119,16 @@ def test_backward_rejections(lib):
     st = lib.hstu_bwd_dq(ctypes.byref(a), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == hstu.HSTU_ERR_INVALID_ARGUMENT and b"dout is null" in lib.hstu_last_error()
     st = lib.hstu_bwd(ctypes.byref(good_args(head_dim=24)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                      FAKE + 16, FAKE + 32, None)
+                      FAKE + 16, FAKE + 32, None, 0, None)
     assert st == hstu.HSTU_ERR_UNSUPPORTED
+
+
+def test_backward_workspace_query(lib):
+    need = ctypes.c_size_t(123)
+    assert lib.hstu_bwd_workspace_size(ctypes.byref(good_args()), ctypes.byref(need)) == hstu.HSTU_OK
+    assert need.value == 0  # the two-kernel backward needs no workspace
+    assert lib.hstu_bwd_workspace_size(None, ctypes.byref(need)) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_workspace_size(ctypes.byref(good_args()), None) == hstu.HSTU_ERR_INVALID_ARGUMENT
 
 
 def test_binding_rejects_host_tensors():
