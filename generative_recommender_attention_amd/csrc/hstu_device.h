@@ -158,32 +158,41 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // M0 + 16 l.  Issued from inline assembly so that the compiler does not track
 // it: it inserts no waits of its own, and the caller orders the copy with
 // wait_global_loads() and a barrier.  `lds` and `gbase` must be wave-uniform.
+// The compiler's hazard recognizer cannot see that the assembly reads M0 and
+// the base SGPRs, so the padding is part of the statement: a vector memory
+// instruction that reads an SGPR written by a VALU instruction (the
+// v_readfirstlane that moves a base pointer computed in vector registers)
+// needs 5 wait states, and an LDS DMA needs 1 after a write of M0; s_nop 4
+// gives 5.
 __device__ __forceinline__ void dma16_lds(uint32_t lds, const void* gbase, uint32_t voff) {
-    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
                      : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase)));
 }
 
-// Staging of one 64-row tile of a (T, H, D) tensor by the 4 waves of a
-// workgroup with dma16_lds: each instruction fills one contiguous 1 KB chunk
-// (4 tile rows), lane l writing the 16 bytes at chunk + 16 l.  The swizzle is
-// applied on the global side: lane l fetches the logical unit that belongs at
-// its physical slot.  Rows at or past `valid_end` repeat the last valid row, so
-// the data stays finite; the kernels mask those rows out.
-template <int D>
+// Staging of one 64-row tile of a (T, H, D) tensor by NW waves with
+// dma16_lds: each instruction fills one contiguous 1 KB chunk (4 tile rows),
+// lane l writing the 16 bytes at chunk + 16 l; wave w of the NW fills chunks
+// w*CPW .. w*CPW + CPW - 1 (CPW = 16 / NW).  The swizzle is applied on the
+// global side: lane l fetches the logical unit that belongs at its physical
+// slot.  Rows at or past `valid_end` repeat the last valid row, so the data
+// stays finite; the kernels mask those rows out.
+template <int D, int NW = 4>
 struct TileDma {
-    uint32_t off[4];  // byte offset of this lane's source from the tile's row 0
-    int wave;         // 0..3 among the loading waves (wave-uniform)
+    static constexpr int CPW = 16 / NW;  // 1 KB chunks per wave
+    static_assert(NW * CPW == 16, "a tile is 16 chunks");
+    uint32_t off[CPW];  // byte offset of this lane's source from the tile's row 0
+    int wave;           // 0 .. NW-1 among the loading waves (wave-uniform)
     int lane;
 
-    __device__ __forceinline__ static int chunk_row(int wave, int i, int lane) { return 4 * (wave * 4 + i) + (lane >> 4); }
+    __device__ __forceinline__ static int chunk_row(int wave, int i, int lane) { return 4 * (wave * CPW + i) + (lane >> 4); }
     __device__ __forceinline__ static int chunk_col(int r, int lane) { return (lane & 15) ^ tile_swz(r); }
 
     __device__ __forceinline__ void init(int wave_, int lane_, int64_t tok) {
         wave = wave_;
         lane = lane_;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < CPW; ++i) {
             const int r = chunk_row(wave, i, lane);
             off[i] = (uint32_t)(2 * (r * tok + 8 * chunk_col(r, lane)));
         }
@@ -193,14 +202,14 @@ struct TileDma {
     __device__ __forceinline__ void issue(uint32_t tile, const uint16_t* base, int64_t tok, int row0,
                                           int valid_end) const {
         const uint16_t* src = base + (int64_t)row0 * tok;
-        const uint32_t dst = tile + (uint32_t)wave * 4096u;
+        const uint32_t dst = tile + (uint32_t)(wave * CPW) * 1024u;
         if (row0 + kTileRows <= valid_end) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < CPW; ++i)
                 if (D == 128 || chunk_col(chunk_row(wave, i, lane), lane) < D / 8) dma16_lds(dst + 1024 * i, src, off[i]);
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < CPW; ++i) {
                 const int r = chunk_row(wave, i, lane), c = chunk_col(r, lane);
                 if (D == 128 || c < D / 8) {
                     const int rr = min(r, valid_end - 1 - row0);
