@@ -220,6 +220,67 @@ struct TileDma {
     }
 };
 
+// Sum of x over the 64 lanes of the wave; every lane receives the sum.
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Work-item order for grids over (row block, sequence).  Sequence b of length
+// L_b = cu[b + 1] - cu[b] has n_b = ceil(L_b / BM) blocks.  The live blocks are
+// numbered in the order: block index m descending (for a causal mask the
+// blocks with the most key tiles come first), then sequence b ascending.
+// Numbering only the live blocks matters: a workgroup that exits at once still
+// holds its place in the dispatcher's in-order queue, and runs of such
+// workgroups at the front of a grid were measured to hold back the dispatch of
+// the live ones behind them (a quarter of the CU slots in use for most of a
+// kernel).  Launching the grid over the host-known bound nblk * B leaves the
+// surplus workgroups at the end, where they cost nothing.
+//
+// Item p -> (b, m), found by the wave without host help: with
+// C(m) = sum_b max(0, n_b - m) (the number of live blocks with index >= m),
+// m is the level with C(m + 1) <= p < C(m) (binary search), and b is the
+// (p - C(m + 1))-th sequence, in order, with n_b > m.  Every lane returns the
+// same values.  Returns false when p >= C(0).  Each step stays inside
+// [0, B) x [0, nblk), so inconsistent metadata cannot send it out of bounds.
+struct BlockItem {
+    int b, m;
+};
+__device__ __forceinline__ bool find_block(const int32_t* cu, int B, int BM, int nblk, int p, BlockItem& it) {
+    const int lane = threadIdx.x & 63;
+    auto nb = [&](int b) { return (cu[b + 1] - cu[b] + BM - 1) / BM; };
+    const int n0 = lane < B ? nb(lane) : 0;  // the first 64 sequences stay in a register
+    auto count_at_least = [&](int m) {  // C(m)
+        int s = max(0, n0 - m);
+        for (int b0 = 64; b0 < B; b0 += 64)
+            if (b0 + lane < B) s += max(0, nb(b0 + lane) - m);
+        return wave_sum(s);
+    };
+    if (p >= count_at_least(0)) return false;
+    int lo = 0, hi = nblk;  // C(lo) > p; C(hi) <= p once hi is reached from above
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (count_at_least(mid) > p) lo = mid;
+        else hi = mid;
+    }
+    int k = max(0, p - count_at_least(lo + 1));
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int n = b0 == 0 ? n0 : (b0 + lane < B ? nb(b0 + lane) : 0);
+        const uint64_t mask = __ballot(n > lo);
+        const int cnt = __popcll(mask);
+        if (k < cnt) {  // then mask has at least k + 1 set bits
+            uint64_t mm = mask;
+            for (int i = 0; i < k; ++i) mm &= mm - 1;  // drop the k lowest set bits
+            it.b = __builtin_amdgcn_readfirstlane(b0 + __builtin_ctzll(mm));
+            it.m = __builtin_amdgcn_readfirstlane(lo);
+            return true;
+        }
+        k -= cnt;
+    }
+    return false;
+}
+
 // Sequence bounds of batch entry b.
 struct SeqBounds {
     int q0, lq, k0, lk;

@@ -11,10 +11,10 @@
 // tiles of parity w >> 1: the two wave pairs run the even and the odd 64-key
 // tiles of the same rows, which halves the longest chain of tiles a workgroup
 // walks (the last rows of a long causal sequence), and add their partial O
-// through LDS at the end.  Grid = (row block, sequence, head) flattened with
-// the head fastest and the row block slowest in reverse, so the blocks with the
-// most key tiles start first.  A block past its sequence's end exits at once;
-// the host never reads the cumulative lengths.
+// through LDS at the end.  Grid = (live row block, head), head fastest, over
+// the live blocks in the order of find_block: block index descending, so the
+// blocks with the most key tiles start first; the host never reads the
+// cumulative lengths and the surplus workgroups sit at the end of the grid.
 //
 // Each wave pair stages its own tiles (64 keys x D of K and of V, row-major,
 // swizzled) into LDS with direct global->LDS loads issued from inline assembly,
@@ -57,17 +57,17 @@ __device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0,
     return pack_operand(pv);
 }
 
-// One 64-key tile for one wave of 64 query rows (two 32-row blocks rb).
-// Reads are issued in product order, PF reads ahead of the MFMAs that use them;
-// each read feeds the two row blocks' products.
-template <int D, bool MASKED>
-__device__ __forceinline__ void fwd_tile(uint32_t kt, uint32_t vt, const uint4 (&qf)[2][D / 16],
-                                         f32x16 (&oacc)[(D < 32 ? 32 : D) / 32][2], const uint32_t (&koff)[D / 16],
-                                         const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, const int (&lim)[2],
-                                         int g) {
+// One 64-key tile for one wave of 32 query rows.  S^T for the first 32 keys
+// (s0), then for the second 32 (s1); P^T of s0 is computed while s1's products
+// run, the first half of O^T += V^T P^T while P^T of s1 is computed.  Reads are
+// issued in product order, PF ahead of the MFMA that uses them.
+template <int D, bool MASKED, uint32_t kt, uint32_t vt>
+__device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
+                                         f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&koff)[D / 16],
+                                         const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, int lim, int g) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;  // 32-column blocks of O^T
     constexpr int NS = D / 16;                   // contraction steps per S^T block
-    constexpr int NK = 2 * NS;                   // K reads: half-major, step-minor
+    constexpr int NK = 2 * NS;                   // K reads: block-major, step-minor
     constexpr int NV = 4 * NDB;                  // V reads: key step-major, column block-minor
     constexpr int PF = 4;
     uint4 rd[NK + NV];
@@ -81,86 +81,66 @@ __device__ __forceinline__ void fwd_tile(uint32_t kt, uint32_t vt, const uint4 (
     };
 #pragma unroll
     for (int r = 0; r < PF; ++r) read(r);
-
-    f32x16 s0[2] = {f32x16{}, f32x16{}}, s1[2] = {f32x16{}, f32x16{}};
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        s0[0] = mfma32x32x16(rd[j], qf[0][j], s0[0]);
-        s0[1] = mfma32x32x16(rd[j], qf[1][j], s0[1]);
+    for (int j = 0; j < NK; ++j) {
+        if (j < NS) s0 = mfma32x32x16(rd[j], qf[j], s0);
+        else s1 = mfma32x32x16(rd[j], qf[j - NS], s1);
         read(j + PF);
     }
-#pragma unroll
-    for (int j = NS; j < NK; ++j) {
-        s1[0] = mfma32x32x16(rd[j], qf[0][j - NS], s1[0]);
-        s1[1] = mfma32x32x16(rd[j], qf[1][j - NS], s1[1]);
-        read(j + PF);
-    }
-    uint4 p0[2][2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) p0[rb][kk] = silu_operand<MASKED>(s0[rb], 8 * kk, n0, lim[rb], g);
+    const uint4 p0 = silu_operand<MASKED>(s0, 0, n0, lim, g);
+    const uint4 p1 = silu_operand<MASKED>(s0, 8, n0, lim, g);
 #pragma unroll
     for (int i = 0; i < 2 * NDB; ++i) {
-        const int kk = i / NDB, db = i % NDB;
-        oacc[db][0] = mfma32x32x16(rd[NK + i], p0[0][kk], oacc[db][0]);
-        oacc[db][1] = mfma32x32x16(rd[NK + i], p0[1][kk], oacc[db][1]);
+        oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < NDB ? p0 : p1, oacc[i % NDB]);
         read(NK + i + PF);
     }
-    uint4 p1[2][2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) p1[rb][kk] = silu_operand<MASKED>(s1[rb], 8 * kk, n0 + 32, lim[rb], g);
+    const uint4 p2 = silu_operand<MASKED>(s1, 0, n0 + 32, lim, g);
+    const uint4 p3 = silu_operand<MASKED>(s1, 8, n0 + 32, lim, g);
 #pragma unroll
     for (int i = 2 * NDB; i < NV; ++i) {
-        const int kk = i / NDB - 2, db = i % NDB;
-        oacc[db][0] = mfma32x32x16(rd[NK + i], p1[0][kk], oacc[db][0]);
-        oacc[db][1] = mfma32x32x16(rd[NK + i], p1[1][kk], oacc[db][1]);
+        oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < 3 * NDB ? p2 : p3, oacc[i % NDB]);
         read(NK + i + PF);
     }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(AttnParams p) {
+template <int D, bool CAUSAL, int KSPLIT>
+__global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParams p) {
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int NDB = DM / 32;
     constexpr int KSTEPS = D / 16;
-    // [pair 0: K slot 0 | K slot 1 | V slot 0 | V slot 1][pair 1: same]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[8 * kTileElems];
+    // [group 0: K slot 0 | K slot 1 | V slot 0 | V slot 1][group 1: same]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * KSPLIT * kTileElems];
     const uint32_t lds0 = lds_addr(smem);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-    const int rg = wave & 1;   // row half of the block
-    const int kg = wave >> 1;  // key tile parity, and wave pair
+    const int rb = wave & 3;   // 32-row block of the workgroup's rows
+    const int kg = KSPLIT == 1 ? 0 : wave >> 2;  // key tile parity, and wave group
     const uint32_t grp = lds0 + (uint32_t)kg * kGroupBytes;
 
-    int idx = blockIdx.x;
-    const int h = idx % p.heads;
-    idx /= p.heads;
-    const int b = idx % p.batch;
-    const int m = p.nblk - 1 - idx / p.batch;
+    // workgroup -> (live row block, head), head fastest; surplus workgroups exit
+    const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
+    BlockItem item;
+    if (!find_block(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BM;
-    if (m0 >= sb.lq) return;
 
     const int kv_end = CAUSAL ? min(sb.lk, m0 + BM) : sb.lk;
     const int ntiles = (kv_end + BN - 1) / BN;
-    const int row0 = m0 + 64 * rg;  // first row of this wave
+    const int row0 = m0 + 32 * rb;  // first row of this wave
+    const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
-    int lim[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) lim[rb] = CAUSAL ? min(kv_end, row0 + 32 * rb + l32 + 1) : kv_end;
+    const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
 
-    uint4 qf[2][KSTEPS];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int r = min(row0 + 32 * rb + l32, sb.lq - 1);
+    uint4 qf[KSTEPS];
+    {
+        const int r = min(my_row, sb.lq - 1);
         const uint16_t* src = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qf[rb][kk] = scale_bf16x8(ld_global16(src + 16 * kk), p.exp_c);
+        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = scale_bf16x8(ld_global16(src + 16 * kk), p.exp_c);
     }
     uint32_t koff[KSTEPS];
 #pragma unroll
@@ -172,20 +152,20 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(AttnParams p) {
         voff[db].x += grp + 2 * kTileBytes;
         voff[db].y += grp + 2 * kTileBytes;
     }
-    f32x16 oacc[NDB][2];
+    f32x16 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db][0] = oacc[db][1] = f32x16{};
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
     if (ntiles > 0) {
         const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
         const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
-        TileDma<D, 2> kdma, vdma;
-        kdma.init(rg, lane, p.k.tok);
-        vdma.init(rg, lane, p.v.tok);
+        TileDma<D> kdma, vdma;
+        kdma.init(rb, lane, p.k.tok);
+        vdma.init(rb, lane, p.v.tok);
         if constexpr (D < 32) {
             // columns D..31 of every slot are read by the 32-wide MFMA blocks
             constexpr int U = kTileRows * (32 - D) / 8;  // 16-byte units per slot
-            for (int u = tid; u < 8 * U; u += 256) {
+            for (int u = tid; u < 4 * KSPLIT * U; u += 256 * KSPLIT) {
                 const int sl = u / U, v = u % U;
                 const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
                 ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
@@ -198,91 +178,98 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(AttnParams p) {
         wait_global_loads();
         __syncthreads();
 
-        // Every step but the last is free of masking for every wave: for a causal
-        // block m the first tile that crosses a wave's diagonal is tile 2m, in the
-        // last step; without a causal mask only the last tile can pass the
-        // sequence end.  The last step runs the masked variant for all waves.
-        const int nsteps = (ntiles + 1) / 2;
-        auto step = [&](int s, auto masked) {
-            const int t = 2 * s + kg;  // this pair's tile
-            const uint32_t cur = (uint32_t)(s & 1) * kTileBytes, nxt = kTileBytes - cur;
-            if (t + 2 < ntiles) {  // the other slots were last read before the previous barrier
-                kdma.issue(grp + nxt, kbase, p.k.tok, (t + 2) * BN, kv_end);
-                vdma.issue(grp + 2 * kTileBytes + nxt, vbase, p.v.tok, (t + 2) * BN, kv_end);
+        // Step s: group kg computes tile t = KSPLIT s + kg from slot s % 2 while the
+        // tile after it (t + KSPLIT) streams into the other slot.  Only the tiles
+        // that cross a wave's diagonal or the sequence end need the per-element
+        // mask, and those are the block's last two tiles: for a causal block m the
+        // first tile crossing a diagonal is tile 2m of 2m + 2; without a causal
+        // mask only the last tile can pass the sequence end.  They fall in the
+        // last step when two groups split the tiles, in the last two otherwise.
+        // Slots alternate at compile time so that every LDS offset is an immediate.
+        const int nsteps = (ntiles + KSPLIT - 1) / KSPLIT;
+        const int nplain = nsteps - min(nsteps, KSPLIT == 1 ? 2 : 1);
+        auto step = [&](int s, auto slot, auto masked) {
+            constexpr uint32_t cur = decltype(slot)::value * kTileBytes, nxt = kTileBytes - cur;
+            const int t = KSPLIT * s + kg;  // this group's tile
+            if (t + KSPLIT < ntiles) {  // the other slots were last read before the previous barrier
+                kdma.issue(grp + nxt, kbase, p.k.tok, (t + KSPLIT) * BN, kv_end);
+                vdma.issue(grp + 2 * kTileBytes + nxt, vbase, p.v.tok, (t + KSPLIT) * BN, kv_end);
             }
             const int n0 = t * BN;
             // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
-            if (t < ntiles && wave_live && !(CAUSAL && n0 > row0 + 63))
-                fwd_tile<D, decltype(masked)::value>(cur, cur, qf, oacc, koff, voff, n0, lim, g);
+            if (t < ntiles && wave_live && !(CAUSAL && n0 > row0 + 31))
+                fwd_tile<D, decltype(masked)::value, cur, cur>(qf, oacc, koff, voff, n0, lim, g);
             wait_global_loads();
             __syncthreads();
         };
-        for (int s = 0; s + 1 < nsteps; ++s) step(s, std::false_type{});
-        step(nsteps - 1, std::true_type{});
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        for (int s = 0; s < nplain; s += 2) {
+            step(s, S0{}, std::false_type{});
+            if (s + 1 < nplain) step(s + 1, S1{}, std::false_type{});
+        }
+        for (int s = nplain; s < nsteps; ++s) {
+            if (s & 1) step(s, S1{}, std::true_type{});
+            else step(s, S0{}, std::true_type{});
+        }
 
-        // the odd-tile pair hands its partial sums to the even-tile pair through LDS
-        if (ntiles > 1) {
-            const uint32_t red = lds0 + (uint32_t)rg * (NDB * 2 * 16 * 64 * 4) + 16u * lane;
+        // the odd-tile group hands its partial sums to the even-tile group through LDS
+        if (KSPLIT > 1 && ntiles > 1) {
+            const uint32_t red = lds0 + (uint32_t)rb * (NDB * 16 * 64 * 4) + 16u * lane;
             if (kg == 1) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f32x16& a = oacc[db][rb];
-                            ds_write16(red + (uint32_t)(((db * 2 + rb) * 4 + j) * 1024),
-                                       make_uint4(__float_as_uint(a[4 * j]), __float_as_uint(a[4 * j + 1]),
-                                                  __float_as_uint(a[4 * j + 2]), __float_as_uint(a[4 * j + 3])));
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x16& a = oacc[db];
+                        ds_write16(red + (uint32_t)((db * 4 + j) * 1024),
+                                   make_uint4(__float_as_uint(a[4 * j]), __float_as_uint(a[4 * j + 1]),
+                                              __float_as_uint(a[4 * j + 2]), __float_as_uint(a[4 * j + 3])));
+                    }
             }
             __syncthreads();
             if (kg == 0) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint4 w = ds_read16(red + (uint32_t)(((db * 2 + rb) * 4 + j) * 1024));
-                            oacc[db][rb][4 * j] += __uint_as_float(w.x);
-                            oacc[db][rb][4 * j + 1] += __uint_as_float(w.y);
-                            oacc[db][rb][4 * j + 2] += __uint_as_float(w.z);
-                            oacc[db][rb][4 * j + 3] += __uint_as_float(w.w);
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 w = ds_read16(red + (uint32_t)((db * 4 + j) * 1024));
+                        oacc[db][4 * j] += __uint_as_float(w.x);
+                        oacc[db][4 * j + 1] += __uint_as_float(w.y);
+                        oacc[db][4 * j + 2] += __uint_as_float(w.z);
+                        oacc[db][4 * j + 3] += __uint_as_float(w.w);
+                    }
             }
         }
     }
 
-    if (kg != 0) return;
+    if (kg != 0 || my_row >= sb.lq) return;
+    uint16_t* dst = p.o.base + (int64_t)(sb.q0 + my_row) * p.o.tok + (int64_t)h * p.o.head;
     const float sc = p.pre_scale;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int my_row = row0 + 32 * rb + l32;
-        if (my_row < sb.lq) {
-            uint16_t* dst = p.o.base + (int64_t)(sb.q0 + my_row) * p.o.tok + (int64_t)h * p.o.head;
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int d0 = db * 32 + 8 * rq + 4 * g;
-                    if (d0 < D) {
-                        const f32x16& a = oacc[db][rb];
-                        const uint2 w = make_uint2(pack_bf16x2(a[4 * rq] * sc, a[4 * rq + 1] * sc),
-                                                   pack_bf16x2(a[4 * rq + 2] * sc, a[4 * rq + 3] * sc));
-                        *reinterpret_cast<uint2*>(dst + d0) = w;
-                    }
-                }
+        for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = db * 32 + 8 * rq + 4 * g;
+            if (d0 < D) {
+                const f32x16& a = oacc[db];
+                const uint2 w = make_uint2(pack_bf16x2(a[4 * rq] * sc, a[4 * rq + 1] * sc),
+                                           pack_bf16x2(a[4 * rq + 2] * sc, a[4 * rq + 3] * sc));
+                *reinterpret_cast<uint2*>(dst + d0) = w;
             }
         }
     }
 }
 
+#ifndef HSTU_FWD_KSPLIT
+#define HSTU_FWD_KSPLIT 1
+#endif
 template <int D, bool CAUSAL>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
+    constexpr int KSPLIT = HSTU_FWD_KSPLIT;
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, KSPLIT>), dim3((unsigned)grid), dim3(256 * KSPLIT), 0, stream, p);
     return hipGetLastError();
 }
 
