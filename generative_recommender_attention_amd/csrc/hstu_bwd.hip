@@ -145,11 +145,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
-    int idx = blockIdx.x;
-    const int h = idx % p.heads;
-    idx /= p.heads;
-    const int b = idx % p.batch;
-    const int m = p.nblk - 1 - idx / p.batch;
+    // workgroup -> (live row block, head), head fastest, blocks with the most key tiles first
+    const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
+    BlockItem item;
+    if (!find_block<true>(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BM;
     if (m0 >= sb.lq) return;
@@ -323,11 +323,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int kw = wave & 3, qh = wave >> 2;  // key sub-block, row half of each tile
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
 
-    int idx = blockIdx.x;
-    const int h = idx % p.heads;
-    idx /= p.heads;
-    const int b = idx % p.batch;
-    const int n = idx / p.batch;
+    // workgroup -> (live key block, head), head fastest, blocks with the most query tiles first
+    const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
+    BlockItem item;
+    if (!find_block<false>(p.cu_k, p.batch, BNK, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int b = item.b, n = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int n0 = n * BNK;
     if (n0 >= sb.lk) return;

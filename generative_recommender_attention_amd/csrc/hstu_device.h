@@ -227,53 +227,59 @@ __device__ __forceinline__ int wave_sum(int x) {
     return x;
 }
 
-// Work-item order for grids over (row block, sequence).  Sequence b of length
-// L_b = cu[b + 1] - cu[b] has n_b = ceil(L_b / BM) blocks.  The live blocks are
-// numbered in the order: block index m descending (for a causal mask the
-// blocks with the most key tiles come first), then sequence b ascending.
-// Numbering only the live blocks matters: a workgroup that exits at once still
-// holds its place in the dispatcher's in-order queue, and runs of such
-// workgroups at the front of a grid were measured to hold back the dispatch of
-// the live ones behind them (a quarter of the CU slots in use for most of a
-// kernel).  Launching the grid over the host-known bound nblk * B leaves the
-// surplus workgroups at the end, where they cost nothing.
+// Work-item order for grids over (block, sequence).  Sequence b of length
+// L_b = cu[b + 1] - cu[b] has n_b = ceil(L_b / BM) blocks of BM rows.  The live
+// blocks are numbered level by level, block index m descending (DESC: for a
+// causal mask the query blocks with the most key tiles come first) or ascending
+// (the key blocks with the most query tiles come first), and by sequence b
+// within a level.  Numbering only the live blocks matters: a workgroup that
+// exits at once still holds its place in the dispatcher's in-order queue, and
+// runs of such workgroups at the front of a grid were measured to hold back the
+// dispatch of the live ones behind them (a quarter of the CU slots in use for
+// most of a kernel).  Launching the grid over the host-known bound nblk * B
+// leaves the surplus workgroups at the end, where they cost nothing.
 //
-// Item p -> (b, m), found by the wave without host help: with
-// C(m) = sum_b max(0, n_b - m) (the number of live blocks with index >= m),
-// m is the level with C(m + 1) <= p < C(m) (binary search), and b is the
-// (p - C(m + 1))-th sequence, in order, with n_b > m.  Every lane returns the
-// same values.  Returns false when p >= C(0).  Each step stays inside
-// [0, B) x [0, nblk), so inconsistent metadata cannot send it out of bounds.
+// Item p -> (b, m), found by the wave without host help: with level l holding
+// block index m(l) = DESC ? nblk - 1 - l : l and before(l) the number of live
+// blocks on the levels below l, the level is the l with
+// before(l) <= p < before(l + 1) (binary search; before is a lane-parallel sum
+// over the sequences) and b is the (p - before(l))-th sequence, in order, with
+// n_b > m(l).  Every lane returns the same values.  Returns false when p is
+// past the last live block.  Each step stays inside [0, B) x [0, nblk), so
+// inconsistent metadata cannot send it out of bounds.
 struct BlockItem {
     int b, m;
 };
+template <bool DESC>
 __device__ __forceinline__ bool find_block(const int32_t* cu, int B, int BM, int nblk, int p, BlockItem& it) {
     const int lane = threadIdx.x & 63;
     auto nb = [&](int b) { return (cu[b + 1] - cu[b] + BM - 1) / BM; };
     const int n0 = lane < B ? nb(lane) : 0;  // the first 64 sequences stay in a register
-    auto count_at_least = [&](int m) {  // C(m)
-        int s = max(0, n0 - m);
+    auto below = [&](int n, int l) { return DESC ? max(0, n - (nblk - l)) : min(n, l); };
+    auto before = [&](int l) {
+        int s = below(n0, l);
         for (int b0 = 64; b0 < B; b0 += 64)
-            if (b0 + lane < B) s += max(0, nb(b0 + lane) - m);
+            if (b0 + lane < B) s += below(nb(b0 + lane), l);
         return wave_sum(s);
     };
-    if (p >= count_at_least(0)) return false;
-    int lo = 0, hi = nblk;  // C(lo) > p; C(hi) <= p once hi is reached from above
+    if (p >= before(nblk)) return false;
+    int lo = 0, hi = nblk;  // before(lo) <= p < before(hi)
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (count_at_least(mid) > p) lo = mid;
+        if (before(mid) <= p) lo = mid;
         else hi = mid;
     }
-    int k = max(0, p - count_at_least(lo + 1));
+    const int m = DESC ? nblk - 1 - lo : lo;
+    int k = max(0, p - before(lo));
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int n = b0 == 0 ? n0 : (b0 + lane < B ? nb(b0 + lane) : 0);
-        const uint64_t mask = __ballot(n > lo);
+        const uint64_t mask = __ballot(n > m);
         const int cnt = __popcll(mask);
         if (k < cnt) {  // then mask has at least k + 1 set bits
             uint64_t mm = mask;
             for (int i = 0; i < k; ++i) mm &= mm - 1;  // drop the k lowest set bits
             it.b = __builtin_amdgcn_readfirstlane(b0 + __builtin_ctzll(mm));
-            it.m = __builtin_amdgcn_readfirstlane(lo);
+            it.m = __builtin_amdgcn_readfirstlane(m);
             return true;
         }
         k -= cnt;

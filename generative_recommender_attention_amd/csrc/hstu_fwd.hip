@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParam
     // workgroup -> (live row block, head), head fastest; surplus workgroups exit
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
     BlockItem item;
-    if (!find_block(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    if (!find_block<true>(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BM;
