@@ -81,6 +81,91 @@ def load_traffic(kernel: str):
     return int(k["hbm_bytes_per_launch"])
 
 
+PROFILE_COMMANDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cfetch -o run -- python3 bench.py --calibrate-copy-mib 256",
+    "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cwrite -o run -- python3 bench.py --calibrate-copy-mib 256",
+}
+ALG_TENSORS = {"fwd_kernel": 4, "bwd_dq_kernel": 5, "bwd_dkdv_kernel": 6}  # (T, H, D) bf16 tensors read + written
+
+
+def summarize_profiles(prof_dir: str, workload: str) -> None:
+    """Turn the rocprofv3 outputs of PROFILE_COMMANDS (run from the repository root,
+    prof_dir relative to it) into profiles/traffic.json and the two text summaries."""
+    import csv
+    import glob
+
+    def rows(sub, pattern):
+        out = []
+        for path in glob.glob(os.path.join(prof_dir, sub, "**", pattern), recursive=True):
+            with open(path) as f:
+                out.extend(csv.DictReader(f))
+        if not out:
+            raise SystemExit(f"no {pattern} under {os.path.join(prof_dir, sub)}")
+        return out
+
+    def counter_kib(sub, counter, match):
+        vals = {}
+        for r in rows(sub, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            name = next((m for m in match if m in r["Kernel_Name"]), None)
+            if name and ("<128," in r["Kernel_Name"] or "copyBuffer" in name):
+                vals.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: float(np.mean(v)) for k, v in vals.items()}
+
+    kernels = list(ALG_TENSORS)
+    copy = ["copyBuffer"]
+    fetch, write = counter_kib("fetch", "FETCH_SIZE", kernels), counter_kib("write", "WRITE_SIZE", kernels)
+    cfetch, cwrite = counter_kib("cfetch", "FETCH_SIZE", copy), counter_kib("cwrite", "WRITE_SIZE", copy)
+    copy_kib = 256 * 1024.0
+    ff, wf = copy_kib / cfetch["copyBuffer"], copy_kib / cwrite["copyBuffer"]
+    from generative_recommender_attention_amd.workloads import named_workload
+
+    wl = named_workload(workload)
+    tensor_bytes = wl.total_q * wl.num_heads * wl.head_dim * 2
+    traffic = {"source_digest": kernel_source_digest(), "workload": workload, "fetch_factor": ff, "write_factor": wf,
+               "kernels": {}}
+    lines = [f"# HBM traffic per dispatch (rocprofv3 PMC), workload {workload}", "",
+             "Commands (GPU box, repository root; one counter per pass):"]
+    lines += ["    " + PROFILE_COMMANDS[k].format(d=prof_dir) for k in ("fetch", "write", "cfetch", "cwrite")]
+    lines += ["", f"copy of {copy_kib:.0f} KiB (the HIP runtime's __amd_rocclr_copyBuffer): FETCH_SIZE reads "
+                  f"{cfetch['copyBuffer']:.1f} KiB -> fetch factor {ff:.4f}",
+              f"{'':48s}WRITE_SIZE reads {cwrite['copyBuffer']:.1f} KiB -> write factor {wf:.4f}", "",
+              f"{'kernel':18s}{'FETCH KiB':>12s}{'WRITE KiB':>12s}{'HBM MB (scaled)':>18s}{'algorithmic MB':>16s}{'ratio':>8s}"]
+    for k in kernels:
+        hbm = (fetch[k] * ff + write[k] * wf) * 1024.0
+        alg = ALG_TENSORS[k] * tensor_bytes
+        traffic["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write[k], "hbm_bytes_per_launch": int(hbm),
+                                 "algorithmic_bytes_per_launch": alg}
+        lines.append(f"{k:18s}{fetch[k]:12.1f}{write[k]:12.1f}{hbm / 1e6:18.1f}{alg / 1e6:16.1f}{hbm / alg:8.2f}")
+    lines += ["", "Algorithmic bytes: fwd reads q, k, v and writes o (4 tensors); dq kernel reads q, do, k, v and",
+              "writes dq (5); dk/dv kernel reads q, do, k, v and writes dk, dv (6); each tensor T*H*D*2 = "
+              f"{tensor_bytes} bytes."]
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_hbm_traffic.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    stats = rows("kt", "*kernel_stats.csv")
+    out = [f"# rocprofv3 kernel trace: HSTU attention fwd + bwd, workload {workload}", "",
+           f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
+           f"{'causal' if wl.causal else 'no mask'}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
+           "hstu_bwd_dq + hstu_bwd_dkdv.", "", "Command (GPU box, from the repository root):",
+           "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir), "",
+           f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        short = next((k for k in kernels if k in name), name.split("(")[0][-26:])
+        out.append(f"{short:26s}{int(r['Calls']):8d}{float(r['AverageNs']):11.0f}{float(r['MinNs']):11.0f}"
+                   f"{float(r['MaxNs']):11.0f}{float(r['Percentage']):7.1f}%")
+    with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(f"wrote profiles/traffic.json and the summaries for {workload}")
+
+
 def cpu_baseline(wl, max_pairs: int):
     """Time the fp64 oracle (fwd + bwd) on whole sequences of the workload whose
     visible pairs add up to at most ``max_pairs`` (shortest first)."""
@@ -129,10 +214,15 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-max-pairs", type=int, default=0,
                     help="bound on the oracle sample in visible pairs per head (0: the whole workload, "
                          "about 15 s on 16 host threads for the default workload)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="only write profiles/ from the rocprofv3 outputs under DIR (see PROFILE_COMMANDS)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC byte-counter calibration)")
     args = ap.parse_args(argv)
 
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
                                    "(every (sequence, head) pair is independent; see the sharding design notes)"}))
