@@ -15,13 +15,15 @@ lengths are drawn first (unless fixed), then q, k, v, each as
 round-to-nearest-even, then (for the backward workload) the upstream gradient
 ``standard_normal((T, H, D), float32)`` rounded the same way.  Key lengths equal
 query lengths; the score scale is the fp32 value of ``1/sqrt(D)``; the
-normaliser ``scaling_seqlen`` is the longest query length.
+normaliser ``scaling_seqlen`` is the longest query length.  The mask is causal
+or full (``causal``) unless a token window ``(left, right)`` is given (HSTU
+Attention page, "Mask support": ``window_size``, -1 = unbounded side).
 """
 
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -75,6 +77,23 @@ class Workload:
     k: np.ndarray                  # (T_k, H, D) uint16
     v: np.ndarray                  # (T_k, H, D) uint16
     do: Optional[np.ndarray] = None  # (T_q, H, D) uint16, backward only
+    window: Optional[Tuple[int, int]] = None  # (left, right); None: causal / full per `causal`
+
+    @property
+    def window_size(self) -> Tuple[int, int]:
+        """The mask as a (left, right) token window, -1 = unbounded."""
+        if self.window is not None:
+            return self.window
+        return (-1, 0) if self.causal else (-1, -1)
+
+    @property
+    def mask_name(self) -> str:
+        left, right = self.window_size
+        if (left, right) == (-1, -1):
+            return "none"
+        if (left, right) == (-1, 0):
+            return "causal"
+        return f"window({left},{right})"
 
     @property
     def batch(self) -> int:
@@ -125,6 +144,7 @@ def make_workload(
     alpha: Optional[float] = None,
     scaling_seqlen: Optional[int] = None,
     rng: Optional[np.random.Generator] = None,
+    window: Optional[Tuple[int, int]] = None,
 ) -> Workload:
     """Build a workload from explicit lengths.
 
@@ -139,6 +159,10 @@ def make_workload(
         raise ValueError("lengths_q/lengths_k must be 1-D of equal length")
     if np.any(lq < 0) or np.any(lk < 0):
         raise ValueError("negative sequence length")
+    if window is not None:
+        window = (int(window[0]), int(window[1]))
+        if min(window) < -1:
+            raise ValueError("window bounds must be >= -1")
     cu_q = _cumulative(lq)
     cu_k = _cumulative(lk)
     tq, tk = int(cu_q[-1]), int(cu_k[-1])
@@ -168,10 +192,11 @@ def make_workload(
         k=k,
         v=v,
         do=do,
+        window=window,
     )
 
 
-# The five synthetic workloads the measurement is defined on.  Names say what
+# The six synthetic workloads the measurement is defined on.  Names say what
 # they are: batch, length law, heads, head dim and mask.
 WORKLOAD_NAMES = (
     "tiny_b2_h1_d16_causal",          # B=2, lengths [5, 11]
@@ -179,11 +204,12 @@ WORKLOAD_NAMES = (
     "zipf_b32_h4_d128_causal",        # B=32, Zipf(1.2) clipped to [16, 4096]
     "long_b4_h8_d128_causal",         # B=4, lengths U[8192, 16384]
     "zipf_b32_h4_d128_causal_fwdbwd",  # the Zipf workload plus an upstream gradient
+    "long_b4_h8_d128_window1024",      # the long workload, sliding window (1024, 0), with gradient
 )
 
 
 def named_workload(name: str) -> Workload:
-    """Return one of the five synthetic workloads, fully deterministic."""
+    """Return one of the six synthetic workloads, fully deterministic."""
     if name == "tiny_b2_h1_d16_causal":
         return make_workload(name, 0, [5, 11], 1, 16, True, 1.0)
     if name == "uniform_b8_h2_d64_full":
@@ -199,4 +225,8 @@ def named_workload(name: str) -> Workload:
         rng = np.random.default_rng(3)
         lens = rng.integers(8192, 16384, size=4, endpoint=True)
         return make_workload(name, 3, lens, 8, 128, True, 0.5, rng=rng)
+    if name == "long_b4_h8_d128_window1024":
+        rng = np.random.default_rng(3)
+        lens = rng.integers(8192, 16384, size=4, endpoint=True)
+        return make_workload(name, 3, lens, 8, 128, False, 0.5, rng=rng, with_do=True, window=(1024, 0))
     raise KeyError(f"unknown workload {name!r}; known: {WORKLOAD_NAMES}")

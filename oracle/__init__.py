@@ -12,7 +12,9 @@ fp64 widening of the fp32 value the GPU receives.
 
 Every function takes packed ``(T, H, D)`` arrays and int32 cumulative offsets
 (HSTU Attention page, "Tensor layout") and returns fp64 arrays of the requested
-rows.  ``rows=None`` computes every row.
+rows.  ``rows=None`` computes every row.  ``mask`` is the page's
+``window_size=(left, right)`` ("Mask support"), -1 leaving a side unbounded;
+``True`` stands for causal ``(-1, 0)`` and ``False`` for full ``(-1, -1)``.
 """
 
 from __future__ import annotations
@@ -59,15 +61,15 @@ def _load():
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_hstu_fwd.restype = ctypes.c_int
             lib.oracle_hstu_fwd.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p,
-                                            ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                            ctypes.c_double, ctypes.c_double, i64, i64,
                                             i64p, i64, f64p]
             lib.oracle_hstu_bwd_dq.restype = ctypes.c_int
             lib.oracle_hstu_bwd_dq.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
-                                               ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                               ctypes.c_double, ctypes.c_double, i64, i64,
                                                i64p, i64, f64p]
             lib.oracle_hstu_bwd_dkdv.restype = ctypes.c_int
             lib.oracle_hstu_bwd_dkdv.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
-                                                 ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                                 ctypes.c_double, ctypes.c_double, i64, i64,
                                                  i64p, i64, f64p, f64p]
             _lib = lib
     return _lib
@@ -94,6 +96,16 @@ def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+def window(mask) -> Tuple[int, int]:
+    """(left, right) of a mask given as a bool (causal / full) or a window pair."""
+    if isinstance(mask, (bool, np.bool_)):
+        return (-1, 0) if mask else (-1, -1)
+    left, right = (int(x) for x in mask)
+    if left < -1 or right < -1:
+        raise ValueError("window bounds must be >= -1")
+    return left, right
+
+
 def _prep(cu_q, cu_k, q, k, v, rows, total):
     cu_q = np.ascontiguousarray(cu_q, dtype=np.int32)
     cu_k = np.ascontiguousarray(cu_k, dtype=np.int32)
@@ -113,7 +125,7 @@ def _prep(cu_q, cu_k, q, k, v, rows, total):
     return cu_q, cu_k, q, k, v, rows_arr, n
 
 
-def fwd(cu_q, cu_k, q, k, v, alpha, scaling_seqlen, causal: bool,
+def fwd(cu_q, cu_k, q, k, v, alpha, scaling_seqlen, mask,
         rows: Optional[np.ndarray] = None) -> np.ndarray:
     """O rows (fp64, shape (n, H, D)) of HSTU attention."""
     cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, q.shape[0])
@@ -122,7 +134,7 @@ def fwd(cu_q, cu_k, q, k, v, alpha, scaling_seqlen, causal: bool,
     rc = _load().oracle_hstu_fwd(
         cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
         _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
-        float(alpha), float(scaling_seqlen), int(bool(causal)),
+        float(alpha), float(scaling_seqlen), *window(mask),
         None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
         _ptr(out, ctypes.c_double))
     if rc != 0:
@@ -130,7 +142,7 @@ def fwd(cu_q, cu_k, q, k, v, alpha, scaling_seqlen, causal: bool,
     return out
 
 
-def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
+def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
            rows: Optional[np.ndarray] = None) -> np.ndarray:
     """dQ rows (fp64) given the upstream gradient ``dout``."""
     cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, q.shape[0])
@@ -142,7 +154,7 @@ def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
     rc = _load().oracle_hstu_bwd_dq(
         cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
         _ptr(dout, ctypes.c_double), _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
-        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), int(bool(causal)),
+        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), *window(mask),
         None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
         _ptr(out, ctypes.c_double))
     if rc != 0:
@@ -150,7 +162,7 @@ def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
     return out
 
 
-def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
+def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
              rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """(dK, dV) rows (fp64) for packed key rows ``rows``."""
     cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, k.shape[0])
@@ -163,7 +175,7 @@ def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
     rc = _load().oracle_hstu_bwd_dkdv(
         cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
         _ptr(dout, ctypes.c_double), _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
-        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), int(bool(causal)),
+        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), *window(mask),
         None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
         _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
     if rc != 0:
@@ -174,7 +186,7 @@ def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, causal: bool,
 def fwd_workload(wl, rows=None) -> np.ndarray:
     """Oracle O for a ``Workload`` (its bf16 inputs widened exactly)."""
     return fwd(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.q, wl.k, wl.v,
-               float(wl.alpha), wl.scaling_seqlen, wl.causal, rows)
+               float(wl.alpha), wl.scaling_seqlen, wl.window_size, rows)
 
 
 def bwd_workload(wl, rows_q=None, rows_k=None):
@@ -182,9 +194,9 @@ def bwd_workload(wl, rows_q=None, rows_k=None):
     if wl.do is None:
         raise ValueError("workload has no upstream gradient")
     dq = bwd_dq(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, wl.q, wl.k, wl.v,
-                float(wl.alpha), wl.scaling_seqlen, wl.causal, rows_q)
+                float(wl.alpha), wl.scaling_seqlen, wl.window_size, rows_q)
     dk, dv = bwd_dkdv(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, wl.q, wl.k, wl.v,
-                      float(wl.alpha), wl.scaling_seqlen, wl.causal, rows_k)
+                      float(wl.alpha), wl.scaling_seqlen, wl.window_size, rows_k)
     return dq, dk, dv
 
 

@@ -12,13 +12,22 @@
  *
  * with no softmax and no row normalisation ("Overview", the paragraph after the
  * equations).  Packed THD layout and cumulative offsets follow the page's
- * "Tensor layout" table.  The mask M is the page's "Mask support" table
- * restricted to full attention (window (-1,-1)) and causal (window (-1,0)).
+ * "Tensor layout" table.  The mask M is the page's "Mask support" table: a
+ * token window (left, right) in which -1 leaves a side unbounded, so (-1,-1) is
+ * full attention, (-1,0) causal, and finite bounds give a local (sliding)
+ * window.
  *
  * Readings where the page is silent (each is listed in the design notes):
- *  - causal is top-left aligned inside each sequence: key j is visible to query
- *    i (both local indices) iff j <= i.  All measured workloads have equal query
- *    and key lengths, where top-left and bottom-right agree;
+ *  - window_size follows the FlashAttention-2 convention, the one the cuDNN
+ *    SDPA page maps its own diagonal band bounds onto (PyTorch custom ops,
+ *    the band conventions): key j is visible to query i iff
+ *    i - left <= j <= i + right, a negative bound dropping its side.  In the
+ *    SDPA page's terms our left is its left bound minus one and our right is
+ *    its right bound; (-1, 0) is then exactly causal, as the HSTU page says;
+ *  - the band is top-left aligned inside each sequence: i and j are local
+ *    indices counted from the sequence's first query and first key, so causal
+ *    (-1, 0) means j <= i.  All measured workloads have equal query and key
+ *    lengths, where top-left and bottom-right agree;
  *  - L_scale is one global scalar for the whole call (the page calls it a
  *    runtime normalisation factor, not a per-sequence token count);
  *  - a query row with no visible key gets O = 0, a key row seen by no query
@@ -57,9 +66,12 @@ static int64_t owner(const int32_t* cu, int64_t B, int64_t r) {
     return -1;
 }
 
-/* Mask M_ij for local query index i and local key index j (both in range). */
-static inline int visible(int causal, int64_t i, int64_t j) {
-    return causal ? (j <= i) : 1;
+/* Mask M_ij for local query index i and local key index j (both in range),
+ * window (left, right), a negative bound meaning that side is unbounded. */
+static inline int visible(int64_t left, int64_t right, int64_t i, int64_t j) {
+    if (left >= 0 && j < i - left) return 0;
+    if (right >= 0 && j > i + right) return 0;
+    return 1;
 }
 
 static inline double dot(const double* x, const double* y, int64_t D) {
@@ -85,7 +97,7 @@ int oracle_num_threads(void) {
  */
 int oracle_hstu_fwd(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t H, int64_t D,
                     const double* q, const double* k, const double* v,
-                    double alpha, double ls, int causal,
+                    double alpha, double ls, int64_t left, int64_t right,
                     const int64_t* rows, int64_t nrows, double* out) {
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2) reduction(| : bad)
@@ -100,7 +112,7 @@ int oracle_hstu_fwd(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t
             const int64_t k0 = cu_k[b], lk = (int64_t)cu_k[b + 1] - cu_k[b];
             const double* qi = q + thd(r, h, 0, H, D);
             for (int64_t j = 0; j < lk; ++j) {
-                if (!visible(causal, i, j)) continue;
+                if (!visible(left, right, i, j)) continue;
                 const double s = alpha * dot(qi, k + thd(k0 + j, h, 0, H, D), D);
                 const double a = s * sigmoid(s) / ls;
                 const double* vj = v + thd(k0 + j, h, 0, H, D);
@@ -114,7 +126,7 @@ int oracle_hstu_fwd(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t
 /* dQ rows: dq[n, h, :] = dQ[rows[n], h, :]. */
 int oracle_hstu_bwd_dq(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t H, int64_t D,
                        const double* dout, const double* q, const double* k, const double* v,
-                       double alpha, double ls, int causal,
+                       double alpha, double ls, int64_t left, int64_t right,
                        const int64_t* rows, int64_t nrows, double* dq) {
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2) reduction(| : bad)
@@ -130,7 +142,7 @@ int oracle_hstu_bwd_dq(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int6
             const double* qi = q + thd(r, h, 0, H, D);
             const double* doi = dout + thd(r, h, 0, H, D);
             for (int64_t j = 0; j < lk; ++j) {
-                if (!visible(causal, i, j)) continue;
+                if (!visible(left, right, i, j)) continue;
                 const double* kj = k + thd(k0 + j, h, 0, H, D);
                 const double s = alpha * dot(qi, kj, D);
                 const double sg = sigmoid(s);
@@ -146,7 +158,7 @@ int oracle_hstu_bwd_dq(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int6
 /* dK and dV rows: dk/dv[n, h, :] = dK/dV[rows[n], h, :] for packed key rows. */
 int oracle_hstu_bwd_dkdv(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t H, int64_t D,
                          const double* dout, const double* q, const double* k, const double* v,
-                         double alpha, double ls, int causal,
+                         double alpha, double ls, int64_t left, int64_t right,
                          const int64_t* rows, int64_t nrows, double* dk, double* dv) {
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2) reduction(| : bad)
@@ -163,7 +175,7 @@ int oracle_hstu_bwd_dkdv(int64_t B, const int32_t* cu_q, const int32_t* cu_k, in
             const double* kj = k + thd(r, h, 0, H, D);
             const double* vj = v + thd(r, h, 0, H, D);
             for (int64_t i = 0; i < lq; ++i) {
-                if (!visible(causal, i, j)) continue;
+                if (!visible(left, right, i, j)) continue;
                 const double* qi = q + thd(q0 + i, h, 0, H, D);
                 const double* doi = dout + thd(q0 + i, h, 0, H, D);
                 const double s = alpha * dot(qi, kj, D);

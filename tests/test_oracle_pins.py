@@ -14,7 +14,13 @@ a missing 1/L_scale) fails at least one of them:
   ("Overview" equations): Q = 0 gives O = 0; V = 1 gives every output column
   equal to the masked SiLU row sum over L_scale; the first causal row; linearity
   in V; alpha folded into Q; permutation and locality across sequences;
-  <dV, V> = <dO, O> and <dQ, Q> = <dK, K>.
+  <dV, V> = <dO, O> and <dQ, Q> = <dK, K>;
+* for the token window of the page's "Mask support" table: the dense brute
+  force with the band built by library ``tril``/``triu`` diagonals, the
+  special windows the table names ((-1, 0) is causal, (-1, -1) full), bounds
+  past the sequence acting as unbounded, the diagonal-only window (0, 0) in
+  closed form, and the count of visible keys per row against an independent
+  closed form (equal keys make every score of a row equal).
 """
 
 import math
@@ -32,6 +38,8 @@ from generative_recommender_attention_amd.workloads import make_workload, named_
 # ----------------------------------------------------------------------------
 def dense_mask(cu_q, cu_k, causal):
     """Block-diagonal mask over global token indices, built by brute force."""
+    if not isinstance(causal, bool):
+        return dense_band_mask(cu_q, cu_k, *causal)
     tq, tk = int(cu_q[-1]), int(cu_k[-1])
     m = np.zeros((tq, tk))
     for b in range(len(cu_q) - 1):
@@ -43,8 +51,25 @@ def dense_mask(cu_q, cu_k, causal):
     return m
 
 
+def dense_band_mask(cu_q, cu_k, left, right):
+    """Block-diagonal mask of a token window: each sequence's block is the band
+    of diagonals -left .. +right of an all-ones (L_q x L_k) block (numpy ``tril``
+    keeps diagonals <= right, ``triu`` those >= -left; -1 drops that cut)."""
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    m = np.zeros((tq, tk))
+    for b in range(len(cu_q) - 1):
+        blk = np.ones((cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]))
+        if right >= 0:
+            blk = np.tril(blk, right)
+        if left >= 0:
+            blk = np.triu(blk, -left)
+        m[cu_q[b]:cu_q[b + 1], cu_k[b]:cu_k[b + 1]] = blk
+    return m
+
+
 def dense_forward_torch(cu_q, cu_k, q, k, v, alpha, ls, causal):
-    """O = ((M * silu(alpha Q K^T)) / ls) V per head, fp64 torch tensors in/out."""
+    """O = ((M * silu(alpha Q K^T)) / ls) V per head, fp64 torch tensors in/out.
+    ``causal`` is a bool (causal / full) or a (left, right) window."""
     m = torch.from_numpy(dense_mask(cu_q, cu_k, causal))
     outs = []
     for h in range(q.shape[1]):
@@ -55,8 +80,10 @@ def dense_forward_torch(cu_q, cu_k, q, k, v, alpha, ls, causal):
 
 
 def random_problem(seed, lq, lk, H, D, causal, scale=1.0):
-    wl = make_workload("pin", seed, lq, H, D, causal, scale, lengths_k=lk, with_do=True)
-    return wl
+    """``causal`` is a bool or a (left, right) window."""
+    if isinstance(causal, bool):
+        return make_workload("pin", seed, lq, H, D, causal, scale, lengths_k=lk, with_do=True)
+    return make_workload("pin", seed, lq, H, D, False, scale, lengths_k=lk, with_do=True, window=causal)
 
 
 def f64(bits):
@@ -72,6 +99,13 @@ TINY_CASES = [
     (14, [7, 3], [4, 3], 2, 4, False),    # L_k < L_q, full mask
     (15, [12], None, 3, 16, True),
     (16, [0, 0, 5], [0, 3, 5], 1, 4, True),
+    # token windows (left, right)
+    (17, [9, 14], None, 2, 8, (3, 0)),
+    (18, [11, 6], None, 1, 8, (2, 4)),
+    (19, [7, 12], [10, 5], 2, 4, (0, 2)),   # L_k != L_q both ways
+    (20, [13], None, 1, 8, (0, 0)),
+    (41, [10, 4], None, 2, 4, (-1, 3)),     # right bound only
+    (42, [8, 0, 15], None, 1, 8, (5, -1)),  # left bound only
 ]
 
 
@@ -102,7 +136,7 @@ def test_backward_matches_autograd_of_dense_forward(oracle_lib, case):
     np.testing.assert_allclose(dv, v.grad.numpy(), rtol=1e-11, atol=1e-13)
 
 
-@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("causal", [True, False, (1, 1)], ids=["causal", "full", "window11"])
 def test_backward_matches_finite_differences(oracle_lib, causal):
     """Central differences of f = <dO, O(Q,K,V)> through the oracle's forward."""
     lq, lk, H, D = [4, 3], [4, 3], 2, 4
@@ -344,3 +378,108 @@ def test_oracle_matches_its_committed_fixtures(oracle_lib):
     dq, dk, dv = oracle.bwd_workload(wl)
     for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
         np.testing.assert_allclose(x.ravel(), g[name], rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# token windows ("Mask support" table)
+# ----------------------------------------------------------------------------
+def _fwd_bwd(wl, mask):
+    args = (wl.cu_seqlens_q, wl.cu_seqlens_k)
+    a, ls = float(wl.alpha), wl.scaling_seqlen
+    o = oracle.fwd(*args, wl.q, wl.k, wl.v, a, ls, mask)
+    dq = oracle.bwd_dq(*args, wl.do, wl.q, wl.k, wl.v, a, ls, mask)
+    dk, dv = oracle.bwd_dkdv(*args, wl.do, wl.q, wl.k, wl.v, a, ls, mask)
+    return o, dq, dk, dv
+
+
+def test_named_windows_are_causal_and_full(oracle_lib):
+    """(-1, 0) is causal and (-1, -1) is full attention, bit for bit."""
+    wl = random_problem(43, [9, 1, 17], [12, 1, 17], 2, 8, True)
+    for window, flag in (((-1, 0), True), ((-1, -1), False)):
+        for x, y in zip(_fwd_bwd(wl, window), _fwd_bwd(wl, flag)):
+            np.testing.assert_array_equal(x, y)
+
+
+def test_bounds_past_the_sequence_are_unbounded(oracle_lib):
+    """A left bound >= L_q - 1 cuts nothing, nor does a right bound >= L_k - 1."""
+    wl = random_problem(44, [9, 6], [7, 10], 1, 8, True)
+    full = _fwd_bwd(wl, (-1, -1))
+    for window in ((8, 9), (8, -1), (-1, 9), (100, 100)):
+        for x, y in zip(_fwd_bwd(wl, window), full):
+            np.testing.assert_array_equal(x, y)
+    causal = _fwd_bwd(wl, (-1, 0))
+    for x, y in zip(_fwd_bwd(wl, (8, 0)), causal):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_diagonal_window_closed_form(oracle_lib):
+    """Window (0, 0): query i sees key i only, so O_i = SiLU(alpha q_i.k_i) v_i / L_scale,
+    dV_i = SiLU(s_ii) dO_i / L, dQ_i = alpha SiLU'(s_ii) (dO_i.v_i) k_i / L and
+    dK_i = alpha SiLU'(s_ii) (dO_i.v_i) q_i / L; rows i >= L_k see nothing."""
+    wl = random_problem(45, [6, 9], [6, 7], 2, 8, (0, 0), scale=1.5)
+    q, k, v, do = (f64(x) for x in (wl.q, wl.k, wl.v, wl.do))
+    a, ls = float(wl.alpha), wl.scaling_seqlen
+    o, dq, dk, dv = _fwd_bwd(wl, (0, 0))
+    for b in range(2):
+        lq, lk = int(wl.lengths_q[b]), int(wl.lengths_k[b])
+        for i in range(lq):
+            r, c = wl.cu_seqlens_q[b] + i, wl.cu_seqlens_k[b] + i
+            for h in range(2):
+                if i >= lk:
+                    assert np.all(o[r, h] == 0.0) and np.all(dq[r, h] == 0.0)
+                    continue
+                s = a * math.fsum(q[r, h] * k[c, h])
+                sig = 1.0 / (1.0 + math.exp(-s))
+                dsilu = sig * (1.0 + s * (1.0 - sig))
+                da = math.fsum(do[r, h] * v[c, h])
+                np.testing.assert_allclose(o[r, h], s * sig * v[c, h] / ls, rtol=1e-12, atol=1e-15)
+                np.testing.assert_allclose(dv[c, h], s * sig * do[r, h] / ls, rtol=1e-12, atol=1e-15)
+                np.testing.assert_allclose(dq[r, h], a * dsilu * da * k[c, h] / ls, rtol=1e-11, atol=1e-15)
+                np.testing.assert_allclose(dk[c, h], a * dsilu * da * q[r, h] / ls, rtol=1e-11, atol=1e-15)
+        for j in range(lq, lk):  # keys no query reaches
+            c = wl.cu_seqlens_k[b] + j
+            assert np.all(dk[c] == 0.0) and np.all(dv[c] == 0.0)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (1, 0), (3, 0), (0, 1), (2, 5), (-1, 2), (4, -1), (6, 6)])
+def test_visible_key_count_per_row(oracle_lib, window):
+    """With every key of a sequence equal and V = 1, every score of query row i is
+    the same value s_i, so O_i = n_i SiLU(s_i) / L_scale in every column, where
+    n_i = #{j in [0, L_k) : i - left <= j <= i + right} is counted here from the
+    interval's clamped ends, not by testing keys one by one."""
+    left, right = window
+    lq, lk = [11, 5, 8], [9, 7, 8]
+    wl = random_problem(46, lq, lk, 1, 8, window)
+    q, k = f64(wl.q), f64(wl.k)
+    cu_q, cu_k = wl.cu_seqlens_q, wl.cu_seqlens_k
+    for b in range(3):
+        k[cu_k[b]:cu_k[b + 1]] = k[cu_k[b]]
+    v = np.ones_like(f64(wl.v))
+    a, ls = float(wl.alpha), wl.scaling_seqlen
+    o = oracle.fwd(cu_q, cu_k, q, k, v, a, ls, window)
+    for b in range(3):
+        for i in range(lq[b]):
+            lo = 0 if left < 0 else max(0, i - left)
+            hi = lk[b] - 1 if right < 0 else min(lk[b] - 1, i + right)
+            n = max(0, hi - lo + 1)
+            r = cu_q[b] + i
+            s = a * math.fsum(q[r, 0] * k[cu_k[b], 0])
+            want = n * s / (1.0 + math.exp(-s)) / ls
+            np.testing.assert_allclose(o[r, 0], np.full(8, want), rtol=1e-12, atol=1e-15)
+
+
+def test_band_splits_into_its_two_sides(oracle_lib):
+    """Keys [i - l, i + r] are the disjoint union of [i - l, i] and [i + 1, i + r], and
+    the masked sum is linear in the key set: O(l, r) = O(l, 0) + O(-1, r) - O(-1, 0)."""
+    wl = random_problem(47, [15, 9], [12, 14], 2, 8, True)
+    args = (wl.cu_seqlens_q, wl.cu_seqlens_k, wl.q, wl.k, wl.v, float(wl.alpha), wl.scaling_seqlen)
+    for l, r in ((2, 3), (0, 5), (4, 1)):
+        lhs = oracle.fwd(*args, (l, r))
+        rhs = oracle.fwd(*args, (l, 0)) + oracle.fwd(*args, (-1, r)) - oracle.fwd(*args, (-1, 0))
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-13)
+
+
+def test_window_bounds_below_minus_one_are_rejected(oracle_lib):
+    wl = random_problem(48, [3], None, 1, 4, True)
+    with pytest.raises(ValueError):
+        oracle.fwd(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.q, wl.k, wl.v, 1.0, 3, (-2, 0))

@@ -20,12 +20,13 @@ EXPECTED_TOTALS = {
     "zipf_b32_h4_d128_causal": 23460,
     "long_b4_h8_d128_causal": 43527,
     "zipf_b32_h4_d128_causal_fwdbwd": 23460,
+    "long_b4_h8_d128_window1024": 43527,
 }
 
 
 def test_lengths_and_totals():
     for name in WORKLOAD_NAMES:
-        if name == "long_b4_h8_d128_causal":
+        if name.startswith("long_b4_h8_d128"):
             continue  # 43527 x 8 x 128 draws: covered by the cheaper length-only check below
         wl = named_workload(name)
         assert wl.total_q == EXPECTED_TOTALS[name]
@@ -71,3 +72,13 @@ def test_value_scale():
     small = make_workload("x", 9, [3, 0, 4], 2, 32, True, lengths_k=[5, 1, 4])
     assert small.total_q == 7 and small.total_k == 10
     assert small.cu_seqlens_k.tolist() == [0, 5, 6, 10]
+
+
+def test_masks_of_the_named_workloads():
+    assert named_workload("tiny_b2_h1_d16_causal").window_size == (-1, 0)
+    assert named_workload("uniform_b8_h2_d64_full").window_size == (-1, -1)
+    w = make_workload("w", 7, [5, 9], 1, 16, False, window=(3, 1))
+    assert w.window_size == (3, 1) and w.mask_name == "window(3,1)"
+    import pytest
+    with pytest.raises(ValueError):
+        make_workload("w", 7, [5], 1, 16, False, window=(-2, 0))
