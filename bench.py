@@ -42,15 +42,17 @@ USEFUL_PER_PAIR_D = {"fwd": 4, "bwd": 10}
 KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel"}
 
 
-def visible_pairs(lengths_q, lengths_k, causal: bool) -> int:
-    """Count of (query, key) pairs the mask keeps (top-left causal: j <= i)."""
+def visible_pairs(lengths_q, lengths_k, window) -> int:
+    """Count of (query, key) pairs a token window (left, right) keeps: key j is
+    visible to query i iff i - left <= j <= i + right, -1 = unbounded side (so
+    (-1, 0) is top-left causal and (-1, -1) full attention)."""
+    left, right = window
     total = 0
     for lq, lk in zip(np.asarray(lengths_q, dtype=np.int64), np.asarray(lengths_k, dtype=np.int64)):
-        if causal:
-            i = np.arange(lq, dtype=np.int64)
-            total += int(np.minimum(i + 1, lk).sum())
-        else:
-            total += int(lq * lk)
+        i = np.arange(lq, dtype=np.int64)
+        lo = np.zeros_like(i) if left < 0 else np.maximum(0, i - left)
+        hi = np.full_like(i, lk) if right < 0 else np.minimum(lk, i + right + 1)
+        total += int(np.maximum(0, hi - lo).sum())
     return total
 
 
@@ -66,14 +68,15 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from the committed PMC summary, if it matches these sources."""
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary, if it matches these
+    sources and this workload."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_digest") != kernel_source_digest():
+    if t.get("source_digest") != kernel_source_digest() or t.get("workload") != workload:
         return None
     k = t.get("kernels", {}).get(kernel)
     if not k:
@@ -152,7 +155,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     stats = rows("kt", "*kernel_stats.csv")
     out = [f"# rocprofv3 kernel trace: HSTU attention fwd + bwd, workload {workload}", "",
            f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
-           f"{'causal' if wl.causal else 'no mask'}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
+           f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
            "hstu_bwd_dq + hstu_bwd_dkdv.", "", "Command (GPU box, from the repository root):",
            "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir), "",
            f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
@@ -175,7 +178,7 @@ def cpu_baseline(wl, max_pairs: int):
     order = np.argsort(wl.lengths_q, kind="stable")
     chosen, pairs = [], 0
     for b in order:
-        p = visible_pairs([wl.lengths_q[b]], [wl.lengths_k[b]], wl.causal)
+        p = visible_pairs([wl.lengths_q[b]], [wl.lengths_k[b]], wl.window_size)
         if max_pairs and pairs + p > max_pairs and chosen:
             continue
         chosen.append(int(b))
@@ -197,7 +200,7 @@ def cpu_baseline(wl, max_pairs: int):
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": (f"fp64 oracle fwd+bwd on {len(chosen)} of {wl.batch} sequences (lengths {lens[0]}..{lens[-1]}, "
-                   f"{pairs} visible pairs x {wl.num_heads} heads = {pairs / visible_pairs(wl.lengths_q, wl.lengths_k, wl.causal):.1%} "
+                   f"{pairs} visible pairs x {wl.num_heads} heads = {pairs / visible_pairs(wl.lengths_q, wl.lengths_k, wl.window_size):.1%} "
                    f"of the workload's pairs), {dt:.1f} s"),
         "seconds": dt,
         "cpu": platform.processor() or platform.machine(),
@@ -253,7 +256,7 @@ def main(argv=None) -> int:
     del lib
     wl = named_workload(args.workload)
     print(f"[bench] workload {wl.name}: B={wl.batch} T={wl.total_q} H={wl.num_heads} D={wl.head_dim} "
-          f"causal={wl.causal}", file=sys.stderr, flush=True)
+          f"mask={wl.mask_name}", file=sys.stderr, flush=True)
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -266,7 +269,7 @@ def main(argv=None) -> int:
     o = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     kw = dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, alpha=float(wl.alpha),
-              scaling_seqlen=wl.scaling_seqlen, causal=wl.causal)
+              scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window)
     stream = torch.cuda.current_stream(dev)
     kernels = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if has_bwd else [])
 
@@ -303,7 +306,7 @@ def main(argv=None) -> int:
         per_kernel_ms[name] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
     ms_per_step = elapsed * 1e3 / args.steps
 
-    pairs = visible_pairs(wl.lengths_q, wl.lengths_k, wl.causal)
+    pairs = visible_pairs(wl.lengths_q, wl.lengths_k, wl.window_size)
     unit_pd = wl.head_dim * wl.num_heads * pairs
     useful = USEFUL_PER_PAIR_D["fwd"] * unit_pd + (USEFUL_PER_PAIR_D["bwd"] * unit_pd if has_bwd else 0)
     value = useful / (ms_per_step * 1e-3) / 1e12
@@ -311,7 +314,7 @@ def main(argv=None) -> int:
     dominant = max(per_kernel_ms, key=per_kernel_ms.get)
     alg_flops = FLOPS_PER_PAIR_D[dominant] * unit_pd
     achieved = alg_flops / (per_kernel_ms[dominant] * 1e-3) / 1e12
-    traffic = load_traffic(KERNEL_SYMBOL[dominant])
+    traffic = load_traffic(KERNEL_SYMBOL[dominant], wl.name)
 
     detail = {}
     for name in kernels:
@@ -334,7 +337,7 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "total_tokens": wl.total_q,
-                   "heads": wl.num_heads, "head_dim": wl.head_dim, "mask": "causal" if wl.causal else "none",
+                   "heads": wl.num_heads, "head_dim": wl.head_dim, "mask": wl.mask_name,
                    "max_seqlen": wl.max_seqlen_q, "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful, "parallelism": "single GPU"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),

@@ -64,13 +64,27 @@ hstu_status_t check_operand(const hstu_args_t& a, Operand& t) {
     return HSTU_OK;
 }
 
+// Kernel mask for validated args: the windows (-1, -1) and (-1, 0) run the full
+// and causal kernels, which are the same masks.
+hstu::MaskKind mask_kind(const hstu_args_t& a) {
+    if (a.mask == HSTU_MASK_CAUSAL) return hstu::MaskKind::Causal;
+    if (a.mask != HSTU_MASK_WINDOW) return hstu::MaskKind::None;
+    if (a.window_left < 0 && a.window_right < 0) return hstu::MaskKind::None;
+    if (a.window_left < 0 && a.window_right == 0) return hstu::MaskKind::Causal;
+    return hstu::MaskKind::Window;
+}
+
 // Scalar checks common to every entry point; fills the kernel parameter block.
 hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int32_t* cu_k, hstu::AttnParams& p) {
     if (a == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args is null");
     if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
         return fail(HSTU_ERR_UNSUPPORTED, "head_dim %d is not one of 16, 32, 64, 128", a->head_dim);
-    if (a->mask != HSTU_MASK_NONE && a->mask != HSTU_MASK_CAUSAL)
-        return fail(HSTU_ERR_UNSUPPORTED, "mask %d is not HSTU_MASK_NONE or HSTU_MASK_CAUSAL", a->mask);
+    if (a->mask != HSTU_MASK_NONE && a->mask != HSTU_MASK_CAUSAL && a->mask != HSTU_MASK_WINDOW)
+        return fail(HSTU_ERR_UNSUPPORTED, "mask %d is not HSTU_MASK_NONE, HSTU_MASK_CAUSAL or HSTU_MASK_WINDOW",
+                    a->mask);
+    if (a->mask == HSTU_MASK_WINDOW && (a->window_left < -1 || a->window_right < -1))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "window (%d, %d): bounds must be >= -1", a->window_left,
+                    a->window_right);
     if (a->batch < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "batch %d < 1", a->batch);
     if (a->num_heads < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_heads %d < 1", a->num_heads);
     if (a->total_q < 0 || a->total_k < 0)
@@ -89,6 +103,8 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
     const int32_t ls = a->scaling_seqlen == 0 ? a->max_seqlen_q : a->scaling_seqlen;
     if (ls < 1 && a->total_q > 0)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "scaling_seqlen resolves to %d; it must be positive", ls);
+    if (mask_kind(*a) == hstu::MaskKind::Window && a->max_seqlen_k > hstu::kMaxWindowSeqlen)
+        return fail(HSTU_ERR_UNSUPPORTED, "a window mask needs max_seqlen_k <= %d", hstu::kMaxWindowSeqlen);
     if (cu_q == nullptr || cu_k == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "cu_seqlens pointer is null");
     if (reinterpret_cast<uintptr_t>(cu_q) % 4 != 0 || reinterpret_cast<uintptr_t>(cu_k) % 4 != 0)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "cu_seqlens pointer is not 4-byte aligned");
@@ -102,6 +118,13 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
     p.exp_c = -a->alpha * 1.4426950408889634f;
     p.out_scale = ls >= 1 ? a->alpha / (float)ls : 0.0f;
     p.pre_scale = p.exp_c != 0.0f ? p.out_scale / p.exp_c : 0.0f;
+    if (mask_kind(*a) == hstu::MaskKind::Window) {
+        // an unbounded side, or one reaching past every sequence, becomes max_seqlen_k:
+        // no row index or key index differs from another by more than that
+        auto side = [&](int32_t w) { return w < 0 || w > a->max_seqlen_k ? a->max_seqlen_k : w; };
+        p.win_left = side(a->window_left);
+        p.win_right = side(a->window_right);
+    }
     return HSTU_OK;
 }
 
@@ -143,7 +166,7 @@ hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, cons
     p.dq = out(ops[4]);
     if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
-    return launched(hstu::launch_bwd_dq(p, a->head_dim, a->mask == HSTU_MASK_CAUSAL, stream), "hstu_bwd_dq");
+    return launched(hstu::launch_bwd_dq(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq");
 }
 
 hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
@@ -165,7 +188,7 @@ hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, co
     p.dv = out(ops[5]);
     if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN)) != HSTU_OK) return st;
     if (a->total_k == 0) return ok();
-    return launched(hstu::launch_bwd_dkdv(p, a->head_dim, a->mask == HSTU_MASK_CAUSAL, stream),
+    return launched(hstu::launch_bwd_dkdv(p, a->head_dim, mask_kind(*a), stream),
                     "hstu_bwd_dkdv");
 }
 
@@ -190,7 +213,7 @@ hstu_status_t hstu_fwd(const hstu_args_t* a, const void* q, const void* k, const
     p.o = out(ops[3]);
     if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
-    return launched(hstu::launch_fwd(p, a->head_dim, a->mask == HSTU_MASK_CAUSAL, stream), "hstu_fwd");
+    return launched(hstu::launch_fwd(p, a->head_dim, mask_kind(*a), stream), "hstu_fwd");
 }
 
 hstu_status_t hstu_bwd_dq(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,

@@ -14,7 +14,7 @@
 // final store.
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
-// same tile walk as the forward, two workgroups per CU (so the exponent work of
+// same tile walk and mask handling as the forward, two workgroups per CU (so the exponent work of
 // one overlaps the products of the other).  Per 64-key tile K and V are staged
 // row-major in LDS; each wave computes S^T = K Q^T and dA^T = V dO^T (A operands:
 // K, V rows), forms dS^T in registers and accumulates dQ^T += K^T dS^T (A
@@ -26,7 +26,10 @@
 // of every query tile, so each wave holds only its dK^T and dV^T accumulators
 // and two waves fit per SIMD; their partial sums are added through LDS at the
 // end.  Causal blocks walk query tiles from the block's first key to the end of
-// the sequence (rows before it see none of these keys).  Per 64-row query tile
+// the sequence (rows before it see none of these keys); under a token window
+// (left, right) they walk rows [first key - right, last key + left], the rows
+// whose band meets the block, and each wave tests per 32-row block whether the
+// band covers, misses or cuts it, as the forward does.  Per 64-row query tile
 // Q and dO are staged row-major; each wave computes S = Q K^T and dA = dO V^T
 // (A operands: Q, dO rows; B operands: K, V rows), forms A' and dS in registers
 // and accumulates dV^T += dO^T A' and dK^T += Q^T dS (A operands: dO, Q read
@@ -60,20 +63,26 @@ __device__ __forceinline__ float dsilu_from(float a, float sig) {
 
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
 
-// dS^T operands of one 32-key block from its score and dA accumulators, masked
-// to keys below `lim` when the block reaches `wlim`.
-__device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc, int key0, int lim, int wlim, int g,
-                                         uint4& d0, uint4& d1) {
+// dS^T operands of one 32-key block from its score and dA accumulators.  Keys
+// outside this lane's interval [lo, lo + span) are zeroed when the block leaves
+// [wlo, wlim), the keys every row of the wave sees (WIN: a window mask, where
+// the block can also start below it).
+template <bool WIN>
+__device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc, int key0, int lo, int span, int wlo,
+                                         int wlim, int g, uint4& d0, uint4& d1) {
     float dv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const float sg = sig_pre(sacc[r]);
         dv[r] = dacc[r] * dsilu_from(sacc[r] * sg, sg);
     }
-    if (key0 + 32 > wlim) {
+    if ((WIN && key0 < wlo) || key0 + 32 > wlim) {
         keep_branch();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dv[r] = key0 + acc_row(r, g) < lim ? dv[r] : 0.0f;
+        for (int r = 0; r < 16; ++r) {
+            const int key = key0 + acc_row(r, g);
+            dv[r] = (WIN ? (unsigned)(key - lo) < (unsigned)span : key < span) ? dv[r] : 0.0f;
+        }
     }
     d0 = pack_operand(dv);
     d1 = pack_operand(dv + 8);
@@ -83,11 +92,11 @@ __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc,
 // (K) and `vt` (V).  Products run S^T and dA^T of both 32-key blocks, then dQ^T
 // of the first block (while dS^T of the second is formed), then of the second;
 // every LDS read is issued PF products ahead of its MFMA.
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&qf)[D / 16],
                                            const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
                                            const uint32_t (&koff)[D / 16], const uint2 (&toff)[(D < 32 ? 32 : D) / 32],
-                                           int n0, int lim, int wlim, int g) {
+                                           int n0, int lo, int span, int wlo, int wlim, int g) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // S and dA products: block kb, step kk, operand (K, V)
@@ -122,7 +131,7 @@ __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         uint4 d0, d1;
-        dq_ds_op(sa[kb], da[kb], n0 + 32 * kb, lim, wlim, g, d0, d1);
+        dq_ds_op<WIN>(sa[kb], da[kb], n0 + 32 * kb, lo, span, wlo, wlim, g, d0, d1);
 #pragma unroll
         for (int j = 0; j < 2 * NDB; ++j) {
             const int i = kb * 2 * NDB + j;
@@ -132,11 +141,13 @@ __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, MaskKind MK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
+    constexpr bool CAUSAL = MK == MaskKind::Causal;
+    constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
-    // [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile t lives in slot t % 2
+    // [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile t lives in slot (t - t0) % 2
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
     const uint32_t lds0 = lds_addr(smem);
     constexpr uint32_t K0 = 0, K1 = kTileBytes, V0 = 2 * kTileBytes, V1 = 3 * kTileBytes;
@@ -154,13 +165,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     const int m0 = m * BM;
     if (m0 >= sb.lq) return;
 
-    const int kv_end = CAUSAL ? min(sb.lk, m0 + BM) : sb.lk;
-    const int ntiles = (kv_end + BN - 1) / BN;
     const int row0 = m0 + 32 * wave;
     const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
-    const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
-    const int wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;
+    // Keys [kv_begin, kv_end) some row of the block sees; this lane's interval
+    // [lo, lo + span); keys every live row of the wave sees [wlo, wlim); keys
+    // some live row of the wave sees [any_lo, any_hi) (window only).
+    int kv_begin = 0, kv_end = sb.lk, lo = 0, span, wlo = 0, wlim, any_lo = 0, any_hi = 0;
+    if constexpr (WINDOW) {
+        const int L = p.win_left, R = p.win_right;
+        const int last = min(m0 + BM, sb.lq) - 1, wlast = min(row0 + 31, sb.lq - 1);
+        kv_begin = max(0, m0 - L);
+        kv_end = max(kv_begin, min(sb.lk, last + R + 1));
+        lo = max(0, my_row - L);
+        span = max(0, min(sb.lk, my_row + R + 1) - lo);
+        wlo = max(0, wlast - L);
+        wlim = min(sb.lk, row0 + R + 1);
+        any_lo = max(0, row0 - L);
+        any_hi = min(sb.lk, wlast + R + 1);
+    } else {
+        if (CAUSAL) kv_end = min(sb.lk, m0 + BM);
+        span = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
+        wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;
+    }
+    const int t0 = kv_begin / BN;
+    const int t1 = kv_end > kv_begin ? (kv_end + BN - 1) / BN : t0;
 
     uint4 qf[KSTEPS], dof[KSTEPS];
     {
@@ -187,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) acc[db] = f32x16{};
 
-    if (ntiles > 0) {
+    if (t1 > t0) {
         const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
         const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
         TileDma<D> kdma, vdma;
@@ -201,25 +230,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
                 ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
             }
         }
-        kdma.issue(lds0 + K0, kbase, p.k.tok, 0, kv_end);
-        vdma.issue(lds0 + V0, vbase, p.v.tok, 0, kv_end);
+        kdma.issue(lds0 + K0, kbase, p.k.tok, t0 * BN, kv_end);
+        vdma.issue(lds0 + V0, vbase, p.v.tok, t0 * BN, kv_end);
         wait_global_loads();
         __syncthreads();
 
         auto step = [&](uint32_t kc, uint32_t vc, uint32_t kn, uint32_t vn, int t) {
             const int n0 = t * BN;
-            if (t + 1 < ntiles) {
+            if (t + 1 < t1) {
                 kdma.issue(lds0 + kn, kbase, p.k.tok, n0 + BN, kv_end);
                 vdma.issue(lds0 + vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
-            if (wave_live && !(CAUSAL && n0 > row0 + 31))
-                dq_tile<D>(kc, vc, qf, dof, acc, koff, toff, n0, lim, wlim, g);
+            // waves that see no key of the tile skip it
+            const bool run = WINDOW ? n0 + BN > any_lo && n0 < any_hi : !(CAUSAL && n0 > row0 + 31);
+            if (wave_live && run) dq_tile<D, WINDOW>(kc, vc, qf, dof, acc, koff, toff, n0, lo, span, wlo, wlim, g);
             wait_global_loads();
             __syncthreads();
         };
-        for (int t = 0; t < ntiles; t += 2) {
+        for (int t = t0; t < t1; t += 2) {
             step(K0, V0, K1, V1, t);
-            if (t + 1 < ntiles) step(K1, V1, K0, V0, t + 1);
+            if (t + 1 < t1) step(K1, V1, K0, V0, t + 1);
         }
     }
 
@@ -308,8 +338,10 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, MaskKind MK>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
+    constexpr bool CAUSAL = MK == MaskKind::Causal;
+    constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
     // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1 | K rows of the block | V rows of the block]
@@ -361,10 +393,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) dvacc[db] = dkacc[db] = f32x16{};
 
-    const int q_begin = CAUSAL ? n0 : 0;
-    const int ntiles = sb.lq > q_begin ? (sb.lq - q_begin + BMQ - 1) / BMQ : 0;
-    const int lo = CAUSAL ? my_key : 0;
-    const int wlo = CAUSAL ? key0 + 31 : 0;  // largest lo in the wave
+    // Query rows [q_begin, q_end) that see some key of the block; this lane's
+    // rows [lo, hi); rows that see every live key of the wave [wlo, whi); rows
+    // that see some live key of the wave [any_lo, any_hi) (window only).
+    int q_begin = 0, q_end = sb.lq, lo = 0, hi = sb.lq, wlo = 0, whi = sb.lq, any_lo = 0, any_hi = 0;
+    if constexpr (WINDOW) {
+        const int L = p.win_left, R = p.win_right;
+        const int last = min(n0 + BNK, sb.lk) - 1, wlast = min(key0 + 31, sb.lk - 1);
+        q_begin = max(0, n0 - R);
+        q_end = max(q_begin, min(sb.lq, last + L + 1));
+        lo = max(0, my_key - R);
+        hi = min(sb.lq, my_key + L + 1);
+        wlo = max(0, wlast - R);
+        whi = min(sb.lq, key0 + L + 1);
+        any_lo = max(0, key0 - R);
+        any_hi = min(sb.lq, wlast + L + 1);
+    } else if constexpr (CAUSAL) {
+        q_begin = n0;
+        lo = my_key;
+        wlo = key0 + 31;  // largest lo in the wave
+    }
+    const int ntiles = q_end > q_begin ? (q_end - q_begin + BMQ - 1) / BMQ : 0;
     const uint32_t krow = KB + 8192u * kw, vrow = VB + 8192u * kw;
 
     if (ntiles > 0) {
@@ -391,12 +440,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
             const int qt0 = q_begin + t * BMQ;
             if (t + 1 < ntiles) dma.issue(lds0 + (qgrp ? qn : dn), sbase, stok, qt0 + BMQ, sb.lq);
             const int row0 = qt0 + 32 * qh;
-            // waves whose keys all follow every row of the block, or lie past the sequence, skip it
-            if (wave_live && !(CAUSAL && row0 + 31 < key0) && row0 < sb.lq) {
+            // waves whose keys no row of the block sees, or that lie past the sequence, skip it
+            const bool run = WINDOW ? row0 + 32 > any_lo && row0 < any_hi : !(CAUSAL && row0 + 31 < key0);
+            if (wave_live && run && row0 < sb.lq) {
                 const uint32_t qr = qc + 8192u * qh, dr = dc + 8192u * qh;
-                // rows below the wave's largest first visible row, or past the sequence, need the mask
-                dkdv_block<D>(row0 < wlo || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff,
-                               row0, lo, sb.lq, g);
+                // rows outside those that see every key of the wave, or past the sequence, need the mask
+                dkdv_block<D>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff,
+                              row0, lo, hi, g);
             }
             wait_global_loads();
             __syncthreads();
@@ -454,42 +504,54 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, MaskKind MK>
 hipError_t launch_dq(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MK>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, MaskKind MK>
 hipError_t launch_dkdv(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool DKDV>
+hipError_t launch_mask(const AttnParams& p, MaskKind mask, hipStream_t stream) {
+    switch (mask) {
+        case MaskKind::None:
+            return DKDV ? launch_dkdv<D, MaskKind::None>(p, stream) : launch_dq<D, MaskKind::None>(p, stream);
+        case MaskKind::Causal:
+            return DKDV ? launch_dkdv<D, MaskKind::Causal>(p, stream) : launch_dq<D, MaskKind::Causal>(p, stream);
+        case MaskKind::Window:
+            return DKDV ? launch_dkdv<D, MaskKind::Window>(p, stream) : launch_dq<D, MaskKind::Window>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool DKDV>
+hipError_t launch_dir(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
+    switch (head_dim) {
+        case 16: return launch_mask<16, DKDV>(p, mask, stream);
+        case 32: return launch_mask<32, DKDV>(p, mask, stream);
+        case 64: return launch_mask<64, DKDV>(p, mask, stream);
+        case 128: return launch_mask<128, DKDV>(p, mask, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, bool causal, hipStream_t stream) {
-    switch (head_dim) {
-        case 16: return causal ? launch_dq<16, true>(p, stream) : launch_dq<16, false>(p, stream);
-        case 32: return causal ? launch_dq<32, true>(p, stream) : launch_dq<32, false>(p, stream);
-        case 64: return causal ? launch_dq<64, true>(p, stream) : launch_dq<64, false>(p, stream);
-        case 128: return causal ? launch_dq<128, true>(p, stream) : launch_dq<128, false>(p, stream);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
+    return launch_dir<false>(p, head_dim, mask, stream);
 }
 
-hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, bool causal, hipStream_t stream) {
-    switch (head_dim) {
-        case 16: return causal ? launch_dkdv<16, true>(p, stream) : launch_dkdv<16, false>(p, stream);
-        case 32: return causal ? launch_dkdv<32, true>(p, stream) : launch_dkdv<32, false>(p, stream);
-        case 64: return causal ? launch_dkdv<64, true>(p, stream) : launch_dkdv<64, false>(p, stream);
-        case 128: return causal ? launch_dkdv<128, true>(p, stream) : launch_dkdv<128, false>(p, stream);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
+    return launch_dir<true>(p, head_dim, mask, stream);
 }
 
 }  // namespace hstu

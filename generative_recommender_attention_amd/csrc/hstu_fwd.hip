@@ -3,29 +3,32 @@
 // Computes, per packed sequence and head (HSTU Attention page, "Overview"
 // equations), O = ((M (.) SiLU(alpha Q K^T)) / L_scale) V with no softmax, so no
 // running maximum, no rescaling and no row statistics are kept: O is a plain
-// sum over key tiles, and any split of the keys combines by addition.
+// sum over key tiles.
 //
-// Workgroup = 4 wavefronts on the 4 SIMDs of one CU (one workgroup per CU, so
-// each wave may use the full 512-register file) = 128 query rows of one
-// (sequence, head).  Wave w owns the 64 rows 64 (w & 1) .. +63 and the key
-// tiles of parity w >> 1: the two wave pairs run the even and the odd 64-key
-// tiles of the same rows, which halves the longest chain of tiles a workgroup
-// walks (the last rows of a long causal sequence), and add their partial O
-// through LDS at the end.  Grid = (live row block, head), head fastest, over
-// the live blocks in the order of find_block: block index descending, so the
-// blocks with the most key tiles start first; the host never reads the
-// cumulative lengths and the surplus workgroups sit at the end of the grid.
+// Workgroup = 4 wavefronts, two workgroups per CU = 128 query rows of one
+// (sequence, head); wave w owns rows 32 w .. 32 w + 31.  Grid = (live row block,
+// head), head fastest, over the live blocks in the order of find_block: block
+// index descending, so that under a causal mask the blocks with the most key
+// tiles start first; the host never reads the cumulative lengths and the
+// surplus workgroups sit at the end of the grid.
 //
-// Each wave pair stages its own tiles (64 keys x D of K and of V, row-major,
-// swizzled) into LDS with direct global->LDS loads issued from inline assembly,
-// double-buffered: the loads of the pair's next tile are issued before the
-// current one is computed and waited for (vmcnt) before the one barrier per
-// step.  Per tile a wave runs, for each 32-key half,
-//   S^T (32 x 64)  = K_half (cQ)^T   on MFMA: A = K rows from LDS, B = Q from
-//                    registers (64 rows = two 32-row blocks, so every LDS read
-//                    feeds two MFMAs), Q pre-scaled by c = -alpha log2 e
+// The mask ("Mask support" table) decides the block's key range and which tiles
+// need the per-element test: full attention walks every key tile and tests only
+// the sequence end; causal stops at the block's diagonal and tests only its last
+// two tiles; a token window (left, right) walks the tiles that meet the band of
+// its rows, [first row - left, last row + right], and each wave decides per tile
+// whether the band covers the tile for all its rows (no test), misses it for all
+// (skip) or cuts it (test each score against the row's own interval).
+//
+// K and V tiles (64 keys x D, row-major, swizzled) are staged into LDS with
+// direct global->LDS loads issued from inline assembly, double-buffered: the
+// loads of the next tile are issued before the current one is computed and
+// waited for (vmcnt) before the one barrier per step.  Per tile a wave runs, for
+// each 32-key half,
+//   S^T (32 x 32)  = K_half (cQ)^T   on MFMA: A = K rows from LDS, B = Q from
+//                    registers, Q pre-scaled by c = -alpha log2 e
 //   P^T            = bf16(y / (1 + 2^y)), masked on edge tiles only
-//   O^T (D x 64)  += V_half^T P^T    on MFMA: A = V read transposed from LDS
+//   O^T (D x 32)  += V_half^T P^T    on MFMA: A = V read transposed from LDS
 // with the scores of one half turned into P^T while the next half's products
 // run, and the epilogue writing O = (alpha / L_scale) O^T^T in bf16.
 #include <type_traits>
@@ -38,21 +41,22 @@ namespace {
 constexpr int BM = kFwdBlockM;                   // 128 query rows per workgroup
 constexpr int BN = kTileRows;                    // 64 keys per tile
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
-constexpr uint32_t kGroupBytes = 4 * kTileBytes; // per wave pair: K slots 0, 1, V slots 0, 1
 
 // bf16 P^T operand from accumulator registers r0..r0+7 of a 32-key block whose
 // first key is key0.  The scores arrive as y = c x with c = -alpha log2(e)
 // folded into Q (x = q.k), so y sig(alpha x) = y / (1 + 2^y) costs one exp, one
 // add, one rcp and one multiply; the factor 1/c is folded into the output
-// scale.  With MASKED, keys at or past this lane's limit `lim` are zeroed.
+// scale.  With MASKED, keys outside this lane's interval [lo, lo + span) are
+// zeroed (one unsigned compare tests both ends).
 template <bool MASKED>
-__device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int lim, int g) {
+__device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int lo, int span, int g) {
     float pv[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) pv[r] = silu_pre(s[r0 + r]);
     if constexpr (MASKED) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) pv[r] = key0 + acc_row(r0 + r, g) < lim ? pv[r] : 0.0f;
+        for (int r = 0; r < 8; ++r)
+            pv[r] = (unsigned)(key0 + acc_row(r0 + r, g) - lo) < (unsigned)span ? pv[r] : 0.0f;
     }
     return pack_operand(pv);
 }
@@ -64,7 +68,8 @@ __device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0,
 template <int D, bool MASKED, uint32_t kt, uint32_t vt>
 __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
                                          f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&koff)[D / 16],
-                                         const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, int lim, int g) {
+                                         const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, int lo, int span,
+                                         int g) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;  // 32-column blocks of O^T
     constexpr int NS = D / 16;                   // contraction steps per S^T block
     constexpr int NK = 2 * NS;                   // K reads: block-major, step-minor
@@ -88,15 +93,15 @@ __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
         else s1 = mfma32x32x16(rd[j], qf[j - NS], s1);
         read(j + PF);
     }
-    const uint4 p0 = silu_operand<MASKED>(s0, 0, n0, lim, g);
-    const uint4 p1 = silu_operand<MASKED>(s0, 8, n0, lim, g);
+    const uint4 p0 = silu_operand<MASKED>(s0, 0, n0, lo, span, g);
+    const uint4 p1 = silu_operand<MASKED>(s0, 8, n0, lo, span, g);
 #pragma unroll
     for (int i = 0; i < 2 * NDB; ++i) {
         oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < NDB ? p0 : p1, oacc[i % NDB]);
         read(NK + i + PF);
     }
-    const uint4 p2 = silu_operand<MASKED>(s1, 0, n0 + 32, lim, g);
-    const uint4 p3 = silu_operand<MASKED>(s1, 8, n0 + 32, lim, g);
+    const uint4 p2 = silu_operand<MASKED>(s1, 0, n0 + 32, lo, span, g);
+    const uint4 p3 = silu_operand<MASKED>(s1, 8, n0 + 32, lo, span, g);
 #pragma unroll
     for (int i = 2 * NDB; i < NV; ++i) {
         oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < 3 * NDB ? p2 : p3, oacc[i % NDB]);
@@ -104,21 +109,20 @@ __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
     }
 }
 
-template <int D, bool CAUSAL, int KSPLIT>
-__global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParams p) {
+template <int D, MaskKind MK>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
+    constexpr bool CAUSAL = MK == MaskKind::Causal;
+    constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int NDB = DM / 32;
     constexpr int KSTEPS = D / 16;
-    // [group 0: K slot 0 | K slot 1 | V slot 0 | V slot 1][group 1: same]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * KSPLIT * kTileElems];
+    // [K slot 0 | K slot 1 | V slot 0 | V slot 1]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
     const uint32_t lds0 = lds_addr(smem);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-    const int rb = wave & 3;   // 32-row block of the workgroup's rows
-    const int kg = KSPLIT == 1 ? 0 : wave >> 2;  // key tile parity, and wave group
-    const uint32_t grp = lds0 + (uint32_t)kg * kGroupBytes;
 
     // workgroup -> (live row block, head), head fastest; surplus workgroups exit
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
@@ -127,13 +131,34 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParam
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BM;
-
-    const int kv_end = CAUSAL ? min(sb.lk, m0 + BM) : sb.lk;
-    const int ntiles = (kv_end + BN - 1) / BN;
-    const int row0 = m0 + 32 * rb;  // first row of this wave
+    const int row0 = m0 + 32 * wave;  // first row of this wave
     const int my_row = row0 + l32;
     const bool wave_live = row0 < sb.lq;
-    const int lim = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
+
+    // Keys [kv_begin, kv_end) some row of the block sees, and this lane's own
+    // interval [lo, lo + span).
+    int kv_begin = 0, kv_end = sb.lk, lo = 0, span;
+    // window only: keys every live row of the wave sees [full_lo, full_hi), and
+    // keys some live row of the wave sees [any_lo, any_hi)
+    int full_lo = 0, full_hi = 0, any_lo = 0, any_hi = 0;
+    if constexpr (WINDOW) {
+        const int L = p.win_left, R = p.win_right;
+        const int last = min(m0 + BM, sb.lq) - 1;
+        kv_begin = max(0, m0 - L);
+        kv_end = max(kv_begin, min(sb.lk, last + R + 1));
+        lo = max(0, my_row - L);
+        span = max(0, min(sb.lk, my_row + R + 1) - lo);
+        const int wlast = min(row0 + 31, sb.lq - 1);
+        full_lo = max(0, wlast - L);
+        full_hi = min(sb.lk, row0 + R + 1);
+        any_lo = max(0, row0 - L);
+        any_hi = min(sb.lk, wlast + R + 1);
+    } else {
+        if (CAUSAL) kv_end = min(sb.lk, m0 + BM);
+        span = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
+    }
+    const int t0 = kv_begin / BN;
+    const int ntiles = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
 
     uint4 qf[KSTEPS];
     {
@@ -144,13 +169,13 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParam
     }
     uint32_t koff[KSTEPS];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = grp + tile_byte(l32, 2 * kk + g);
+    for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = lds0 + tile_byte(l32, 2 * kk + g);
     uint2 voff[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         voff[db] = tr_offsets(32 * db, lane);
-        voff[db].x += grp + 2 * kTileBytes;
-        voff[db].y += grp + 2 * kTileBytes;
+        voff[db].x += lds0 + 2 * kTileBytes;
+        voff[db].y += lds0 + 2 * kTileBytes;
     }
     f32x16 oacc[NDB];
 #pragma unroll
@@ -160,45 +185,49 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParam
         const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
         const uint16_t* vbase = p.v.base + (int64_t)sb.k0 * p.v.tok + (int64_t)h * p.v.head;
         TileDma<D> kdma, vdma;
-        kdma.init(rb, lane, p.k.tok);
-        vdma.init(rb, lane, p.v.tok);
+        kdma.init(wave, lane, p.k.tok);
+        vdma.init(wave, lane, p.v.tok);
         if constexpr (D < 32) {
             // columns D..31 of every slot are read by the 32-wide MFMA blocks
             constexpr int U = kTileRows * (32 - D) / 8;  // 16-byte units per slot
-            for (int u = tid; u < 4 * KSPLIT * U; u += 256 * KSPLIT) {
+            for (int u = tid; u < 4 * U; u += 256) {
                 const int sl = u / U, v = u % U;
                 const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
                 ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
             }
         }
-        if (kg < ntiles) {
-            kdma.issue(grp, kbase, p.k.tok, kg * BN, kv_end);
-            vdma.issue(grp + 2 * kTileBytes, vbase, p.v.tok, kg * BN, kv_end);
-        }
+        kdma.issue(lds0, kbase, p.k.tok, t0 * BN, kv_end);
+        vdma.issue(lds0 + 2 * kTileBytes, vbase, p.v.tok, t0 * BN, kv_end);
         wait_global_loads();
         __syncthreads();
 
-        // Step s: group kg computes tile t = KSPLIT s + kg from slot s % 2 while the
-        // tile after it (t + KSPLIT) streams into the other slot.  Only the tiles
-        // that cross a wave's diagonal or the sequence end need the per-element
-        // mask, and those are the block's last two tiles: for a causal block m the
-        // first tile crossing a diagonal is tile 2m of 2m + 2; without a causal
-        // mask only the last tile can pass the sequence end.  They fall in the
-        // last step when two groups split the tiles, in the last two otherwise.
-        // Slots alternate at compile time so that every LDS offset is an immediate.
-        const int nsteps = (ntiles + KSPLIT - 1) / KSPLIT;
-        const int nplain = nsteps - min(nsteps, KSPLIT == 1 ? 2 : 1);
+        // Step s computes tile t0 + s from slot s % 2 while tile t0 + s + 1 streams
+        // into the other slot.  Without a window only the tiles that cross a
+        // wave's diagonal or the sequence end need the per-element mask, and those
+        // are the block's last two tiles: for a causal block m the first tile
+        // crossing a diagonal is tile 2m of 2m + 2; without a causal mask only the
+        // last tile can pass the sequence end.  Slots alternate at compile time so
+        // that every LDS offset is an immediate.
+        const int nplain = WINDOW ? ntiles : ntiles - min(ntiles, 2);
         auto step = [&](int s, auto slot, auto masked) {
             constexpr uint32_t cur = decltype(slot)::value * kTileBytes, nxt = kTileBytes - cur;
-            const int t = KSPLIT * s + kg;  // this group's tile
-            if (t + KSPLIT < ntiles) {  // the other slots were last read before the previous barrier
-                kdma.issue(grp + nxt, kbase, p.k.tok, (t + KSPLIT) * BN, kv_end);
-                vdma.issue(grp + 2 * kTileBytes + nxt, vbase, p.v.tok, (t + KSPLIT) * BN, kv_end);
+            if (s + 1 < ntiles) {  // the other slots were last read before the previous barrier
+                kdma.issue(lds0 + nxt, kbase, p.k.tok, (t0 + s + 1) * BN, kv_end);
+                vdma.issue(lds0 + 2 * kTileBytes + nxt, vbase, p.v.tok, (t0 + s + 1) * BN, kv_end);
             }
-            const int n0 = t * BN;
-            // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
-            if (t < ntiles && wave_live && !(CAUSAL && n0 > row0 + 31))
-                fwd_tile<D, decltype(masked)::value, cur, cur>(qf, oacc, koff, voff, n0, lim, g);
+            const int n0 = (t0 + s) * BN;
+            if constexpr (WINDOW) {
+                if (wave_live && n0 + BN > any_lo && n0 < any_hi) {
+                    if (n0 >= full_lo && n0 + BN <= full_hi)
+                        fwd_tile<D, false, cur, cur>(qf, oacc, koff, voff, n0, lo, span, g);
+                    else
+                        fwd_tile<D, true, cur, cur>(qf, oacc, koff, voff, n0, lo, span, g);
+                }
+            } else {
+                // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
+                if (wave_live && !(CAUSAL && n0 > row0 + 31))
+                    fwd_tile<D, decltype(masked)::value, cur, cur>(qf, oacc, koff, voff, n0, lo, span, g);
+            }
             wait_global_loads();
             __syncthreads();
         };
@@ -208,42 +237,13 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParam
             step(s, S0{}, std::false_type{});
             if (s + 1 < nplain) step(s + 1, S1{}, std::false_type{});
         }
-        for (int s = nplain; s < nsteps; ++s) {
+        for (int s = nplain; s < ntiles; ++s) {
             if (s & 1) step(s, S1{}, std::true_type{});
             else step(s, S0{}, std::true_type{});
         }
-
-        // the odd-tile group hands its partial sums to the even-tile group through LDS
-        if (KSPLIT > 1 && ntiles > 1) {
-            const uint32_t red = lds0 + (uint32_t)rb * (NDB * 16 * 64 * 4) + 16u * lane;
-            if (kg == 1) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const f32x16& a = oacc[db];
-                        ds_write16(red + (uint32_t)((db * 4 + j) * 1024),
-                                   make_uint4(__float_as_uint(a[4 * j]), __float_as_uint(a[4 * j + 1]),
-                                              __float_as_uint(a[4 * j + 2]), __float_as_uint(a[4 * j + 3])));
-                    }
-            }
-            __syncthreads();
-            if (kg == 0) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint4 w = ds_read16(red + (uint32_t)((db * 4 + j) * 1024));
-                        oacc[db][4 * j] += __uint_as_float(w.x);
-                        oacc[db][4 * j + 1] += __uint_as_float(w.y);
-                        oacc[db][4 * j + 2] += __uint_as_float(w.z);
-                        oacc[db][4 * j + 3] += __uint_as_float(w.w);
-                    }
-            }
-        }
     }
 
-    if (kg != 0 || my_row >= sb.lq) return;
+    if (my_row >= sb.lq) return;
     uint16_t* dst = p.o.base + (int64_t)(sb.q0 + my_row) * p.o.tok + (int64_t)h * p.o.head;
     const float sc = p.pre_scale;
 #pragma unroll
@@ -261,26 +261,32 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_kernel(AttnParam
     }
 }
 
-#ifndef HSTU_FWD_KSPLIT
-#define HSTU_FWD_KSPLIT 1
-#endif
-template <int D, bool CAUSAL>
+template <int D, MaskKind MK>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
-    constexpr int KSPLIT = HSTU_FWD_KSPLIT;
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, KSPLIT>), dim3((unsigned)grid), dim3(256 * KSPLIT), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, MK>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams& p, MaskKind mask, hipStream_t stream) {
+    switch (mask) {
+        case MaskKind::None: return launch<D, MaskKind::None>(p, stream);
+        case MaskKind::Causal: return launch<D, MaskKind::Causal>(p, stream);
+        case MaskKind::Window: return launch<D, MaskKind::Window>(p, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const AttnParams& p, int head_dim, bool causal, hipStream_t stream) {
+hipError_t launch_fwd(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
     switch (head_dim) {
-        case 16: return causal ? launch<16, true>(p, stream) : launch<16, false>(p, stream);
-        case 32: return causal ? launch<32, true>(p, stream) : launch<32, false>(p, stream);
-        case 64: return causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-        case 128: return causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+        case 16: return launch_d<16>(p, mask, stream);
+        case 32: return launch_d<32>(p, mask, stream);
+        case 64: return launch_d<64>(p, mask, stream);
+        case 128: return launch_d<128>(p, mask, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -9,6 +9,12 @@
 
 namespace hstu {
 
+// Mask the kernels are built for.  A token window (left, right) admits key j for
+// query i (local indices) iff i - left <= j <= i + right; the host resolves the
+// windows that equal full attention or causal to those kinds, and a window side
+// with no bound to a bound of max_seqlen_k, which cuts nothing.
+enum class MaskKind : int { None = 0, Causal = 1, Window = 2 };
+
 struct AttnParams {
     const int32_t* cu_q;   // (B + 1) cumulative query lengths, device
     const int32_t* cu_k;   // (B + 1) cumulative key lengths, device
@@ -21,6 +27,8 @@ struct AttnParams {
     float out_scale;       // alpha / L_scale: the epilogue factor of dQ and dK
     float pre_scale;       // alpha / (L_scale c): the factor of O and dV, whose sums run over
                            // scores pre-multiplied by c = exp_c (0 when alpha = 0)
+    int32_t win_left;      // MaskKind::Window: 0 <= left, right <= max_seqlen_k <= 2^29
+    int32_t win_right;
     TensorRef q, k, v, dout;
     TensorOut o, dq, dk, dv;
 };
@@ -33,8 +41,12 @@ constexpr int kBwdBlockN = 128;   // key rows per dK/dV workgroup
 // most 64 strides, addressed by unsigned 32-bit byte offsets.
 constexpr int64_t kMaxTokenStride = int64_t(1) << 24;
 
-hipError_t launch_fwd(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
-hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, bool causal, hipStream_t stream);
+// Largest max_seqlen_k a window mask accepts: bounds such as i + right + 1, for
+// rows i up to a block (128 rows) past the sequence end, stay inside int32.
+constexpr int32_t kMaxWindowSeqlen = 1 << 29;
+
+hipError_t launch_fwd(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 
 }  // namespace hstu

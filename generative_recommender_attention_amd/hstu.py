@@ -6,8 +6,10 @@ stream.  The functions mirror the HSTU Attention page's allocating functions
 ("High-level functions"): ``hstu_fwd`` returns the packed output, ``hstu_bwd``
 returns (dq, dk, dv); caller-owned outputs may be passed in and are
 overwritten.  ``causal=True`` is the page's ``window_size=(-1, 0)`` and
-``causal=False`` its ``(-1, -1)``.  There is no fallback: if the library is
-missing, every call raises.
+``causal=False`` its ``(-1, -1)``; ``window_size=(left, right)``, when given,
+sets the mask instead ("Mask support": key j visible to query i iff
+i - left <= j <= i + right, -1 = unbounded).  There is no fallback: if the
+library is missing, every call raises.
 """
 
 from __future__ import annotations
@@ -36,6 +38,7 @@ __all__ = [
     "HSTU_ERR_DEVICE",
     "HSTU_MASK_NONE",
     "HSTU_MASK_CAUSAL",
+    "HSTU_MASK_WINDOW",
 ]
 
 HSTU_OK = 0
@@ -44,7 +47,8 @@ HSTU_ERR_UNSUPPORTED = 2
 HSTU_ERR_DEVICE = 3
 HSTU_MASK_NONE = 0
 HSTU_MASK_CAUSAL = 1
-ABI_VERSION = 2
+HSTU_MASK_WINDOW = 2
+ABI_VERSION = 3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -73,6 +77,8 @@ class HstuArgs(ctypes.Structure):
         ("alpha", ctypes.c_float),
         ("scaling_seqlen", ctypes.c_int32),
         ("mask", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
         ("q", HstuStride),
         ("k", HstuStride),
         ("v", HstuStride),
@@ -173,7 +179,7 @@ def _stream(stream, device) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal) -> HstuArgs:
+def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size) -> HstuArgs:
     a = HstuArgs()
     a.batch = int(cu_q.shape[0]) - 1
     a.total_q = int(q.shape[0])
@@ -184,7 +190,11 @@ def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal)
     a.max_seqlen_k = int(max_seqlen_k)
     a.alpha = float(alpha)
     a.scaling_seqlen = 0 if scaling_seqlen is None else int(scaling_seqlen)
-    a.mask = HSTU_MASK_CAUSAL if causal else HSTU_MASK_NONE
+    if window_size is None:
+        a.mask = HSTU_MASK_CAUSAL if causal else HSTU_MASK_NONE
+    else:
+        left, right = (int(w) for w in window_size)
+        a.mask, a.window_left, a.window_right = HSTU_MASK_WINDOW, left, right
     if scaling_seqlen is not None and int(scaling_seqlen) <= 0:
         raise ValueError("scaling_seqlen must be positive")
     return a
@@ -209,23 +219,25 @@ def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
              max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
              scaling_seqlen: Optional[int] = None, causal: bool = True,
-             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, stream=None,
+             window_size: Optional[Tuple[int, int]] = None) -> torch.Tensor:
     """O = HSTU(q, k, v) on packed (T, H, D) bf16 tensors; returns ``out``."""
     H, D, pq, pk = _inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     _thd("out", out, int(q.shape[0]), H, D)
-    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal)
+    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
     a.q, a.k, a.v, a.o = _stride(q), _stride(k), _stride(v), _stride(out)
     _check(library().hstu_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(), pq, pk,
                               out.data_ptr(), _stream(stream, q.device)))
     return out
 
 
-def _bwd_common(dout, q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal):
+def _bwd_common(dout, q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal,
+                window_size):
     H, D, pq, pk = _inputs(q, k, v, cu_q, cu_k)
     _thd("dout", dout, int(q.shape[0]), H, D)
-    a = _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal)
+    a = _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
     a.q, a.k, a.v, a.dout = _stride(q), _stride(k), _stride(v), _stride(dout)
     return H, D, pq, pk, a
 
@@ -235,13 +247,13 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
              scaling_seqlen: Optional[int] = None, causal: bool = True,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None
-             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+             window_size: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.  ``workspace``
     (a device byte tensor) is allocated here when the library asks for one and
     none is given."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -262,20 +274,21 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
 
 
 def hstu_bwd_workspace_size(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                            alpha=1.0, scaling_seqlen=None, causal=True) -> int:
+                            alpha=1.0, scaling_seqlen=None, causal=True, window_size=None) -> int:
     """Bytes of device workspace ``hstu_bwd`` needs for this problem."""
     _, _, _, _, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, alpha,
-                                scaling_seqlen, causal)
+                                scaling_seqlen, causal, window_size)
     need = ctypes.c_size_t(0)
     _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
     return int(need.value)
 
 
 def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                alpha=1.0, scaling_seqlen=None, causal=True, dq=None, stream=None) -> torch.Tensor:
+                alpha=1.0, scaling_seqlen=None, causal=True, dq=None, stream=None,
+                window_size=None) -> torch.Tensor:
     """dq only (the query-major backward kernel)."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     _thd("dq", dq, int(q.shape[0]), H, D)
     a.dq = _stride(dq)
@@ -285,10 +298,11 @@ def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seq
 
 
 def hstu_bwd_dkdv(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                  alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None):
+                  alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None,
+                  window_size=None):
     """(dk, dv) only (the key-major backward kernel)."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     _thd("dk", dk, int(k.shape[0]), H, D)

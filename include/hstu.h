@@ -36,11 +36,21 @@
  *   fine; overlap between an output and a live input is not checked.
  *
  * -- Masks ("Mask support" table) ---------------------------------------------
+ *   The page's window_size = (left, right): key j is visible to query i (both
+ *   indices local to the sequence, counted from its first query and first key)
+ *   iff i - left <= j <= i + right, where -1 leaves that side unbounded.  This
+ *   is the FlashAttention-2 convention, the one the cuDNN SDPA page relates its
+ *   diagonal band bounds to (its left bound is our left + 1, its right bound our
+ *   right).  The band is aligned top-left; with equal query and key lengths
+ *   this is also the bottom-right alignment.
  *   HSTU_MASK_NONE   : window (-1, -1), every key of the sequence is visible.
- *   HSTU_MASK_CAUSAL : window (-1, 0), key j is visible to query i (both indices
- *                      local to the sequence) iff j <= i.  The diagonal is
- *                      aligned top-left; with equal query and key lengths this
- *                      is the usual causal mask.
+ *   HSTU_MASK_CAUSAL : window (-1, 0): j <= i.
+ *   HSTU_MASK_WINDOW : window (window_left, window_right), each >= -1; a local
+ *                      (sliding) window when either side is finite.  (-1, -1)
+ *                      and (-1, 0) run exactly as HSTU_MASK_NONE and
+ *                      HSTU_MASK_CAUSAL.  Needs max_seqlen_k <= 2^29
+ *                      (HSTU_ERR_UNSUPPORTED otherwise).
+ *   window_left and window_right are read only with HSTU_MASK_WINDOW.
  *
  * -- Trust and validation ("Tensor layout", the paragraph on metadata) --------
  *   The library checks every scalar and pointer argument on the host and never
@@ -81,7 +91,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 2
+#define HSTU_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define HSTU_API __attribute__((visibility("default")))
@@ -98,7 +108,8 @@ typedef enum hstu_status {
 
 typedef enum hstu_mask {
     HSTU_MASK_NONE = 0,   /* window (-1, -1) */
-    HSTU_MASK_CAUSAL = 1  /* window (-1, 0), top-left aligned */
+    HSTU_MASK_CAUSAL = 1, /* window (-1, 0), top-left aligned */
+    HSTU_MASK_WINDOW = 2  /* window (window_left, window_right), top-left aligned */
 } hstu_mask_t;
 
 /* Strides of one (T, H, D) tensor, in elements.  {0, 0} = packed. */
@@ -120,6 +131,8 @@ typedef struct hstu_args {
     float alpha;            /* score scale, finite                                        */
     int32_t scaling_seqlen; /* L_scale > 0; 0 selects max_seqlen_q; < 0 is rejected      */
     int32_t mask;           /* an hstu_mask_t                                             */
+    int32_t window_left;    /* HSTU_MASK_WINDOW: keys j >= i - window_left; -1 = no bound  */
+    int32_t window_right;   /* HSTU_MASK_WINDOW: keys j <= i + window_right; -1 = no bound */
     hstu_stride_t q, k, v;  /* input strides                                              */
     hstu_stride_t o;        /* forward output                                             */
     hstu_stride_t dout;     /* backward upstream gradient                                 */

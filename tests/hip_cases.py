@@ -50,7 +50,7 @@ class DeviceWorkload:
     def kw(self):
         wl = self.wl
         return dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, alpha=float(wl.alpha),
-                    scaling_seqlen=wl.scaling_seqlen, causal=wl.causal)
+                    scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window)
 
     def fwd(self, **over):
         kw = self.kw()

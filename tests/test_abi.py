@@ -46,10 +46,14 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    # 7 int32 + float + 2 int32 = 40 bytes, then 8 stride pairs of 16 bytes
-    assert ctypes.sizeof(hstu.HstuArgs) == 40 + 8 * 16
-    assert hstu.HstuArgs.q.offset == 40
-    assert hstu.HstuArgs.dv.offset == 40 + 7 * 16
+    # 7 int32 + float + 4 int32 = 48 bytes, then 8 stride pairs of 16 bytes
+    assert ctypes.sizeof(hstu.HstuArgs) == 48 + 8 * 16
+    assert hstu.HstuArgs.mask.offset == 36
+    assert hstu.HstuArgs.window_left.offset == 40 and hstu.HstuArgs.window_right.offset == 44
+    assert hstu.HstuArgs.q.offset == 48
+    assert hstu.HstuArgs.dv.offset == 48 + 7 * 16
+    text = open(HEADER).read()
+    assert re.search(r"HSTU_MASK_WINDOW\s*=\s*2", text) and hstu.HSTU_MASK_WINDOW == 2
 
 
 def good_args(**kw):
@@ -72,7 +76,11 @@ REJECT = [
     # (description, args overrides, expected status)
     ("head_dim 48", dict(head_dim=48), hstu.HSTU_ERR_UNSUPPORTED),
     ("head_dim 256", dict(head_dim=256), hstu.HSTU_ERR_UNSUPPORTED),
-    ("mask 2", dict(mask=2), hstu.HSTU_ERR_UNSUPPORTED),
+    ("mask 3", dict(mask=3), hstu.HSTU_ERR_UNSUPPORTED),
+    ("window left -2", dict(mask=2, window_left=-2, window_right=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("window right -5", dict(mask=2, window_left=3, window_right=-5), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("window past 2^29 keys", dict(mask=2, window_left=8, window_right=0, total_q=(1 << 29) + 2,
+                                   total_k=(1 << 29) + 2, max_seqlen_k=(1 << 29) + 1), hstu.HSTU_ERR_UNSUPPORTED),
     ("batch 0", dict(batch=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("heads 0", dict(num_heads=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("negative total", dict(total_q=-1), hstu.HSTU_ERR_INVALID_ARGUMENT),

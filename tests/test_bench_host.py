@@ -1,0 +1,36 @@
+"""Host logic of the benchmark: the visible-pair count its flop figures rest on,
+and the refusal of more than one GPU.  No GPU is touched."""
+
+import json
+
+import numpy as np
+import pytest
+
+import bench
+
+
+def brute_pairs(lq, lk, left, right):
+    n = 0
+    for i in range(lq):
+        for j in range(lk):
+            if (left < 0 or j >= i - left) and (right < 0 or j <= i + right):
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (-1, 0), (0, 0), (3, 0), (2, 5), (-1, 4), (7, -1), (40, 40)])
+def test_visible_pairs_matches_brute_force(window):
+    lens_q, lens_k = [0, 1, 9, 17, 30], [4, 1, 12, 17, 25]
+    want = sum(brute_pairs(a, b, *window) for a, b in zip(lens_q, lens_k))
+    assert bench.visible_pairs(lens_q, lens_k, window) == want
+
+
+def test_causal_pairs_closed_form():
+    n = np.array([1, 64, 4096])
+    assert bench.visible_pairs(n, n, (-1, 0)) == int((n * (n + 1) // 2).sum())
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    out = json.loads(capsys.readouterr().out.strip())
+    assert "one GPU" in out["error"]

@@ -27,7 +27,7 @@ def _need_gpu():
 
 def run_fwd_check(wl, rows=None, tag=""):
     dw = DeviceWorkload(wl)
-    say(f"hstu_fwd {wl.name}{tag}: B={wl.batch} T={wl.total_q} H={wl.num_heads} D={wl.head_dim} causal={wl.causal}")
+    say(f"hstu_fwd {wl.name}{tag}: B={wl.batch} T={wl.total_q} H={wl.num_heads} D={wl.head_dim} mask={wl.mask_name}")
     o = dw.fwd()
     torch.cuda.synchronize()
     got = to_f64(o)
@@ -40,7 +40,7 @@ def run_fwd_check(wl, rows=None, tag=""):
 def run_bwd_check(wl, rows_q=None, rows_k=None, tag=""):
     dw = DeviceWorkload(wl)
     say(f"hstu_bwd {wl.name}{tag}: B={wl.batch} Tq={wl.total_q} Tk={wl.total_k} H={wl.num_heads} "
-        f"D={wl.head_dim} causal={wl.causal}")
+        f"D={wl.head_dim} mask={wl.mask_name}")
     dq, dk, dv = dw.bwd()
     torch.cuda.synchronize()
     rq, rk, rv = oracle.bwd_workload(wl, rows_q, rows_k)
@@ -118,6 +118,66 @@ def test_single_long_sequence_full_mask(oracle_lib):
     wl = make_workload("single", 111, [777], 1, 128, False, 0.5, with_do=True)
     run_fwd_check(wl)
     run_bwd_check(wl)
+
+
+# ------------------------------------------------------------------ token windows
+WINDOW_CASES = [
+    # (seed, lengths_q, lengths_k or None, H, D, (left, right))
+    (130, EDGE_LENGTHS, None, 2, 128, (64, 0)),
+    (131, EDGE_LENGTHS, None, 2, 64, (0, 0)),                    # diagonal only
+    (132, EDGE_LENGTHS, None, 1, 32, (100, 37)),                 # bounds off the tile grid
+    (133, EDGE_LENGTHS, None, 2, 16, (-1, 65)),                  # right bound only
+    (134, EDGE_LENGTHS, None, 2, 128, (129, -1)),                # left bound only
+    (135, [300, 5, 0, 257], [310, 9, 4, 257], 2, 64, (31, 3)),   # L_k > L_q
+    (136, [130, 40, 7], [131, 38, 3], 3, 128, (5, 70)),          # L_k < L_q
+    (137, [700, 1000], None, 2, 128, (256, 128)),                # interior tiles with no per-element test
+    (138, [3] * 40 + [250], None, 1, 128, (1, 1)),               # many tiny sequences
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[f"seed{c[0]}_d{c[4]}_w{c[5][0]}_{c[5][1]}"
+                                                    for c in WINDOW_CASES])
+def test_window_fwd_bwd(oracle_lib, case):
+    seed, lq, lk, H, D, window = case
+    wl = make_workload(f"win{seed}", seed, lq, H, D, False, 1.0, lengths_k=lk, with_do=True, window=window)
+    run_fwd_check(wl)
+    run_bwd_check(wl)
+
+
+def test_long_window_workload_sampled(oracle_lib):
+    wl = named_workload("long_b4_h8_d128_window1024")
+    rows = sample_rows(wl.cu_seqlens_q, per_seq=24, seed=5)
+    rel, worst = run_fwd_check(wl, rows, " (sampled rows)")
+    print(f"long window fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
+    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    print("long window bwd (err/max, worst per-seq):", res)
+
+
+def test_windows_naming_full_and_causal_are_those_masks_bitwise():
+    """(-1, 0) and (-1, -1) run the causal and full kernels; a window whose bounds
+    reach past every sequence runs the window kernel and must agree bit for bit
+    with full attention (same tiles, same order, only the masking path differs)."""
+    wl = make_workload("wnames", 139, [200, 64, 129], 2, 64, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    say("window (-1, 0) vs causal, (-1, -1) and (500, 500) vs full")
+    oc, gc = dw.fwd(causal=True), dw.bwd(causal=True)
+    ow, gw = dw.fwd(window_size=(-1, 0)), dw.bwd(window_size=(-1, 0))
+    of, gf = dw.fwd(causal=False), dw.bwd(causal=False)
+    on, gn = dw.fwd(window_size=(-1, -1)), dw.bwd(window_size=(-1, -1))
+    ob, gb = dw.fwd(window_size=(500, 500)), dw.bwd(window_size=(500, 500))
+    torch.cuda.synchronize()
+    assert torch.equal(oc, ow) and all(torch.equal(a, b) for a, b in zip(gc, gw))
+    assert torch.equal(of, on) and all(torch.equal(a, b) for a, b in zip(gf, gn))
+    assert torch.equal(of, ob) and all(torch.equal(a, b) for a, b in zip(gf, gb))
+
+
+def test_window_invalid_bounds_raise():
+    wl = make_workload("wbad", 140, [10], 1, 16, True)
+    dw = DeviceWorkload(wl)
+    with pytest.raises(hstu.HstuError):
+        dw.fwd(window_size=(-2, 0))
+    with pytest.raises(hstu.HstuError):
+        hstu.hstu_bwd(dw.q, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, 10, 10, window_size=(3, -7))
 
 
 # ------------------------------------------------------------------ invariants
