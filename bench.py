@@ -85,9 +85,9 @@ def load_traffic(kernel: str, workload: str):
 
 
 PROFILE_COMMANDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py --no-cpu-baseline --workload {w}",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cfetch -o run -- python3 bench.py --calibrate-copy-mib 256",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cwrite -o run -- python3 bench.py --calibrate-copy-mib 256",
 }
@@ -96,7 +96,8 @@ ALG_TENSORS = {"fwd_kernel": 4, "bwd_dq_kernel": 5, "bwd_dkdv_kernel": 6}  # (T,
 
 def summarize_profiles(prof_dir: str, workload: str) -> None:
     """Turn the rocprofv3 outputs of PROFILE_COMMANDS (run from the repository root,
-    prof_dir relative to it) into profiles/traffic.json and the two text summaries."""
+    prof_dir relative to it) into the kernel-trace summary and, when the PMC passes
+    are there too, profiles/traffic.json and the HBM-traffic summary."""
     import csv
     import glob
 
@@ -121,19 +122,36 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
 
     kernels = list(ALG_TENSORS)
     copy = ["copyBuffer"]
+    from generative_recommender_attention_amd.workloads import named_workload
+
+    wl = named_workload(workload)
+    stats = rows("kt", "*kernel_stats.csv")
+    out = [f"# rocprofv3 kernel trace: HSTU attention fwd + bwd, workload {workload}", "",
+           f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
+           f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
+           "hstu_bwd_dq + hstu_bwd_dkdv.", "", "Command (GPU box, from the repository root):",
+           "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir, w=workload), "",
+           f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        short = next((k for k in kernels if k in name), name.split("(")[0][-26:])
+        out.append(f"{short:26s}{int(r['Calls']):8d}{float(r['AverageNs']):11.0f}{float(r['MinNs']):11.0f}"
+                   f"{float(r['MaxNs']):11.0f}{float(r['Percentage']):7.1f}%")
+    with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    if not os.path.isdir(os.path.join(prof_dir, "fetch")):
+        print(f"wrote the kernel-trace summary for {workload} (no PMC passes under {prof_dir})")
+        return
     fetch, write = counter_kib("fetch", "FETCH_SIZE", kernels), counter_kib("write", "WRITE_SIZE", kernels)
     cfetch, cwrite = counter_kib("cfetch", "FETCH_SIZE", copy), counter_kib("cwrite", "WRITE_SIZE", copy)
     copy_kib = 256 * 1024.0
     ff, wf = copy_kib / cfetch["copyBuffer"], copy_kib / cwrite["copyBuffer"]
-    from generative_recommender_attention_amd.workloads import named_workload
-
-    wl = named_workload(workload)
     tensor_bytes = wl.total_q * wl.num_heads * wl.head_dim * 2
     traffic = {"source_digest": kernel_source_digest(), "workload": workload, "fetch_factor": ff, "write_factor": wf,
                "kernels": {}}
     lines = [f"# HBM traffic per dispatch (rocprofv3 PMC), workload {workload}", "",
              "Commands (GPU box, repository root; one counter per pass):"]
-    lines += ["    " + PROFILE_COMMANDS[k].format(d=prof_dir) for k in ("fetch", "write", "cfetch", "cwrite")]
+    lines += ["    " + PROFILE_COMMANDS[k].format(d=prof_dir, w=workload) for k in ("fetch", "write", "cfetch", "cwrite")]
     lines += ["", f"copy of {copy_kib:.0f} KiB (the HIP runtime's __amd_rocclr_copyBuffer): FETCH_SIZE reads "
                   f"{cfetch['copyBuffer']:.1f} KiB -> fetch factor {ff:.4f}",
               f"{'':48s}WRITE_SIZE reads {cwrite['copyBuffer']:.1f} KiB -> write factor {wf:.4f}", "",
@@ -152,20 +170,6 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_hbm_traffic.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    stats = rows("kt", "*kernel_stats.csv")
-    out = [f"# rocprofv3 kernel trace: HSTU attention fwd + bwd, workload {workload}", "",
-           f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
-           f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
-           "hstu_bwd_dq + hstu_bwd_dkdv.", "", "Command (GPU box, from the repository root):",
-           "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir), "",
-           f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"]
-        short = next((k for k in kernels if k in name), name.split("(")[0][-26:])
-        out.append(f"{short:26s}{int(r['Calls']):8d}{float(r['AverageNs']):11.0f}{float(r['MinNs']):11.0f}"
-                   f"{float(r['MaxNs']):11.0f}{float(r['Percentage']):7.1f}%")
-    with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_kernel_trace.txt"), "w") as f:
-        f.write("\n".join(out) + "\n")
     print(f"wrote profiles/traffic.json and the summaries for {workload}")
 
 
