@@ -17,7 +17,10 @@ round-to-nearest-even, then (for the backward workload) the upstream gradient
 query lengths; the score scale is the fp32 value of ``1/sqrt(D)``; the
 normaliser ``scaling_seqlen`` is the longest query length.  The mask is causal
 or full (``causal``) unless a token window ``(left, right)`` is given (HSTU
-Attention page, "Mask support": ``window_size``, -1 = unbounded side).
+Attention page, "Mask support": ``window_size``, -1 = unbounded side), or an
+arbitrary mask: the page's ``func_tensor``, held here as an int32 ``(N, T_q)``
+array whose column r lists the endpoints of packed query row r (visible keys
+``[0, F0) u [F1, F2) u ...`` in local key indices).
 """
 
 from __future__ import annotations
@@ -33,6 +36,8 @@ __all__ = [
     "bf16_bits_to_f32",
     "make_workload",
     "named_workload",
+    "func_target_mask",
+    "func_random_mask",
     "WORKLOAD_NAMES",
 ]
 
@@ -78,6 +83,7 @@ class Workload:
     v: np.ndarray                  # (T_k, H, D) uint16
     do: Optional[np.ndarray] = None  # (T_q, H, D) uint16, backward only
     window: Optional[Tuple[int, int]] = None  # (left, right); None: causal / full per `causal`
+    func: Optional[np.ndarray] = None         # (N, T_q) int32 interval endpoints; overrides the rest
 
     @property
     def window_size(self) -> Tuple[int, int]:
@@ -87,7 +93,14 @@ class Workload:
         return (-1, 0) if self.causal else (-1, -1)
 
     @property
+    def mask_spec(self):
+        """The mask as the oracle takes it: the func array, else the window pair."""
+        return self.func if self.func is not None else self.window_size
+
+    @property
     def mask_name(self) -> str:
+        if self.func is not None:
+            return f"func(N={self.func.shape[0]})"
         left, right = self.window_size
         if (left, right) == (-1, -1):
             return "none"
@@ -145,6 +158,7 @@ def make_workload(
     scaling_seqlen: Optional[int] = None,
     rng: Optional[np.random.Generator] = None,
     window: Optional[Tuple[int, int]] = None,
+    func: Optional[np.ndarray] = None,
 ) -> Workload:
     """Build a workload from explicit lengths.
 
@@ -193,10 +207,53 @@ def make_workload(
         v=v,
         do=do,
         window=window,
+        func=None if func is None else _check_func(func, tq),
     )
 
 
-# The six synthetic workloads the measurement is defined on.  Names say what
+def _check_func(func: np.ndarray, total_q: int) -> np.ndarray:
+    f = np.ascontiguousarray(func, dtype=np.int32)
+    if f.ndim != 2 or f.shape[0] % 2 != 1 or f.shape[1] != total_q:
+        raise ValueError("func must be (N, T_q) int32 with N odd")
+    return f
+
+
+def func_target_mask(lengths: Sequence[int], max_candidates: int = 256) -> np.ndarray:
+    """Arbitrary-mask endpoints (N = 3) for a history + candidates layout: in a
+    sequence of length L the last c = min(max_candidates, max(1, L // 8)) tokens are
+    candidates.  History row i sees keys [0, i + 1) (causal); candidate row i sees
+    the whole history [0, L - c) and itself [i, i + 1), no other candidate."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    total = int(lengths.sum())
+    f = np.zeros((3, total), dtype=np.int32)
+    r = 0
+    for L in lengths.tolist():
+        c = min(max_candidates, max(1, L // 8)) if L else 0
+        h = L - c
+        i = np.arange(L)
+        hist = i < h
+        f[0, r:r + L] = np.where(hist, i + 1, h)
+        f[1, r:r + L] = np.where(hist, 0, i)
+        f[2, r:r + L] = np.where(hist, 0, i + 1)
+        r += L
+    return f
+
+
+def func_random_mask(rng: np.random.Generator, lengths_q: Sequence[int], lengths_k: Sequence[int],
+                     n: int) -> np.ndarray:
+    """Random endpoints, n (odd) per query row, drawn uniformly from
+    [-3, L_k + 3] of the row's sequence: intervals overlap, come in any order,
+    may be empty or reversed, and reach past both ends of the sequence."""
+    if n % 2 != 1:
+        raise ValueError("n must be odd")
+    cols = []
+    for lq, lk in zip(np.asarray(lengths_q).tolist(), np.asarray(lengths_k).tolist()):
+        cols.append(rng.integers(-3, lk + 3, size=(n, lq), endpoint=True))
+    f = np.concatenate(cols, axis=1) if cols else np.zeros((n, 0))
+    return f.astype(np.int32)
+
+
+# The seven synthetic workloads the measurement is defined on.  Names say what
 # they are: batch, length law, heads, head dim and mask.
 WORKLOAD_NAMES = (
     "tiny_b2_h1_d16_causal",          # B=2, lengths [5, 11]
@@ -205,11 +262,12 @@ WORKLOAD_NAMES = (
     "long_b4_h8_d128_causal",         # B=4, lengths U[8192, 16384]
     "zipf_b32_h4_d128_causal_fwdbwd",  # the Zipf workload plus an upstream gradient
     "long_b4_h8_d128_window1024",      # the long workload, sliding window (1024, 0), with gradient
+    "zipf_b32_h4_d128_target_fwdbwd",  # the Zipf workload, history + candidates func mask, with gradient
 )
 
 
 def named_workload(name: str) -> Workload:
-    """Return one of the six synthetic workloads, fully deterministic."""
+    """Return one of the seven synthetic workloads, fully deterministic."""
     if name == "tiny_b2_h1_d16_causal":
         return make_workload(name, 0, [5, 11], 1, 16, True, 1.0)
     if name == "uniform_b8_h2_d64_full":
@@ -221,6 +279,11 @@ def named_workload(name: str) -> Workload:
         lens = np.clip(rng.zipf(1.2, size=32), 16, 4096)
         return make_workload(name, 2, lens, 4, 128, True, 0.5, rng=rng,
                              with_do=name.endswith("fwdbwd"))
+    if name == "zipf_b32_h4_d128_target_fwdbwd":
+        rng = np.random.default_rng(2)
+        lens = np.clip(rng.zipf(1.2, size=32), 16, 4096)
+        return make_workload(name, 2, lens, 4, 128, False, 0.5, rng=rng, with_do=True,
+                             func=func_target_mask(lens))
     if name == "long_b4_h8_d128_causal":
         rng = np.random.default_rng(3)
         lens = rng.integers(8192, 16384, size=4, endpoint=True)

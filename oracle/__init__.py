@@ -14,7 +14,9 @@ Every function takes packed ``(T, H, D)`` arrays and int32 cumulative offsets
 (HSTU Attention page, "Tensor layout") and returns fp64 arrays of the requested
 rows.  ``rows=None`` computes every row.  ``mask`` is the page's
 ``window_size=(left, right)`` ("Mask support"), -1 leaving a side unbounded;
-``True`` stands for causal ``(-1, 0)`` and ``False`` for full ``(-1, -1)``.
+``True`` stands for causal ``(-1, 0)`` and ``False`` for full ``(-1, -1)``; an
+int32 array of shape ``(N, L)`` or ``(1, N, L)`` is the page's arbitrary mask
+``func_tensor`` (row r's endpoints in column r).
 """
 
 from __future__ import annotations
@@ -61,15 +63,15 @@ def _load():
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_hstu_fwd.restype = ctypes.c_int
             lib.oracle_hstu_fwd.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p,
-                                            ctypes.c_double, ctypes.c_double, i64, i64,
+                                            ctypes.c_double, ctypes.c_double, i64, i64, i32p, i64, i64,
                                             i64p, i64, f64p]
             lib.oracle_hstu_bwd_dq.restype = ctypes.c_int
             lib.oracle_hstu_bwd_dq.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
-                                               ctypes.c_double, ctypes.c_double, i64, i64,
+                                               ctypes.c_double, ctypes.c_double, i64, i64, i32p, i64, i64,
                                                i64p, i64, f64p]
             lib.oracle_hstu_bwd_dkdv.restype = ctypes.c_int
             lib.oracle_hstu_bwd_dkdv.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
-                                                 ctypes.c_double, ctypes.c_double, i64, i64,
+                                                 ctypes.c_double, ctypes.c_double, i64, i64, i32p, i64, i64,
                                                  i64p, i64, f64p, f64p]
             _lib = lib
     return _lib
@@ -106,6 +108,21 @@ def window(mask) -> Tuple[int, int]:
     return left, right
 
 
+def _mask_args(mask, total_q: int):
+    """The C oracle's mask arguments (left, right, func, func_n, func_ld) and the
+    array they point into (kept alive by the caller)."""
+    if isinstance(mask, np.ndarray):
+        f = mask[0] if mask.ndim == 3 else mask
+        if f.ndim != 2 or f.dtype != np.int32 or f.shape[0] < 1 or f.shape[0] % 2 != 1:
+            raise ValueError("func mask must be int32 of shape (N, L) or (1, N, L) with N odd")
+        if f.shape[1] < total_q:
+            raise ValueError("func mask needs a column for every query row")
+        f = np.ascontiguousarray(f)
+        return (-1, -1, _ptr(f, ctypes.c_int32), f.shape[0], f.shape[1]), f
+    left, right = window(mask)
+    return (left, right, None, 0, 0), None
+
+
 def _prep(cu_q, cu_k, q, k, v, rows, total):
     cu_q = np.ascontiguousarray(cu_q, dtype=np.int32)
     cu_k = np.ascontiguousarray(cu_k, dtype=np.int32)
@@ -129,12 +146,13 @@ def fwd(cu_q, cu_k, q, k, v, alpha, scaling_seqlen, mask,
         rows: Optional[np.ndarray] = None) -> np.ndarray:
     """O rows (fp64, shape (n, H, D)) of HSTU attention."""
     cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, q.shape[0])
+    margs, _keep = _mask_args(mask, q.shape[0])
     H, D = q.shape[1], q.shape[2]
     out = np.empty((n, H, D), dtype=np.float64)
     rc = _load().oracle_hstu_fwd(
         cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
         _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
-        float(alpha), float(scaling_seqlen), *window(mask),
+        float(alpha), float(scaling_seqlen), *margs,
         None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
         _ptr(out, ctypes.c_double))
     if rc != 0:
@@ -146,6 +164,7 @@ def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
            rows: Optional[np.ndarray] = None) -> np.ndarray:
     """dQ rows (fp64) given the upstream gradient ``dout``."""
     cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, q.shape[0])
+    margs, _keep = _mask_args(mask, q.shape[0])
     dout = _f64(dout)
     if dout.shape != q.shape:
         raise ValueError("dout must match q")
@@ -154,7 +173,7 @@ def bwd_dq(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
     rc = _load().oracle_hstu_bwd_dq(
         cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
         _ptr(dout, ctypes.c_double), _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
-        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), *window(mask),
+        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), *margs,
         None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
         _ptr(out, ctypes.c_double))
     if rc != 0:
@@ -166,6 +185,7 @@ def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
              rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """(dK, dV) rows (fp64) for packed key rows ``rows``."""
     cu_q, cu_k, q, k, v, rows_arr, n = _prep(cu_q, cu_k, q, k, v, rows, k.shape[0])
+    margs, _keep = _mask_args(mask, q.shape[0])
     dout = _f64(dout)
     if dout.shape != q.shape:
         raise ValueError("dout must match q")
@@ -175,7 +195,7 @@ def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
     rc = _load().oracle_hstu_bwd_dkdv(
         cu_q.size - 1, _ptr(cu_q, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), H, D,
         _ptr(dout, ctypes.c_double), _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
-        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), *window(mask),
+        _ptr(v, ctypes.c_double), float(alpha), float(scaling_seqlen), *margs,
         None if rows_arr is None else _ptr(rows_arr, ctypes.c_int64), n,
         _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
     if rc != 0:
@@ -186,7 +206,7 @@ def bwd_dkdv(cu_q, cu_k, dout, q, k, v, alpha, scaling_seqlen, mask,
 def fwd_workload(wl, rows=None) -> np.ndarray:
     """Oracle O for a ``Workload`` (its bf16 inputs widened exactly)."""
     return fwd(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.q, wl.k, wl.v,
-               float(wl.alpha), wl.scaling_seqlen, wl.window_size, rows)
+               float(wl.alpha), wl.scaling_seqlen, wl.mask_spec, rows)
 
 
 def bwd_workload(wl, rows_q=None, rows_k=None):
@@ -194,9 +214,9 @@ def bwd_workload(wl, rows_q=None, rows_k=None):
     if wl.do is None:
         raise ValueError("workload has no upstream gradient")
     dq = bwd_dq(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, wl.q, wl.k, wl.v,
-                float(wl.alpha), wl.scaling_seqlen, wl.window_size, rows_q)
+                float(wl.alpha), wl.scaling_seqlen, wl.mask_spec, rows_q)
     dk, dv = bwd_dkdv(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, wl.q, wl.k, wl.v,
-                      float(wl.alpha), wl.scaling_seqlen, wl.window_size, rows_k)
+                      float(wl.alpha), wl.scaling_seqlen, wl.mask_spec, rows_k)
     return dq, dk, dv
 
 

@@ -15,7 +15,11 @@
  * "Tensor layout" table.  The mask M is the page's "Mask support" table: a
  * token window (left, right) in which -1 leaves a side unbounded, so (-1,-1) is
  * full attention, (-1,0) causal, and finite bounds give a local (sliding)
- * window.
+ * window; or the table's arbitrary mask: per packed query row r, endpoints
+ * F0, F1, ..., F_{N-1} (N odd) read from func[n * ld + r] make the visible keys
+ * [0, F0) u [F1, F2) u [F3, F4) u ..., each interval taken on its own (they may
+ * overlap or come in any order, and an interval whose end is not above its
+ * start is empty); keys outside the sequence stay invisible.
  *
  * Readings where the page is silent (each is listed in the design notes):
  *  - window_size follows the FlashAttention-2 convention, the one the cuDNN
@@ -28,6 +32,8 @@
  *    indices counted from the sequence's first query and first key, so causal
  *    (-1, 0) means j <= i.  All measured workloads have equal query and key
  *    lengths, where top-left and bottom-right agree;
+ *  - the arbitrary mask's endpoints are local key indices like j (the union
+ *    starts at key 0 of the sequence), indexed by the packed (global) query row;
  *  - L_scale is one global scalar for the whole call (the page calls it a
  *    runtime normalisation factor, not a per-sequence token count);
  *  - a query row with no visible key gets O = 0, a key row seen by no query
@@ -66,11 +72,27 @@ static int64_t owner(const int32_t* cu, int64_t B, int64_t r) {
     return -1;
 }
 
-/* Mask M_ij for local query index i and local key index j (both in range),
- * window (left, right), a negative bound meaning that side is unbounded. */
-static inline int visible(int64_t left, int64_t right, int64_t i, int64_t j) {
-    if (left >= 0 && j < i - left) return 0;
-    if (right >= 0 && j > i + right) return 0;
+/* The mask: a token window (left, right), a negative bound meaning that side
+ * is unbounded, or, when func is not NULL, the interval list of each query row
+ * (func_n endpoints, row r's n-th at func[n * func_ld + r]). */
+typedef struct {
+    int64_t left, right;
+    const int32_t* func;
+    int64_t func_n, func_ld;
+} mask_t;
+
+/* M_ij for packed query row r = local query index i of its sequence, and local
+ * key index j (0 <= j < L_k). */
+static inline int visible(const mask_t* m, int64_t r, int64_t i, int64_t j) {
+    if (m->func) {
+        const int32_t* f = m->func + r;
+        if (j < f[0]) return 1;
+        for (int64_t n = 1; n + 1 < m->func_n; n += 2)
+            if (f[n * m->func_ld] <= j && j < f[(n + 1) * m->func_ld]) return 1;
+        return 0;
+    }
+    if (m->left >= 0 && j < i - m->left) return 0;
+    if (m->right >= 0 && j > i + m->right) return 0;
     return 1;
 }
 
@@ -98,7 +120,9 @@ int oracle_num_threads(void) {
 int oracle_hstu_fwd(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t H, int64_t D,
                     const double* q, const double* k, const double* v,
                     double alpha, double ls, int64_t left, int64_t right,
+                    const int32_t* func, int64_t func_n, int64_t func_ld,
                     const int64_t* rows, int64_t nrows, double* out) {
+    const mask_t mk = {left, right, func, func_n, func_ld};
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2) reduction(| : bad)
     for (int64_t n = 0; n < nrows; ++n) {
@@ -112,7 +136,7 @@ int oracle_hstu_fwd(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t
             const int64_t k0 = cu_k[b], lk = (int64_t)cu_k[b + 1] - cu_k[b];
             const double* qi = q + thd(r, h, 0, H, D);
             for (int64_t j = 0; j < lk; ++j) {
-                if (!visible(left, right, i, j)) continue;
+                if (!visible(&mk, r, i, j)) continue;
                 const double s = alpha * dot(qi, k + thd(k0 + j, h, 0, H, D), D);
                 const double a = s * sigmoid(s) / ls;
                 const double* vj = v + thd(k0 + j, h, 0, H, D);
@@ -127,7 +151,9 @@ int oracle_hstu_fwd(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t
 int oracle_hstu_bwd_dq(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t H, int64_t D,
                        const double* dout, const double* q, const double* k, const double* v,
                        double alpha, double ls, int64_t left, int64_t right,
+                    const int32_t* func, int64_t func_n, int64_t func_ld,
                        const int64_t* rows, int64_t nrows, double* dq) {
+    const mask_t mk = {left, right, func, func_n, func_ld};
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2) reduction(| : bad)
     for (int64_t n = 0; n < nrows; ++n) {
@@ -142,7 +168,7 @@ int oracle_hstu_bwd_dq(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int6
             const double* qi = q + thd(r, h, 0, H, D);
             const double* doi = dout + thd(r, h, 0, H, D);
             for (int64_t j = 0; j < lk; ++j) {
-                if (!visible(left, right, i, j)) continue;
+                if (!visible(&mk, r, i, j)) continue;
                 const double* kj = k + thd(k0 + j, h, 0, H, D);
                 const double s = alpha * dot(qi, kj, D);
                 const double sg = sigmoid(s);
@@ -159,7 +185,9 @@ int oracle_hstu_bwd_dq(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int6
 int oracle_hstu_bwd_dkdv(int64_t B, const int32_t* cu_q, const int32_t* cu_k, int64_t H, int64_t D,
                          const double* dout, const double* q, const double* k, const double* v,
                          double alpha, double ls, int64_t left, int64_t right,
+                    const int32_t* func, int64_t func_n, int64_t func_ld,
                          const int64_t* rows, int64_t nrows, double* dk, double* dv) {
+    const mask_t mk = {left, right, func, func_n, func_ld};
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2) reduction(| : bad)
     for (int64_t n = 0; n < nrows; ++n) {
@@ -175,7 +203,7 @@ int oracle_hstu_bwd_dkdv(int64_t B, const int32_t* cu_q, const int32_t* cu_k, in
             const double* kj = k + thd(r, h, 0, H, D);
             const double* vj = v + thd(r, h, 0, H, D);
             for (int64_t i = 0; i < lq; ++i) {
-                if (!visible(left, right, i, j)) continue;
+                if (!visible(&mk, q0 + i, i, j)) continue;
                 const double* qi = q + thd(q0 + i, h, 0, H, D);
                 const double* doi = dout + thd(q0 + i, h, 0, H, D);
                 const double s = alpha * dot(qi, kj, D);
