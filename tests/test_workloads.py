@@ -21,6 +21,7 @@ EXPECTED_TOTALS = {
     "long_b4_h8_d128_causal": 43527,
     "zipf_b32_h4_d128_causal_fwdbwd": 23460,
     "long_b4_h8_d128_window1024": 43527,
+    "zipf_b32_h4_d128_target_fwdbwd": 23460,
 }
 
 
@@ -77,6 +78,9 @@ def test_value_scale():
 def test_masks_of_the_named_workloads():
     assert named_workload("tiny_b2_h1_d16_causal").window_size == (-1, 0)
     assert named_workload("uniform_b8_h2_d64_full").window_size == (-1, -1)
+    t = named_workload("zipf_b32_h4_d128_target_fwdbwd")
+    assert t.func.shape == (3, t.total_q) and t.mask_name == "func(N=3)"
+    np.testing.assert_array_equal(t.q, named_workload("zipf_b32_h4_d128_causal").q)
     w = make_workload("w", 7, [5, 9], 1, 16, False, window=(3, 1))
     assert w.window_size == (3, 1) and w.mask_name == "window(3,1)"
     import pytest
