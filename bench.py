@@ -56,6 +56,28 @@ def visible_pairs(lengths_q, lengths_k, window) -> int:
     return total
 
 
+def func_visible_pairs(func, lengths_q, lengths_k) -> int:
+    """Count of (query, key) pairs an interval-list mask keeps: packed row r sees the
+    local keys [0, F0) u [F1, F2) u ... (F_n = func[n, r]) inside [0, L_k)."""
+    total, r0 = 0, 0
+    for lq, lk in zip(np.asarray(lengths_q, dtype=np.int64), np.asarray(lengths_k, dtype=np.int64)):
+        j = np.arange(lk, dtype=np.int64)[None, :]
+        for c0 in range(0, int(lq), 1024):
+            f = func[:, r0 + c0:r0 + min(int(lq), c0 + 1024)].astype(np.int64)
+            seen = j < f[0][:, None]
+            for n in range(1, f.shape[0] - 1, 2):
+                seen |= (f[n][:, None] <= j) & (j < f[n + 1][:, None])
+            total += int(seen.sum())
+        r0 += int(lq)
+    return total
+
+
+def workload_pairs(wl) -> int:
+    if wl.func is not None:
+        return func_visible_pairs(wl.func, wl.lengths_q, wl.lengths_k)
+    return visible_pairs(wl.lengths_q, wl.lengths_k, wl.window_size)
+
+
 def kernel_source_digest() -> str:
     """Digest of the kernel sources and of the build script that sets their compile flags."""
     pkg = os.path.join(ROOT, "generative_recommender_attention_amd")
@@ -182,7 +204,11 @@ def cpu_baseline(wl, max_pairs: int):
     order = np.argsort(wl.lengths_q, kind="stable")
     chosen, pairs = [], 0
     for b in order:
-        p = visible_pairs([wl.lengths_q[b]], [wl.lengths_k[b]], wl.window_size)
+        if wl.func is not None:
+            r0 = int(wl.cu_seqlens_q[b])
+            p = func_visible_pairs(wl.func[:, r0:r0 + int(wl.lengths_q[b])], [wl.lengths_q[b]], [wl.lengths_k[b]])
+        else:
+            p = visible_pairs([wl.lengths_q[b]], [wl.lengths_k[b]], wl.window_size)
         if max_pairs and pairs + p > max_pairs and chosen:
             continue
         chosen.append(int(b))
@@ -204,7 +230,7 @@ def cpu_baseline(wl, max_pairs: int):
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": (f"fp64 oracle fwd+bwd on {len(chosen)} of {wl.batch} sequences (lengths {lens[0]}..{lens[-1]}, "
-                   f"{pairs} visible pairs x {wl.num_heads} heads = {pairs / visible_pairs(wl.lengths_q, wl.lengths_k, wl.window_size):.1%} "
+                   f"{pairs} visible pairs x {wl.num_heads} heads = {pairs / workload_pairs(wl):.1%} "
                    f"of the workload's pairs), {dt:.1f} s"),
         "seconds": dt,
         "cpu": platform.processor() or platform.machine(),
@@ -273,7 +299,8 @@ def main(argv=None) -> int:
     o = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     kw = dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, alpha=float(wl.alpha),
-              scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window)
+              scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window,
+              func=torch.from_numpy(wl.func).to(dev) if wl.func is not None else None)
     stream = torch.cuda.current_stream(dev)
     kernels = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if has_bwd else [])
 
@@ -310,7 +337,7 @@ def main(argv=None) -> int:
         per_kernel_ms[name] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
     ms_per_step = elapsed * 1e3 / args.steps
 
-    pairs = visible_pairs(wl.lengths_q, wl.lengths_k, wl.window_size)
+    pairs = workload_pairs(wl)
     unit_pd = wl.head_dim * wl.num_heads * pairs
     useful = USEFUL_PER_PAIR_D["fwd"] * unit_pd + (USEFUL_PER_PAIR_D["bwd"] * unit_pd if has_bwd else 0)
     value = useful / (ms_per_step * 1e-3) / 1e12

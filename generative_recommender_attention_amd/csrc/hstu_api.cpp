@@ -68,6 +68,7 @@ hstu_status_t check_operand(const hstu_args_t& a, Operand& t) {
 // and causal kernels, which are the same masks.
 hstu::MaskKind mask_kind(const hstu_args_t& a) {
     if (a.mask == HSTU_MASK_CAUSAL) return hstu::MaskKind::Causal;
+    if (a.mask == HSTU_MASK_FUNC) return hstu::MaskKind::Func;
     if (a.mask != HSTU_MASK_WINDOW) return hstu::MaskKind::None;
     if (a.window_left < 0 && a.window_right < 0) return hstu::MaskKind::None;
     if (a.window_left < 0 && a.window_right == 0) return hstu::MaskKind::Causal;
@@ -79,12 +80,20 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
     if (a == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args is null");
     if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
         return fail(HSTU_ERR_UNSUPPORTED, "head_dim %d is not one of 16, 32, 64, 128", a->head_dim);
-    if (a->mask != HSTU_MASK_NONE && a->mask != HSTU_MASK_CAUSAL && a->mask != HSTU_MASK_WINDOW)
-        return fail(HSTU_ERR_UNSUPPORTED, "mask %d is not HSTU_MASK_NONE, HSTU_MASK_CAUSAL or HSTU_MASK_WINDOW",
-                    a->mask);
+    if (a->mask != HSTU_MASK_NONE && a->mask != HSTU_MASK_CAUSAL && a->mask != HSTU_MASK_WINDOW &&
+        a->mask != HSTU_MASK_FUNC)
+        return fail(HSTU_ERR_UNSUPPORTED, "mask %d is not one of HSTU_MASK_NONE, _CAUSAL, _WINDOW, _FUNC", a->mask);
     if (a->mask == HSTU_MASK_WINDOW && (a->window_left < -1 || a->window_right < -1))
         return fail(HSTU_ERR_INVALID_ARGUMENT, "window (%d, %d): bounds must be >= -1", a->window_left,
                     a->window_right);
+    if (a->mask == HSTU_MASK_FUNC) {
+        if (a->func_n < 1 || a->func_n % 2 != 1)
+            return fail(HSTU_ERR_INVALID_ARGUMENT, "func_n %d must be odd and positive", a->func_n);
+        if (a->total_q > 0 && a->func_ld < a->total_q)
+            return fail(HSTU_ERR_INVALID_ARGUMENT, "func_ld %d < total_q %d", a->func_ld, a->total_q);
+        if (a->total_q > 0 && (a->func == nullptr || reinterpret_cast<uintptr_t>(a->func) % 4 != 0))
+            return fail(HSTU_ERR_INVALID_ARGUMENT, "func is null or not 4-byte aligned");
+    }
     if (a->batch < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "batch %d < 1", a->batch);
     if (a->num_heads < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_heads %d < 1", a->num_heads);
     if (a->total_q < 0 || a->total_k < 0)
@@ -124,6 +133,11 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
         auto side = [&](int32_t w) { return w < 0 || w > a->max_seqlen_k ? a->max_seqlen_k : w; };
         p.win_left = side(a->window_left);
         p.win_right = side(a->window_right);
+    }
+    if (mask_kind(*a) == hstu::MaskKind::Func) {
+        p.func = a->func;
+        p.func_n = a->func_n;
+        p.func_ld = a->func_ld;
     }
     return HSTU_OK;
 }

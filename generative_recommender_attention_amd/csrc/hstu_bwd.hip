@@ -63,11 +63,17 @@ __device__ __forceinline__ float dsilu_from(float a, float sig) {
 
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
 
-// dS^T operands of one 32-key block from its score and dA accumulators.  Keys
-// outside this lane's interval [lo, lo + span) are zeroed when the block leaves
-// [wlo, wlim), the keys every row of the wave sees (WIN: a window mask, where
-// the block can also start below it).
-template <bool WIN>
+// How the dq kernel masks a 32-key block: kNoMask never; kInterval (full or
+// causal) when the block reaches past wlim, the end of the keys every row of the
+// wave sees, against this lane's keys [0, span); kBand (token window) when the
+// block leaves [wlo, wlim), against [lo, lo + span); kBits always, against the
+// block's bit word `lo` (pre-shifted by 4 g: bit 8 (r / 4) + r % 4 is the key of
+// accumulator register r).
+enum DqMask : int { kNoMask = 0, kInterval = 1, kBand = 2, kBits = 3 };
+
+// dS^T operands of one 32-key block from its score and dA accumulators, masked
+// as MT says.
+template <int MT>
 __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc, int key0, int lo, int span, int wlo,
                                          int wlim, int g, uint4& d0, uint4& d1) {
     float dv[16];
@@ -76,12 +82,17 @@ __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc,
         const float sg = sig_pre(sacc[r]);
         dv[r] = dacc[r] * dsilu_from(sacc[r] * sg, sg);
     }
-    if ((WIN && key0 < wlo) || key0 + 32 > wlim) {
-        keep_branch();
+    if constexpr (MT == kBits) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + acc_row(r, g);
-            dv[r] = (WIN ? (unsigned)(key - lo) < (unsigned)span : key < span) ? dv[r] : 0.0f;
+        for (int r = 0; r < 16; ++r) dv[r] = ((unsigned)lo >> (8 * (r >> 2) + (r & 3))) & 1u ? dv[r] : 0.0f;
+    } else if constexpr (MT != kNoMask) {
+        if ((MT == kBand && key0 < wlo) || key0 + 32 > wlim) {
+            keep_branch();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + acc_row(r, g);
+                dv[r] = (MT == kBand ? (unsigned)(key - lo) < (unsigned)span : key < span) ? dv[r] : 0.0f;
+            }
         }
     }
     d0 = pack_operand(dv);
@@ -92,11 +103,11 @@ __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc,
 // (K) and `vt` (V).  Products run S^T and dA^T of both 32-key blocks, then dQ^T
 // of the first block (while dS^T of the second is formed), then of the second;
 // every LDS read is issued PF products ahead of its MFMA.
-template <int D, bool WIN>
+template <int D, int MT>
 __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&qf)[D / 16],
                                            const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
                                            const uint32_t (&koff)[D / 16], const uint2 (&toff)[(D < 32 ? 32 : D) / 32],
-                                           int n0, int lo, int span, int wlo, int wlim, int g) {
+                                           int n0, int lo, int span, int wlo, int wlim, int lo1, int g) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // S and dA products: block kb, step kk, operand (K, V)
@@ -131,7 +142,7 @@ __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         uint4 d0, d1;
-        dq_ds_op<WIN>(sa[kb], da[kb], n0 + 32 * kb, lo, span, wlo, wlim, g, d0, d1);
+        dq_ds_op<MT>(sa[kb], da[kb], n0 + 32 * kb, kb ? lo1 : lo, span, wlo, wlim, g, d0, d1);
 #pragma unroll
         for (int j = 0; j < 2 * NDB; ++j) {
             const int i = kb * 2 * NDB + j;
@@ -145,10 +156,12 @@ template <int D, MaskKind MK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
+    constexpr bool FUNC = MK == MaskKind::Func;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
     // [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile t lives in slot (t - t0) % 2
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
+    __shared__ int kv_red[FUNC ? 8 : 1];  // func: per-wave key range of the block's rows
     const uint32_t lds0 = lds_addr(smem);
     constexpr uint32_t K0 = 0, K1 = kTileBytes, V0 = 2 * kTileBytes, V1 = 3 * kTileBytes;
 
@@ -183,12 +196,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
         wlim = min(sb.lk, row0 + R + 1);
         any_lo = max(0, row0 - L);
         any_hi = min(sb.lk, wlast + R + 1);
+    } else if constexpr (FUNC) {
+        // keys between the smallest and the largest visible key of any row of the block
+        int rlo = 0x7fffffff, rhi = 0;
+        if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
+        rlo = wave_min(rlo);
+        rhi = wave_max(rhi);
+        if (lane == 0) {
+            kv_red[2 * wave] = rlo;
+            kv_red[2 * wave + 1] = rhi;
+        }
+        __syncthreads();
+        kv_begin = min(min(kv_red[0], kv_red[2]), min(kv_red[4], kv_red[6]));
+        kv_end = max(max(kv_red[1], kv_red[3]), max(kv_red[5], kv_red[7]));
+        span = 0;
+        wlim = 0;
     } else {
         if (CAUSAL) kv_end = min(sb.lk, m0 + BM);
         span = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
         wlim = CAUSAL ? min(kv_end, row0 + 1) : kv_end;
     }
-    const int t0 = kv_begin / BN;
+    const int t0 = kv_end > kv_begin ? kv_begin / BN : 0;
     const int t1 = kv_end > kv_begin ? (kv_end + BN - 1) / BN : t0;
 
     uint4 qf[KSTEPS], dof[KSTEPS];
@@ -241,9 +269,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
                 kdma.issue(lds0 + kn, kbase, p.k.tok, n0 + BN, kv_end);
                 vdma.issue(lds0 + vn, vbase, p.v.tok, n0 + BN, kv_end);
             }
-            // waves that see no key of the tile skip it
-            const bool run = WINDOW ? n0 + BN > any_lo && n0 < any_hi : !(CAUSAL && n0 > row0 + 31);
-            if (wave_live && run) dq_tile<D, WINDOW>(kc, vc, qf, dof, acc, koff, toff, n0, lo, span, wlo, wlim, g);
+            if constexpr (FUNC) {
+                // this lane's visible keys of the tile; the live rows of the wave decide
+                // between skipping the tile, the unmasked code and the bit-masked code
+                if (wave_live) {
+                    const bool live = my_row < sb.lq;
+                    const uint64_t bits =
+                        func_bits64(p.func, p.func_ld, p.func_n, sb.q0 + min(my_row, sb.lq - 1), n0, sb.lk);
+                    const uint64_t seen = __ballot(live && bits != 0);
+                    const uint64_t cut = __ballot(live && bits != ~0ull);
+                    const uint64_t sh = bits >> (4 * g);
+                    if (cut == 0)
+                        dq_tile<D, kNoMask>(kc, vc, qf, dof, acc, koff, toff, n0, 0, 0, 0, 0, 0, g);
+                    else if (seen != 0)
+                        dq_tile<D, kBits>(kc, vc, qf, dof, acc, koff, toff, n0, (int)(uint32_t)sh, 0, 0, 0,
+                                          (int)(uint32_t)(sh >> 32), g);
+                }
+            } else {
+                // waves that see no key of the tile skip it
+                const bool run = WINDOW ? n0 + BN > any_lo && n0 < any_hi : !(CAUSAL && n0 > row0 + 31);
+                if (wave_live && run)
+                    dq_tile<D, WINDOW ? kBand : kInterval>(kc, vc, qf, dof, acc, koff, toff, n0, lo, span, wlo, wlim,
+                                                           lo, g);
+            }
             wait_global_loads();
             __syncthreads();
         };
@@ -274,13 +322,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
 
 // One 32-row block for one wave: S = Q K^T and dA = dO V^T (A operands: Q, dO
 // rows of the block; B operands: the wave's K, V rows), then dV^T += dO^T A' and
-// dK^T += Q^T dS over the block's two contraction steps.
-template <int D>
+// dK^T += Q^T dS over the block's two contraction steps.  MT = kInterval: when
+// `mask`, rows outside this lane's [lo, hi) are zeroed; kBits: row 8 k + 4 g + j
+// of the block (accumulator register 4 k + j) is tested against bit l32 of the
+// LDS word at mw + 32 k + 4 j; kNoMask: nothing is zeroed.
+template <int D, int MT>
 __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t drow, uint32_t krow, uint32_t vrow, uint32_t qtr,
                                             uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
                                             const uint2 (&toff)[(D < 32 ? 32 : D) / 32], int row0, int lo, int hi,
-                                            int g) {
+                                            int g, uint32_t mw) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // reads for S and dA: step kk, (Q, K, dO, V)
@@ -317,14 +368,29 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
         av[r] = y * sg;
         dv[r] = da[r] * dsilu_from(av[r], sg);
     }
-    if (mask) {
-        keep_branch();
+    if constexpr (MT == kBits) {
+        const int l32 = threadIdx.x & 31;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = row0 + acc_row(r, g);
-            const bool ok = row >= lo && row < hi;
-            av[r] = ok ? av[r] : 0.0f;
-            dv[r] = ok ? dv[r] : 0.0f;
+        for (int k = 0; k < 4; ++k) {
+            const uint4 w = ds_read16(mw + 32 * k);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = (ws[j] >> l32) & 1u;
+                av[4 * k + j] = ok ? av[4 * k + j] : 0.0f;
+                dv[4 * k + j] = ok ? dv[4 * k + j] : 0.0f;
+            }
+        }
+    } else if constexpr (MT == kInterval) {
+        if (mask) {
+            keep_branch();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + acc_row(r, g);
+                const bool ok = row >= lo && row < hi;
+                av[r] = ok ? av[r] : 0.0f;
+                dv[r] = ok ? dv[r] : 0.0f;
+            }
         }
     }
     const uint4 a[2] = {pack_operand(av), pack_operand(av + 8)};
@@ -342,10 +408,15 @@ template <int D, MaskKind MK>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
+    constexpr bool FUNC = MK == MaskKind::Func;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
     // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1 | K rows of the block | V rows of the block]
     __shared__ __attribute__((aligned(16))) uint16_t smem[8 * kTileElems];
+    // func: visibility words of a query tile, two slots of [32-key word w][64 rows]
+    // (bit k of word w, row r: key n0 + 32 w + k visible to row r of the tile)
+    __shared__ __attribute__((aligned(16))) uint32_t fmask[FUNC ? 2 * 256 : 4];
+    __shared__ int q_red[FUNC ? 16 : 1];
     const uint32_t lds0 = lds_addr(smem);
     constexpr uint32_t Q0 = 0, Q1 = kTileBytes, D0 = 2 * kTileBytes, D1 = 3 * kTileBytes;
     constexpr uint32_t KB = 4 * kTileBytes, VB = 6 * kTileBytes;
@@ -412,8 +483,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         q_begin = n0;
         lo = my_key;
         wlo = key0 + 31;  // largest lo in the wave
+    } else if constexpr (FUNC) {
+        // the first and last rows of the sequence that see a key of the block
+        const int k1 = min(n0 + BNK, sb.lk);
+        int qlo = 0x7fffffff, qhi = -1;
+        for (int i = tid; i < sb.lq; i += 512)
+            if (func_row_meets(p.func, p.func_ld, p.func_n, sb.q0 + i, n0, k1)) {
+                qlo = min(qlo, i);
+                qhi = max(qhi, i);
+            }
+        qlo = wave_min(qlo);
+        qhi = wave_max(qhi);
+        if (lane == 0) {
+            q_red[2 * wave] = qlo;
+            q_red[2 * wave + 1] = qhi;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            qlo = min(qlo, q_red[2 * w]);
+            qhi = max(qhi, q_red[2 * w + 1]);
+        }
+        q_begin = qhi >= qlo ? qlo : 0;
+        q_end = qhi >= qlo ? qhi + 1 : 0;
     }
     const int ntiles = q_end > q_begin ? (q_end - q_begin + BMQ - 1) / BMQ : 0;
+    // func: the words of the tile at rows qt0.. into slot `slot` (threads 0-255, one word each)
+    auto build_words = [&](int slot, int qt0) {
+        if constexpr (FUNC) {
+            if (tid < 256) {
+                const int row = tid & 63, w = tid >> 6;
+                const int i = qt0 + row;
+                fmask[slot * 256 + w * 64 + row] =
+                    i < sb.lq ? func_bits32(p.func, p.func_ld, p.func_n, sb.q0 + i, n0 + 32 * w, sb.lk) : 0u;
+            }
+        }
+    };
     const uint32_t krow = KB + 8192u * kw, vrow = VB + 8192u * kw;
 
     if (ntiles > 0) {
@@ -433,20 +538,44 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
             }
         }
         dma.issue(lds0 + (qgrp ? Q0 : D0), sbase, stok, q_begin, sb.lq);
+        build_words(0, q_begin);
         wait_global_loads();
         __syncthreads();
 
         auto step = [&](uint32_t qc, uint32_t dc, uint32_t qn, uint32_t dn, int t) {
             const int qt0 = q_begin + t * BMQ;
-            if (t + 1 < ntiles) dma.issue(lds0 + (qgrp ? qn : dn), sbase, stok, qt0 + BMQ, sb.lq);
+            if (t + 1 < ntiles) {
+                dma.issue(lds0 + (qgrp ? qn : dn), sbase, stok, qt0 + BMQ, sb.lq);
+                build_words((t + 1) & 1, qt0 + BMQ);  // that slot was last read before the previous barrier
+            }
             const int row0 = qt0 + 32 * qh;
-            // waves whose keys no row of the block sees, or that lie past the sequence, skip it
-            const bool run = WINDOW ? row0 + 32 > any_lo && row0 < any_hi : !(CAUSAL && row0 + 31 < key0);
-            if (wave_live && run && row0 < sb.lq) {
-                const uint32_t qr = qc + 8192u * qh, dr = dc + 8192u * qh;
-                // rows outside those that see every key of the wave, or past the sequence, need the mask
-                dkdv_block<D>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff,
-                              row0, lo, hi, g);
+            const uint32_t qr = qc + 8192u * qh, dr = dc + 8192u * qh;
+            if constexpr (FUNC) {
+                // the live rows of the block and the wave's live keys decide between
+                // skipping it, the unmasked code and the bit-masked code
+                if (wave_live && row0 < sb.lq) {
+                    const uint32_t wbase = (uint32_t)((t & 1) * 256 + kw * 64 + 32 * qh);
+                    const uint32_t word = fmask[wbase + l32];
+                    const bool live = row0 + l32 < sb.lq;
+                    const uint32_t valid = sb.lk - key0 >= 32 ? ~0u : (1u << (sb.lk - key0)) - 1u;
+                    const uint64_t seen = __ballot(live && word != 0);
+                    const uint64_t cut = __ballot(live && word != valid);
+                    // rows past the sequence (copies of its last row) must be masked out too
+                    if (cut == 0 && row0 + 32 <= sb.lq)
+                        dkdv_block<D, kNoMask>(false, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff, row0, 0, 0,
+                                               g, 0);
+                    else if (seen != 0)
+                        dkdv_block<D, kBits>(true, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff, row0, 0, 0, g,
+                                             lds_addr(fmask) + 4u * (wbase + 4 * g));
+                }
+            } else {
+                // waves whose keys no row of the block sees, or that lie past the sequence, skip it
+                const bool run = WINDOW ? row0 + 32 > any_lo && row0 < any_hi : !(CAUSAL && row0 + 31 < key0);
+                if (wave_live && run && row0 < sb.lq) {
+                    // rows outside those that see every key of the wave, or past the sequence, need the mask
+                    dkdv_block<D, kInterval>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
+                                             roff, toff, row0, lo, hi, g, 0);
+                }
             }
             wait_global_loads();
             __syncthreads();
@@ -529,6 +658,8 @@ hipError_t launch_mask(const AttnParams& p, MaskKind mask, hipStream_t stream) {
             return DKDV ? launch_dkdv<D, MaskKind::Causal>(p, stream) : launch_dq<D, MaskKind::Causal>(p, stream);
         case MaskKind::Window:
             return DKDV ? launch_dkdv<D, MaskKind::Window>(p, stream) : launch_dq<D, MaskKind::Window>(p, stream);
+        case MaskKind::Func:
+            return DKDV ? launch_dkdv<D, MaskKind::Func>(p, stream) : launch_dq<D, MaskKind::Func>(p, stream);
     }
     return hipErrorInvalidValue;
 }

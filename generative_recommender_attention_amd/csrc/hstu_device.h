@@ -311,6 +311,76 @@ __device__ __forceinline__ float silu_pre(float y) {
 // (always executed) version would cost two VALU instructions per score.
 __device__ __forceinline__ void keep_branch() { __asm__ volatile(""); }
 
+// ---- interval-list masks -------------------------------------------------------
+// Bits of the W keys n0 .. n0 + W - 1 (W = 32 or 64; bit k is key n0 + k) that the
+// interval [a, b) covers.  Any int32 endpoints are safe: differences are taken
+// only where they cannot overflow.
+__device__ __forceinline__ uint64_t span_bits64(int a, int b, int n0) {
+    const int lo = a <= n0 ? 0 : min(a - n0, 64);
+    const int hi = b <= n0 ? 0 : min(b - n0, 64);
+    if (hi <= lo) return 0;
+    const uint64_t below_hi = hi >= 64 ? ~0ull : (1ull << hi) - 1;
+    return below_hi & ~((1ull << lo) - 1);
+}
+__device__ __forceinline__ uint32_t span_bits32(int a, int b, int n0) {
+    const int lo = a <= n0 ? 0 : min(a - n0, 32);
+    const int hi = b <= n0 ? 0 : min(b - n0, 32);
+    if (hi <= lo) return 0;
+    const uint32_t below_hi = hi >= 32 ? ~0u : (1u << hi) - 1;
+    return below_hi & ~((1u << lo) - 1);
+}
+
+// Visible keys of packed query row `row` among local keys n0 .. n0 + 63 of a
+// sequence with lk keys, for endpoints f[n * ld + row], n < N (N odd):
+// [0, F0) u [F1, F2) u ... , cut to [0, lk).
+__device__ __forceinline__ uint64_t func_bits64(const int32_t* f, int ld, int N, int row, int n0, int lk) {
+    uint64_t m = span_bits64(0, f[row], n0);
+    for (int n = 1; n + 1 < N; n += 2)
+        m |= span_bits64(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
+    return m & span_bits64(0, lk, n0);
+}
+__device__ __forceinline__ uint32_t func_bits32(const int32_t* f, int ld, int N, int row, int n0, int lk) {
+    uint32_t m = span_bits32(0, f[row], n0);
+    for (int n = 1; n + 1 < N; n += 2)
+        m |= span_bits32(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
+    return m & span_bits32(0, lk, n0);
+}
+
+// Smallest and one past the largest visible key of row `row` (lo >= hi: none).
+__device__ __forceinline__ void func_key_range(const int32_t* f, int ld, int N, int row, int lk, int& lo, int& hi) {
+    lo = 0x7fffffff;
+    hi = 0;
+    auto add = [&](int a, int b) {
+        a = max(a, 0);
+        b = min(b, lk);
+        if (b > a) {
+            lo = min(lo, a);
+            hi = max(hi, b);
+        }
+    };
+    add(0, f[row]);
+    for (int n = 1; n + 1 < N; n += 2) add(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row]);
+}
+
+// Whether row `row` sees any key of [k0, k1) (0 <= k0, k1 <= lk).
+__device__ __forceinline__ bool func_row_meets(const int32_t* f, int ld, int N, int row, int k0, int k1) {
+    bool hit = min(f[row], k1) > k0;
+    for (int n = 1; n + 1 < N; n += 2)
+        hit |= min(f[(int64_t)(n + 1) * ld + row], k1) > max(f[(int64_t)n * ld + row], k0);
+    return hit;
+}
+
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
 // Row of accumulator register r (0..15) inside a 32-row block, for lane half g.
 __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 

@@ -42,21 +42,32 @@ constexpr int BM = kFwdBlockM;                   // 128 query rows per workgroup
 constexpr int BN = kTileRows;                    // 64 keys per tile
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
 
+// How a tile's scores are masked: not at all; against this lane's key interval
+// [lo, lo + span) (one unsigned compare tests both ends); or against a bit word
+// per 32-key block (bit 8 (r / 4) + r % 4 of the word, pre-shifted by 4 g, is the
+// key of accumulator register r).
+enum TileMask : int { kNoMask = 0, kInterval = 1, kBits = 2 };
+
 // bf16 P^T operand from accumulator registers r0..r0+7 of a 32-key block whose
 // first key is key0.  The scores arrive as y = c x with c = -alpha log2(e)
 // folded into Q (x = q.k), so y sig(alpha x) = y / (1 + 2^y) costs one exp, one
 // add, one rcp and one multiply; the factor 1/c is folded into the output
-// scale.  With MASKED, keys outside this lane's interval [lo, lo + span) are
-// zeroed (one unsigned compare tests both ends).
-template <bool MASKED>
-__device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int lo, int span, int g) {
+// scale.  kInterval: (a, b) = (lo, span); kBits: a = the block's bit word.
+template <int MT>
+__device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int a, int b, int g) {
     float pv[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) pv[r] = silu_pre(s[r0 + r]);
-    if constexpr (MASKED) {
+    if constexpr (MT == kInterval) {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
-            pv[r] = (unsigned)(key0 + acc_row(r0 + r, g) - lo) < (unsigned)span ? pv[r] : 0.0f;
+            pv[r] = (unsigned)(key0 + acc_row(r0 + r, g) - a) < (unsigned)b ? pv[r] : 0.0f;
+    } else if constexpr (MT == kBits) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int bit = 8 * ((r0 + r) >> 2) + ((r0 + r) & 3);
+            pv[r] = ((unsigned)a >> bit) & 1u ? pv[r] : 0.0f;
+        }
     }
     return pack_operand(pv);
 }
@@ -65,11 +76,11 @@ __device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0,
 // (s0), then for the second 32 (s1); P^T of s0 is computed while s1's products
 // run, the first half of O^T += V^T P^T while P^T of s1 is computed.  Reads are
 // issued in product order, PF ahead of the MFMA that uses them.
-template <int D, bool MASKED, uint32_t kt, uint32_t vt>
+template <int D, int MT, uint32_t kt, uint32_t vt>
 __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
                                          f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&koff)[D / 16],
-                                         const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, int lo, int span,
-                                         int g) {
+                                         const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, int a0, int b0,
+                                         int a1, int b1, int g) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;  // 32-column blocks of O^T
     constexpr int NS = D / 16;                   // contraction steps per S^T block
     constexpr int NK = 2 * NS;                   // K reads: block-major, step-minor
@@ -93,15 +104,15 @@ __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
         else s1 = mfma32x32x16(rd[j], qf[j - NS], s1);
         read(j + PF);
     }
-    const uint4 p0 = silu_operand<MASKED>(s0, 0, n0, lo, span, g);
-    const uint4 p1 = silu_operand<MASKED>(s0, 8, n0, lo, span, g);
+    const uint4 p0 = silu_operand<MT>(s0, 0, n0, a0, b0, g);
+    const uint4 p1 = silu_operand<MT>(s0, 8, n0, a0, b0, g);
 #pragma unroll
     for (int i = 0; i < 2 * NDB; ++i) {
         oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < NDB ? p0 : p1, oacc[i % NDB]);
         read(NK + i + PF);
     }
-    const uint4 p2 = silu_operand<MASKED>(s1, 0, n0 + 32, lo, span, g);
-    const uint4 p3 = silu_operand<MASKED>(s1, 8, n0 + 32, lo, span, g);
+    const uint4 p2 = silu_operand<MT>(s1, 0, n0 + 32, a1, b1, g);
+    const uint4 p3 = silu_operand<MT>(s1, 8, n0 + 32, a1, b1, g);
 #pragma unroll
     for (int i = 2 * NDB; i < NV; ++i) {
         oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < 3 * NDB ? p2 : p3, oacc[i % NDB]);
@@ -113,11 +124,13 @@ template <int D, MaskKind MK>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
+    constexpr bool FUNC = MK == MaskKind::Func;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int NDB = DM / 32;
     constexpr int KSTEPS = D / 16;
     // [K slot 0 | K slot 1 | V slot 0 | V slot 1]
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
+    __shared__ int kv_red[FUNC ? 8 : 1];  // func: per-wave key range of the block's rows
     const uint32_t lds0 = lds_addr(smem);
 
     const int tid = threadIdx.x;
@@ -153,11 +166,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
         full_hi = min(sb.lk, row0 + R + 1);
         any_lo = max(0, row0 - L);
         any_hi = min(sb.lk, wlast + R + 1);
+    } else if constexpr (FUNC) {
+        // keys between the smallest and the largest visible key of any row of the block
+        int rlo = 0x7fffffff, rhi = 0;
+        if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
+        rlo = wave_min(rlo);
+        rhi = wave_max(rhi);
+        if (lane == 0) {
+            kv_red[2 * wave] = rlo;
+            kv_red[2 * wave + 1] = rhi;
+        }
+        __syncthreads();
+        kv_begin = min(min(kv_red[0], kv_red[2]), min(kv_red[4], kv_red[6]));
+        kv_end = max(max(kv_red[1], kv_red[3]), max(kv_red[5], kv_red[7]));
+        span = 0;
     } else {
         if (CAUSAL) kv_end = min(sb.lk, m0 + BM);
         span = CAUSAL ? min(kv_end, my_row + 1) : kv_end;
     }
-    const int t0 = kv_begin / BN;
+    const int t0 = kv_end > kv_begin ? kv_begin / BN : 0;
     const int ntiles = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
 
     uint4 qf[KSTEPS];
@@ -208,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
         // crossing a diagonal is tile 2m of 2m + 2; without a causal mask only the
         // last tile can pass the sequence end.  Slots alternate at compile time so
         // that every LDS offset is an immediate.
-        const int nplain = WINDOW ? ntiles : ntiles - min(ntiles, 2);
+        const int nplain = WINDOW || FUNC ? ntiles : ntiles - min(ntiles, 2);
         auto step = [&](int s, auto slot, auto masked) {
             constexpr uint32_t cur = decltype(slot)::value * kTileBytes, nxt = kTileBytes - cur;
             if (s + 1 < ntiles) {  // the other slots were last read before the previous barrier
@@ -219,14 +246,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
             if constexpr (WINDOW) {
                 if (wave_live && n0 + BN > any_lo && n0 < any_hi) {
                     if (n0 >= full_lo && n0 + BN <= full_hi)
-                        fwd_tile<D, false, cur, cur>(qf, oacc, koff, voff, n0, lo, span, g);
+                        fwd_tile<D, kNoMask, cur, cur>(qf, oacc, koff, voff, n0, 0, 0, 0, 0, g);
                     else
-                        fwd_tile<D, true, cur, cur>(qf, oacc, koff, voff, n0, lo, span, g);
+                        fwd_tile<D, kInterval, cur, cur>(qf, oacc, koff, voff, n0, lo, span, lo, span, g);
+                }
+            } else if constexpr (FUNC) {
+                // this lane's visible keys of the tile; the live rows of the wave decide
+                // between skipping the tile, the unmasked code and the bit-masked code
+                if (wave_live) {
+                    const bool live = my_row < sb.lq;
+                    const uint64_t bits =
+                        func_bits64(p.func, p.func_ld, p.func_n, sb.q0 + min(my_row, sb.lq - 1), n0, sb.lk);
+                    const uint64_t seen = __ballot(live && bits != 0);
+                    const uint64_t cut = __ballot(live && bits != ~0ull);
+                    if (cut == 0) {
+                        fwd_tile<D, kNoMask, cur, cur>(qf, oacc, koff, voff, n0, 0, 0, 0, 0, g);
+                    } else if (seen != 0) {
+                        const uint64_t sh = bits >> (4 * g);
+                        fwd_tile<D, kBits, cur, cur>(qf, oacc, koff, voff, n0, (int)(uint32_t)sh, 0,
+                                                     (int)(uint32_t)(sh >> 32), 0, g);
+                    }
                 }
             } else {
                 // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
                 if (wave_live && !(CAUSAL && n0 > row0 + 31))
-                    fwd_tile<D, decltype(masked)::value, cur, cur>(qf, oacc, koff, voff, n0, lo, span, g);
+                    fwd_tile<D, decltype(masked)::value ? kInterval : kNoMask, cur, cur>(qf, oacc, koff, voff, n0, lo,
+                                                                                         span, lo, span, g);
             }
             wait_global_loads();
             __syncthreads();
@@ -275,6 +320,7 @@ hipError_t launch_d(const AttnParams& p, MaskKind mask, hipStream_t stream) {
         case MaskKind::None: return launch<D, MaskKind::None>(p, stream);
         case MaskKind::Causal: return launch<D, MaskKind::Causal>(p, stream);
         case MaskKind::Window: return launch<D, MaskKind::Window>(p, stream);
+        case MaskKind::Func: return launch<D, MaskKind::Func>(p, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -12,8 +12,10 @@ namespace hstu {
 // Mask the kernels are built for.  A token window (left, right) admits key j for
 // query i (local indices) iff i - left <= j <= i + right; the host resolves the
 // windows that equal full attention or causal to those kinds, and a window side
-// with no bound to a bound of max_seqlen_k, which cuts nothing.
-enum class MaskKind : int { None = 0, Causal = 1, Window = 2 };
+// with no bound to a bound of max_seqlen_k, which cuts nothing.  Func: each
+// packed query row r lists endpoints F0..F_{N-1} (func[n * func_ld + r]) and
+// sees the local keys [0, F0) u [F1, F2) u ...
+enum class MaskKind : int { None = 0, Causal = 1, Window = 2, Func = 3 };
 
 struct AttnParams {
     const int32_t* cu_q;   // (B + 1) cumulative query lengths, device
@@ -29,6 +31,9 @@ struct AttnParams {
                            // scores pre-multiplied by c = exp_c (0 when alpha = 0)
     int32_t win_left;      // MaskKind::Window: 0 <= left, right <= max_seqlen_k <= 2^29
     int32_t win_right;
+    const int32_t* func;   // MaskKind::Func: endpoints, device, func_n rows of func_ld >= T_q
+    int32_t func_n;        // odd, >= 1
+    int32_t func_ld;
     TensorRef q, k, v, dout;
     TensorOut o, dq, dk, dv;
 };

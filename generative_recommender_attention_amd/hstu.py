@@ -8,8 +8,11 @@ returns (dq, dk, dv); caller-owned outputs may be passed in and are
 overwritten.  ``causal=True`` is the page's ``window_size=(-1, 0)`` and
 ``causal=False`` its ``(-1, -1)``; ``window_size=(left, right)``, when given,
 sets the mask instead ("Mask support": key j visible to query i iff
-i - left <= j <= i + right, -1 = unbounded).  There is no fallback: if the
-library is missing, every call raises.
+i - left <= j <= i + right, -1 = unbounded); ``func=`` (a device int32 tensor of
+shape ``(N, L)`` or the page's ``(1, N, L)``, N odd, L >= T_q) selects the
+arbitrary mask: packed query row r sees the local keys
+``[0, F0) u [F1, F2) u ...`` with ``F_n = func[..., n, r]``.  There is no
+fallback: if the library is missing, every call raises.
 """
 
 from __future__ import annotations
@@ -39,6 +42,7 @@ __all__ = [
     "HSTU_MASK_NONE",
     "HSTU_MASK_CAUSAL",
     "HSTU_MASK_WINDOW",
+    "HSTU_MASK_FUNC",
 ]
 
 HSTU_OK = 0
@@ -48,7 +52,8 @@ HSTU_ERR_DEVICE = 3
 HSTU_MASK_NONE = 0
 HSTU_MASK_CAUSAL = 1
 HSTU_MASK_WINDOW = 2
-ABI_VERSION = 3
+HSTU_MASK_FUNC = 3
+ABI_VERSION = 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -79,6 +84,9 @@ class HstuArgs(ctypes.Structure):
         ("mask", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("func_n", ctypes.c_int32),
+        ("func_ld", ctypes.c_int32),
+        ("func", ctypes.c_void_p),
         ("q", HstuStride),
         ("k", HstuStride),
         ("v", HstuStride),
@@ -179,7 +187,8 @@ def _stream(stream, device) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size) -> HstuArgs:
+def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size,
+          func=None) -> HstuArgs:
     a = HstuArgs()
     a.batch = int(cu_q.shape[0]) - 1
     a.total_q = int(q.shape[0])
@@ -190,7 +199,18 @@ def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal,
     a.max_seqlen_k = int(max_seqlen_k)
     a.alpha = float(alpha)
     a.scaling_seqlen = 0 if scaling_seqlen is None else int(scaling_seqlen)
-    if window_size is None:
+    if func is not None:
+        if window_size is not None:
+            raise ValueError("func and window_size cannot be combined")
+        if not isinstance(func, torch.Tensor) or func.dtype != torch.int32:
+            raise TypeError("func must be an int32 tensor")
+        f = func[0] if func.dim() == 3 else func
+        if f.dim() != 2 or f.device != q.device or f.stride(1) != 1:
+            raise ValueError("func must be (N, L) or (1, N, L) on the device of q, rows contiguous")
+        if f.shape[0] % 2 != 1 or f.shape[1] < q.shape[0]:
+            raise ValueError("func needs an odd number of endpoint rows of at least T_q columns")
+        a.mask, a.func_n, a.func_ld, a.func = HSTU_MASK_FUNC, int(f.shape[0]), int(f.stride(0)), f.data_ptr()
+    elif window_size is None:
         a.mask = HSTU_MASK_CAUSAL if causal else HSTU_MASK_NONE
     else:
         left, right = (int(w) for w in window_size)
@@ -220,13 +240,13 @@ def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
              scaling_seqlen: Optional[int] = None, causal: bool = True,
              out: Optional[torch.Tensor] = None, stream=None,
-             window_size: Optional[Tuple[int, int]] = None) -> torch.Tensor:
+             window_size: Optional[Tuple[int, int]] = None, func: Optional[torch.Tensor] = None) -> torch.Tensor:
     """O = HSTU(q, k, v) on packed (T, H, D) bf16 tensors; returns ``out``."""
     H, D, pq, pk = _inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     _thd("out", out, int(q.shape[0]), H, D)
-    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     a.q, a.k, a.v, a.o = _stride(q), _stride(k), _stride(v), _stride(out)
     _check(library().hstu_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(), pq, pk,
                               out.data_ptr(), _stream(stream, q.device)))
@@ -234,10 +254,10 @@ def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def _bwd_common(dout, q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal,
-                window_size):
+                window_size, func=None):
     H, D, pq, pk = _inputs(q, k, v, cu_q, cu_k)
     _thd("dout", dout, int(q.shape[0]), H, D)
-    a = _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+    a = _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     a.q, a.k, a.v, a.dout = _stride(q), _stride(k), _stride(v), _stride(dout)
     return H, D, pq, pk, a
 
@@ -248,12 +268,13 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              scaling_seqlen: Optional[int] = None, causal: bool = True,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-             window_size: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             window_size: Optional[Tuple[int, int]] = None, func: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.  ``workspace``
     (a device byte tensor) is allocated here when the library asks for one and
     none is given."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -274,10 +295,10 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
 
 
 def hstu_bwd_workspace_size(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                            alpha=1.0, scaling_seqlen=None, causal=True, window_size=None) -> int:
+                            alpha=1.0, scaling_seqlen=None, causal=True, window_size=None, func=None) -> int:
     """Bytes of device workspace ``hstu_bwd`` needs for this problem."""
     _, _, _, _, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, alpha,
-                                scaling_seqlen, causal, window_size)
+                                scaling_seqlen, causal, window_size, func)
     need = ctypes.c_size_t(0)
     _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
     return int(need.value)
@@ -285,10 +306,10 @@ def hstu_bwd_workspace_size(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqle
 
 def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                 alpha=1.0, scaling_seqlen=None, causal=True, dq=None, stream=None,
-                window_size=None) -> torch.Tensor:
+                window_size=None, func=None) -> torch.Tensor:
     """dq only (the query-major backward kernel)."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     _thd("dq", dq, int(q.shape[0]), H, D)
     a.dq = _stride(dq)
@@ -299,10 +320,10 @@ def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seq
 
 def hstu_bwd_dkdv(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                   alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None,
-                  window_size=None):
+                  window_size=None, func=None):
     """(dk, dv) only (the key-major backward kernel)."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     _thd("dk", dk, int(k.shape[0]), H, D)

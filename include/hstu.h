@@ -50,7 +50,23 @@
  *                      and (-1, 0) run exactly as HSTU_MASK_NONE and
  *                      HSTU_MASK_CAUSAL.  Needs max_seqlen_k <= 2^29
  *                      (HSTU_ERR_UNSUPPORTED otherwise).
- *   window_left and window_right are read only with HSTU_MASK_WINDOW.
+ *   HSTU_MASK_FUNC   : the arbitrary mask ("Mask support", the func_tensor
+ *                      paragraphs).  `func` (device, int32) holds func_n
+ *                      endpoint rows of func_ld elements: packed query row r
+ *                      (0 <= r < T_q) has endpoints F_n = func[n * func_ld + r],
+ *                      n < func_n, func_n odd, and sees the local keys
+ *                      [0, F0) u [F1, F2) u [F3, F4) u ... of its sequence.  The
+ *                      intervals are independent (they may overlap, come in any
+ *                      order, be empty or reach past either end of the
+ *                      sequence; keys outside it stay invisible).  The page's
+ *                      (1, N, L) tensor with L >= T_q + 256 is func_n = N,
+ *                      func_ld = L; only columns below T_q are read, so
+ *                      func_ld >= T_q suffices.  The endpoint values are
+ *                      trusted and never read on the host; any int32 values are
+ *                      safe on the device.  func is read by every kernel of the
+ *                      call, so in-place changes between calls are seen.
+ *   window_left and window_right are read only with HSTU_MASK_WINDOW, func,
+ *   func_n and func_ld only with HSTU_MASK_FUNC.
  *
  * -- Trust and validation ("Tensor layout", the paragraph on metadata) --------
  *   The library checks every scalar and pointer argument on the host and never
@@ -91,7 +107,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 3
+#define HSTU_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define HSTU_API __attribute__((visibility("default")))
@@ -109,7 +125,8 @@ typedef enum hstu_status {
 typedef enum hstu_mask {
     HSTU_MASK_NONE = 0,   /* window (-1, -1) */
     HSTU_MASK_CAUSAL = 1, /* window (-1, 0), top-left aligned */
-    HSTU_MASK_WINDOW = 2  /* window (window_left, window_right), top-left aligned */
+    HSTU_MASK_WINDOW = 2, /* window (window_left, window_right), top-left aligned */
+    HSTU_MASK_FUNC = 3    /* per-row interval list in func (the page's func_tensor) */
 } hstu_mask_t;
 
 /* Strides of one (T, H, D) tensor, in elements.  {0, 0} = packed. */
@@ -133,6 +150,9 @@ typedef struct hstu_args {
     int32_t mask;           /* an hstu_mask_t                                             */
     int32_t window_left;    /* HSTU_MASK_WINDOW: keys j >= i - window_left; -1 = no bound  */
     int32_t window_right;   /* HSTU_MASK_WINDOW: keys j <= i + window_right; -1 = no bound */
+    int32_t func_n;         /* HSTU_MASK_FUNC: endpoints per query row, odd, >= 1          */
+    int32_t func_ld;        /* HSTU_MASK_FUNC: elements between endpoint rows, >= T_q       */
+    const int32_t* func;    /* HSTU_MASK_FUNC: device, 4-byte aligned, func_n x func_ld     */
     hstu_stride_t q, k, v;  /* input strides                                              */
     hstu_stride_t o;        /* forward output                                             */
     hstu_stride_t dout;     /* backward upstream gradient                                 */

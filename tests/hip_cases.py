@@ -46,11 +46,12 @@ class DeviceWorkload:
         self.do = to_dev(wl.do, device) if wl.do is not None else None
         self.cu_q = torch.from_numpy(wl.cu_seqlens_q).to(device)
         self.cu_k = torch.from_numpy(wl.cu_seqlens_k).to(device)
+        self.func = torch.from_numpy(wl.func).to(device) if wl.func is not None else None
 
     def kw(self):
         wl = self.wl
         return dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, alpha=float(wl.alpha),
-                    scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window)
+                    scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window, func=self.func)
 
     def fwd(self, **over):
         kw = self.kw()

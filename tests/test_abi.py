@@ -46,14 +46,17 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    # 7 int32 + float + 4 int32 = 48 bytes, then 8 stride pairs of 16 bytes
-    assert ctypes.sizeof(hstu.HstuArgs) == 48 + 8 * 16
+    # 7 int32 + float + 6 int32 = 56 bytes, the func pointer (8), then 8 stride pairs of 16 bytes
+    assert ctypes.sizeof(hstu.HstuArgs) == 64 + 8 * 16
     assert hstu.HstuArgs.mask.offset == 36
     assert hstu.HstuArgs.window_left.offset == 40 and hstu.HstuArgs.window_right.offset == 44
-    assert hstu.HstuArgs.q.offset == 48
-    assert hstu.HstuArgs.dv.offset == 48 + 7 * 16
+    assert hstu.HstuArgs.func_n.offset == 48 and hstu.HstuArgs.func_ld.offset == 52
+    assert hstu.HstuArgs.func.offset == 56
+    assert hstu.HstuArgs.q.offset == 64
+    assert hstu.HstuArgs.dv.offset == 64 + 7 * 16
     text = open(HEADER).read()
     assert re.search(r"HSTU_MASK_WINDOW\s*=\s*2", text) and hstu.HSTU_MASK_WINDOW == 2
+    assert re.search(r"HSTU_MASK_FUNC\s*=\s*3", text) and hstu.HSTU_MASK_FUNC == 3
 
 
 def good_args(**kw):
@@ -76,7 +79,12 @@ REJECT = [
     # (description, args overrides, expected status)
     ("head_dim 48", dict(head_dim=48), hstu.HSTU_ERR_UNSUPPORTED),
     ("head_dim 256", dict(head_dim=256), hstu.HSTU_ERR_UNSUPPORTED),
-    ("mask 3", dict(mask=3), hstu.HSTU_ERR_UNSUPPORTED),
+    ("mask 4", dict(mask=4), hstu.HSTU_ERR_UNSUPPORTED),
+    ("func_n even", dict(mask=3, func_n=2, func_ld=32, func=FAKE), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("func_n 0", dict(mask=3, func_n=0, func_ld=32, func=FAKE), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("func_ld below total_q", dict(mask=3, func_n=3, func_ld=31, func=FAKE), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("func null", dict(mask=3, func_n=3, func_ld=32, func=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("func misaligned", dict(mask=3, func_n=3, func_ld=32, func=FAKE + 2), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("window left -2", dict(mask=2, window_left=-2, window_right=0), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("window right -5", dict(mask=2, window_left=3, window_right=-5), hstu.HSTU_ERR_INVALID_ARGUMENT),
     ("window past 2^29 keys", dict(mask=2, window_left=8, window_right=0, total_q=(1 << 29) + 2,

@@ -34,3 +34,22 @@ def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     out = json.loads(capsys.readouterr().out.strip())
     assert "one GPU" in out["error"]
+
+
+def test_func_pairs_match_window_and_random_brute_force():
+    from generative_recommender_attention_amd.workloads import func_random_mask
+
+    lens_q, lens_k = [5, 0, 13, 9], [7, 2, 13, 4]
+    i = np.concatenate([np.arange(n) for n in lens_q])
+    f = np.stack([np.zeros_like(i), i - 2, i + 4]).astype(np.int32)  # window (2, 3)
+    assert bench.func_visible_pairs(f, lens_q, lens_k) == bench.visible_pairs(lens_q, lens_k, (2, 3))
+    f = func_random_mask(np.random.default_rng(3), lens_q, lens_k, 5)
+    want, r0 = 0, 0
+    for lq, lk in zip(lens_q, lens_k):
+        for r in range(r0, r0 + lq):
+            keys = set(range(0, min(lk, max(0, f[0, r]))))
+            for n in (1, 3):
+                keys |= set(range(max(0, f[n, r]), min(lk, f[n + 1, r])))
+            want += len(keys)
+        r0 += lq
+    assert bench.func_visible_pairs(f, lens_q, lens_k) == want

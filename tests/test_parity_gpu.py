@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from generative_recommender_attention_amd import hstu
-from generative_recommender_attention_amd.workloads import make_workload, named_workload
+from generative_recommender_attention_amd.workloads import func_random_mask, make_workload, named_workload
 
 from hip_cases import DeviceWorkload, check_close, sample_rows, say, to_f64
 
@@ -178,6 +178,73 @@ def test_window_invalid_bounds_raise():
         dw.fwd(window_size=(-2, 0))
     with pytest.raises(hstu.HstuError):
         hstu.hstu_bwd(dw.q, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, 10, 10, window_size=(3, -7))
+
+
+# ------------------------------------------------------------------ arbitrary interval masks
+FUNC_CASES = [
+    # (seed, lengths_q, lengths_k or None, H, D, endpoints per row)
+    (150, EDGE_LENGTHS, None, 2, 128, 3),
+    (151, EDGE_LENGTHS, None, 2, 64, 1),
+    (152, EDGE_LENGTHS, None, 1, 32, 5),
+    (153, EDGE_LENGTHS, None, 2, 16, 3),
+    (154, [300, 5, 0, 257], [310, 9, 4, 257], 2, 128, 5),     # L_k > L_q
+    (155, [130, 40, 7], [131, 38, 3], 3, 64, 3),              # L_k < L_q
+    (156, [700, 1000], None, 2, 128, 1),                      # long rows, one interval [0, F0)
+]
+
+
+@pytest.mark.parametrize("case", FUNC_CASES, ids=[f"seed{c[0]}_d{c[4]}_n{c[5]}" for c in FUNC_CASES])
+def test_func_mask_fwd_bwd(oracle_lib, case):
+    seed, lq, lk, H, D, n = case
+    lk = lq if lk is None else lk
+    f = func_random_mask(np.random.default_rng(seed), lq, lk, n)
+    wl = make_workload(f"func{seed}", seed, lq, H, D, False, 1.0, lengths_k=lk, with_do=True, func=f)
+    run_fwd_check(wl)
+    run_bwd_check(wl)
+
+
+def test_func_target_workload_sampled(oracle_lib):
+    wl = named_workload("zipf_b32_h4_d128_target_fwdbwd")
+    rows = sample_rows(wl.cu_seqlens_q, per_seq=32, seed=6)
+    tail = np.concatenate([np.arange(max(s, e - 40), e) for s, e in zip(wl.cu_seqlens_q[:-1], wl.cu_seqlens_q[1:])])
+    rows = np.union1d(rows, tail)  # the candidate rows of every sequence
+    rel, worst = run_fwd_check(wl, rows, " (sampled rows)")
+    print(f"target fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
+    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    print("target bwd (err/max, worst per-seq):", res)
+
+
+def test_func_spelling_causal_and_window_is_bitwise_those_masks():
+    """Endpoints that spell causal (F0 = i + 1) or a window walk the same tiles in the
+    same order as those kernels, so the results agree bit for bit."""
+    lens = [200, 64, 129, 1]
+    wl = make_workload("fspell", 157, lens, 2, 128, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    i = np.concatenate([np.arange(n) for n in lens])
+    causal_f = torch.from_numpy((i + 1)[None, :].astype(np.int32)).cuda()
+    left, right = 70, 0
+    win_f = torch.from_numpy(np.stack([np.zeros_like(i), i - left, i + right + 1]).astype(np.int32)).cuda()
+    say("func spelling causal / window (70, 0) vs those kernels")
+    oc, gc = dw.fwd(causal=True), dw.bwd(causal=True)
+    of, gf = dw.fwd(func=causal_f), dw.bwd(func=causal_f)
+    ow, gw = dw.fwd(window_size=(left, right)), dw.bwd(window_size=(left, right))
+    ofw, gfw = dw.fwd(func=win_f), dw.bwd(func=win_f)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, of) and all(torch.equal(a, b) for a, b in zip(gc, gf))
+    assert torch.equal(ow, ofw) and all(torch.equal(a, b) for a, b in zip(gw, gfw))
+
+
+def test_func_invalid_arguments_raise():
+    wl = make_workload("fbad", 158, [10], 1, 16, True)
+    dw = DeviceWorkload(wl)
+    even = torch.zeros(2, 10, dtype=torch.int32, device="cuda")
+    short = torch.zeros(3, 9, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        dw.fwd(func=even)
+    with pytest.raises(ValueError):
+        dw.fwd(func=short)
+    with pytest.raises(ValueError):
+        dw.fwd(func=torch.zeros(1, 10, dtype=torch.int32, device="cuda"), window_size=(1, 1))
 
 
 # ------------------------------------------------------------------ invariants
