@@ -66,9 +66,9 @@ constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
 // How the dq kernel masks a 32-key block: kNoMask never; kInterval (full or
 // causal) when the block reaches past wlim, the end of the keys every row of the
 // wave sees, against this lane's keys [0, span); kBand (token window) when the
-// block leaves [wlo, wlim), against [lo, lo + span); kBits always, against the
-// block's bit word `lo` (pre-shifted by 4 g: bit 8 (r / 4) + r % 4 is the key of
-// accumulator register r).
+// block leaves [wlo, wlim), against [lo, lo + span); kBits when the wave-uniform
+// flag `span` is set, against the block's bit word `lo` (pre-shifted by 4 g: bit
+// 8 (r / 4) + r % 4 is the key of accumulator register r).
 enum DqMask : int { kNoMask = 0, kInterval = 1, kBand = 2, kBits = 3 };
 
 // dS^T operands of one 32-key block from its score and dA accumulators, masked
@@ -83,8 +83,11 @@ __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc,
         dv[r] = dacc[r] * dsilu_from(sacc[r] * sg, sg);
     }
     if constexpr (MT == kBits) {
+        if (span) {
+            keep_branch();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dv[r] = ((unsigned)lo >> (8 * (r >> 2) + (r & 3))) & 1u ? dv[r] : 0.0f;
+            for (int r = 0; r < 16; ++r) dv[r] = ((unsigned)lo >> (8 * (r >> 2) + (r & 3))) & 1u ? dv[r] : 0.0f;
+        }
     } else if constexpr (MT != kNoMask) {
         if ((MT == kBand && key0 < wlo) || key0 + 32 > wlim) {
             keep_branch();
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     // [lo, lo + span); keys every live row of the wave sees [wlo, wlim); keys
     // some live row of the wave sees [any_lo, any_hi) (window only).
     int kv_begin = 0, kv_end = sb.lk, lo = 0, span, wlo = 0, wlim, any_lo = 0, any_hi = 0;
+    int f0 = 0, f1 = 0, f2 = 0;  // func: this lane's first endpoints, kept for the whole walk
     if constexpr (WINDOW) {
         const int L = p.win_left, R = p.win_right;
         const int last = min(m0 + BM, sb.lq) - 1, wlast = min(row0 + 31, sb.lq - 1);
@@ -200,6 +204,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
         // keys between the smallest and the largest visible key of any row of the block
         int rlo = 0x7fffffff, rhi = 0;
         if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
+        const int frow = sb.q0 + min(my_row, sb.lq - 1);
+        f0 = p.func[frow];
+        if (p.func_n > 1) {
+            f1 = p.func[(int64_t)p.func_ld + frow];
+            f2 = p.func[2 * (int64_t)p.func_ld + frow];
+        }
         rlo = wave_min(rlo);
         rhi = wave_max(rhi);
         if (lane == 0) {
@@ -274,15 +284,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
                 // between skipping the tile, the unmasked code and the bit-masked code
                 if (wave_live) {
                     const bool live = my_row < sb.lq;
-                    const uint64_t bits =
-                        func_bits64(p.func, p.func_ld, p.func_n, sb.q0 + min(my_row, sb.lq - 1), n0, sb.lk);
+                    const uint64_t bits = func_bits64_pre(f0, f1, f2, p.func, p.func_ld, p.func_n,
+                                                          sb.q0 + min(my_row, sb.lq - 1), n0, sb.lk);
                     const uint64_t seen = __ballot(live && bits != 0);
-                    const uint64_t cut = __ballot(live && bits != ~0ull);
+                    const int cut = __ballot(live && bits != ~0ull) != 0;
                     const uint64_t sh = bits >> (4 * g);
-                    if (cut == 0)
-                        dq_tile<D, kNoMask>(kc, vc, qf, dof, acc, koff, toff, n0, 0, 0, 0, 0, 0, g);
-                    else if (seen != 0)
-                        dq_tile<D, kBits>(kc, vc, qf, dof, acc, koff, toff, n0, (int)(uint32_t)sh, 0, 0, 0,
+                    if (seen != 0)
+                        dq_tile<D, kBits>(kc, vc, qf, dof, acc, koff, toff, n0, (int)(uint32_t)sh, cut, 0, 0,
                                           (int)(uint32_t)(sh >> 32), g);
                 }
             } else {
@@ -322,10 +330,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
 
 // One 32-row block for one wave: S = Q K^T and dA = dO V^T (A operands: Q, dO
 // rows of the block; B operands: the wave's K, V rows), then dV^T += dO^T A' and
-// dK^T += Q^T dS over the block's two contraction steps.  MT = kInterval: when
-// `mask`, rows outside this lane's [lo, hi) are zeroed; kBits: row 8 k + 4 g + j
-// of the block (accumulator register 4 k + j) is tested against bit l32 of the
-// LDS word at mw + 32 k + 4 j; kNoMask: nothing is zeroed.
+// dK^T += Q^T dS over the block's two contraction steps.  When `mask` (wave-
+// uniform): MT = kInterval zeroes the rows outside this lane's [lo, hi); kBits
+// tests row 8 k + 4 g + j of the block (accumulator register 4 k + j) against
+// bit l32 of the LDS word at mw + 32 k + 4 j.
 template <int D, int MT>
 __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t drow, uint32_t krow, uint32_t vrow, uint32_t qtr,
                                             uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
@@ -369,16 +377,19 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
         dv[r] = da[r] * dsilu_from(av[r], sg);
     }
     if constexpr (MT == kBits) {
-        const int l32 = threadIdx.x & 31;
+        if (mask) {
+            keep_branch();
+            const int l32 = threadIdx.x & 31;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint4 w = ds_read16(mw + 32 * k);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            for (int k = 0; k < 4; ++k) {
+                const uint4 w = ds_read16(mw + 32 * k);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool ok = (ws[j] >> l32) & 1u;
-                av[4 * k + j] = ok ? av[4 * k + j] : 0.0f;
-                dv[4 * k + j] = ok ? dv[4 * k + j] : 0.0f;
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = (ws[j] >> l32) & 1u;
+                    av[4 * k + j] = ok ? av[4 * k + j] : 0.0f;
+                    dv[4 * k + j] = ok ? dv[4 * k + j] : 0.0f;
+                }
             }
         }
     } else if constexpr (MT == kInterval) {
@@ -508,15 +519,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         q_end = qhi >= qlo ? qhi + 1 : 0;
     }
     const int ntiles = q_end > q_begin ? (q_end - q_begin + BMQ - 1) / BMQ : 0;
-    // func: the words of the tile at rows qt0.. into slot `slot` (threads 0-255, one word each)
-    auto build_words = [&](int slot, int qt0) {
+    // func: the words of the tile at rows qt0.. (threads 0-255, one word each: row
+    // tid % 64, keys n0 + 32 (tid / 64) ..), in two halves: load_ends reads the
+    // row's first endpoints, store_word turns them into the word for slot `slot`
+    // (the rest of the endpoints, if any, are read there).
+    const int wrow = tid & 63, wkey = n0 + 32 * (tid >> 6);
+    auto load_ends = [&](int qt0, int& e0, int& e1, int& e2) {
+        e0 = e1 = e2 = 0;
         if constexpr (FUNC) {
-            if (tid < 256) {
-                const int row = tid & 63, w = tid >> 6;
-                const int i = qt0 + row;
-                fmask[slot * 256 + w * 64 + row] =
-                    i < sb.lq ? func_bits32(p.func, p.func_ld, p.func_n, sb.q0 + i, n0 + 32 * w, sb.lk) : 0u;
+            const int i = qt0 + wrow;
+            if (tid < 256 && i < sb.lq) {
+                e0 = p.func[sb.q0 + i];
+                if (p.func_n > 1) {
+                    e1 = p.func[(int64_t)p.func_ld + sb.q0 + i];
+                    e2 = p.func[2 * (int64_t)p.func_ld + sb.q0 + i];
+                }
             }
+        }
+    };
+    auto store_word = [&](int slot, int qt0, int e0, int e1, int e2) {
+        if constexpr (FUNC) {
+            const int i = qt0 + wrow;
+            if (tid < 256)
+                fmask[slot * 256 + tid] =
+                    i < sb.lq ? func_bits32_pre(e0, e1, e2, p.func, p.func_ld, p.func_n, sb.q0 + i, wkey, sb.lk) : 0u;
         }
     };
     const uint32_t krow = KB + 8192u * kw, vrow = VB + 8192u * kw;
@@ -538,15 +564,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
             }
         }
         dma.issue(lds0 + (qgrp ? Q0 : D0), sbase, stok, q_begin, sb.lq);
-        build_words(0, q_begin);
+        {
+            int e0, e1, e2;
+            load_ends(q_begin, e0, e1, e2);
+            store_word(0, q_begin, e0, e1, e2);
+        }
         wait_global_loads();
         __syncthreads();
 
         auto step = [&](uint32_t qc, uint32_t dc, uint32_t qn, uint32_t dn, int t) {
             const int qt0 = q_begin + t * BMQ;
+            int e0 = 0, e1 = 0, e2 = 0;  // func: the next tile's endpoints, in flight with its DMA
             if (t + 1 < ntiles) {
                 dma.issue(lds0 + (qgrp ? qn : dn), sbase, stok, qt0 + BMQ, sb.lq);
-                build_words((t + 1) & 1, qt0 + BMQ);  // that slot was last read before the previous barrier
+                load_ends(qt0 + BMQ, e0, e1, e2);
             }
             const int row0 = qt0 + 32 * qh;
             const uint32_t qr = qc + 8192u * qh, dr = dc + 8192u * qh;
@@ -561,12 +592,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     const uint64_t seen = __ballot(live && word != 0);
                     const uint64_t cut = __ballot(live && word != valid);
                     // rows past the sequence (copies of its last row) must be masked out too
-                    if (cut == 0 && row0 + 32 <= sb.lq)
-                        dkdv_block<D, kNoMask>(false, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff, row0, 0, 0,
-                                               g, 0);
-                    else if (seen != 0)
-                        dkdv_block<D, kBits>(true, qr, dr, krow, vrow, qr, dr, dvacc, dkacc, roff, toff, row0, 0, 0, g,
-                                             lds_addr(fmask) + 4u * (wbase + 4 * g));
+                    if (seen != 0)
+                        dkdv_block<D, kBits>(cut != 0 || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
+                                             roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g));
                 }
             } else {
                 // waves whose keys no row of the block sees, or that lie past the sequence, skip it
@@ -578,6 +606,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                 }
             }
             wait_global_loads();
+            // the next tile's words into the other slot, last read before the previous barrier
+            if (FUNC && t + 1 < ntiles) store_word((t + 1) & 1, qt0 + BMQ, e0, e1, e2);
             __syncthreads();
         };
         for (int t = 0; t < ntiles; t += 2) {

@@ -181,41 +181,34 @@ template <int D, int NW = 4>
 struct TileDma {
     static constexpr int CPW = 16 / NW;  // 1 KB chunks per wave
     static_assert(NW * CPW == 16, "a tile is 16 chunks");
-    uint32_t off[CPW];  // byte offset of this lane's source from the tile's row 0
-    int wave;           // 0 .. NW-1 among the loading waves (wave-uniform)
+    int wave;  // 0 .. NW-1 among the loading waves (wave-uniform)
     int lane;
 
     __device__ __forceinline__ static int chunk_row(int wave, int i, int lane) { return 4 * (wave * CPW + i) + (lane >> 4); }
     __device__ __forceinline__ static int chunk_col(int r, int lane) { return (lane & 15) ^ tile_swz(r); }
 
-    __device__ __forceinline__ void init(int wave_, int lane_, int64_t tok) {
+    __device__ __forceinline__ void init(int wave_, int lane_, int64_t) {
         wave = wave_;
         lane = lane_;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int r = chunk_row(wave, i, lane);
-            off[i] = (uint32_t)(2 * (r * tok + 8 * chunk_col(r, lane)));
-        }
     }
     // Fill the tile at LDS byte `tile` with local rows row0 .. row0+63 of the
-    // tensor at `base`; rows at or past valid_end repeat row valid_end - 1.
+    // tensor at `base`; rows at or past valid_end repeat row valid_end - 1.  The
+    // per-lane source offsets are recomputed at every call (a few VALU
+    // instructions) rather than kept in registers across the tile loop: kept,
+    // they were among the first values spilled under register pressure, and a
+    // reload from scratch between two of these copies made the wave wait for the
+    // copy before it.  Offsets fit 32 bits: 2 * (63 tok + 8 * 15) < 2^32 for
+    // token strides up to 2^24 elements.
     __device__ __forceinline__ void issue(uint32_t tile, const uint16_t* base, int64_t tok, int row0,
                                           int valid_end) const {
         const uint16_t* src = base + (int64_t)row0 * tok;
         const uint32_t dst = tile + (uint32_t)(wave * CPW) * 1024u;
-        if (row0 + kTileRows <= valid_end) {
+        const int last = row0 + kTileRows <= valid_end ? kTileRows - 1 : valid_end - 1 - row0;
+        const uint32_t tok2 = 2u * (uint32_t)tok;
 #pragma unroll
-            for (int i = 0; i < CPW; ++i)
-                if (D == 128 || chunk_col(chunk_row(wave, i, lane), lane) < D / 8) dma16_lds(dst + 1024 * i, src, off[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-                const int r = chunk_row(wave, i, lane), c = chunk_col(r, lane);
-                if (D == 128 || c < D / 8) {
-                    const int rr = min(r, valid_end - 1 - row0);
-                    dma16_lds(dst + 1024 * i, src, (uint32_t)(2 * (rr * tok + 8 * c)));
-                }
-            }
+        for (int i = 0; i < CPW; ++i) {
+            const int r = chunk_row(wave, i, lane), c = chunk_col(r, lane);
+            if (D == 128 || c < D / 8) dma16_lds(dst + 1024 * i, src, (uint32_t)min(r, last) * tok2 + 16u * (uint32_t)c);
         }
     }
 };
@@ -291,12 +284,14 @@ __device__ __forceinline__ bool find_block(const int32_t* cu, int B, int BM, int
 struct SeqBounds {
     int q0, lq, k0, lk;
 };
+// The values are wave-uniform (b is); saying so keeps them, and the tile base
+// pointers derived from them, in scalar registers.
 __device__ __forceinline__ SeqBounds seq_bounds(const int32_t* cu_q, const int32_t* cu_k, int b) {
     SeqBounds s;
-    s.q0 = cu_q[b];
-    s.lq = cu_q[b + 1] - s.q0;
-    s.k0 = cu_k[b];
-    s.lk = cu_k[b + 1] - s.k0;
+    s.q0 = __builtin_amdgcn_readfirstlane(cu_q[b]);
+    s.lq = __builtin_amdgcn_readfirstlane(cu_q[b + 1]) - s.q0;
+    s.k0 = __builtin_amdgcn_readfirstlane(cu_k[b]);
+    s.lk = __builtin_amdgcn_readfirstlane(cu_k[b + 1]) - s.k0;
     return s;
 }
 
@@ -342,6 +337,25 @@ __device__ __forceinline__ uint64_t func_bits64(const int32_t* f, int ld, int N,
 __device__ __forceinline__ uint32_t func_bits32(const int32_t* f, int ld, int N, int row, int n0, int lk) {
     uint32_t m = span_bits32(0, f[row], n0);
     for (int n = 1; n + 1 < N; n += 2)
+        m |= span_bits32(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
+    return m & span_bits32(0, lk, n0);
+}
+
+// The same, with the row's first three endpoints already in registers (f0; f1, f2
+// when N > 1): only endpoints past the third are read from memory.
+__device__ __forceinline__ uint64_t func_bits64_pre(int f0, int f1, int f2, const int32_t* f, int ld, int N, int row,
+                                                    int n0, int lk) {
+    uint64_t m = span_bits64(0, f0, n0);
+    if (N > 1) m |= span_bits64(f1, f2, n0);
+    for (int n = 3; n + 1 < N; n += 2)
+        m |= span_bits64(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
+    return m & span_bits64(0, lk, n0);
+}
+__device__ __forceinline__ uint32_t func_bits32_pre(int f0, int f1, int f2, const int32_t* f, int ld, int N, int row,
+                                                    int n0, int lk) {
+    uint32_t m = span_bits32(0, f0, n0);
+    if (N > 1) m |= span_bits32(f1, f2, n0);
+    for (int n = 3; n + 1 < N; n += 2)
         m |= span_bits32(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
     return m & span_bits32(0, lk, n0);
 }

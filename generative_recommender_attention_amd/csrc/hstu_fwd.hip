@@ -43,16 +43,16 @@ constexpr int BN = kTileRows;                    // 64 keys per tile
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
 
 // How a tile's scores are masked: not at all; against this lane's key interval
-// [lo, lo + span) (one unsigned compare tests both ends); or against a bit word
-// per 32-key block (bit 8 (r / 4) + r % 4 of the word, pre-shifted by 4 g, is the
-// key of accumulator register r).
+// [lo, lo + span) (one unsigned compare tests both ends); or, when the wave-uniform
+// flag is set, against a bit word per 32-key block (bit 8 (r / 4) + r % 4 of the
+// word, pre-shifted by 4 g, is the key of accumulator register r).
 enum TileMask : int { kNoMask = 0, kInterval = 1, kBits = 2 };
 
 // bf16 P^T operand from accumulator registers r0..r0+7 of a 32-key block whose
 // first key is key0.  The scores arrive as y = c x with c = -alpha log2(e)
 // folded into Q (x = q.k), so y sig(alpha x) = y / (1 + 2^y) costs one exp, one
 // add, one rcp and one multiply; the factor 1/c is folded into the output
-// scale.  kInterval: (a, b) = (lo, span); kBits: a = the block's bit word.
+// scale.  kInterval: (a, b) = (lo, span); kBits: a = the block's bit word, b the flag.
 template <int MT>
 __device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int a, int b, int g) {
     float pv[8];
@@ -63,10 +63,13 @@ __device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0,
         for (int r = 0; r < 8; ++r)
             pv[r] = (unsigned)(key0 + acc_row(r0 + r, g) - a) < (unsigned)b ? pv[r] : 0.0f;
     } else if constexpr (MT == kBits) {
+        if (b) {
+            keep_branch();
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int bit = 8 * ((r0 + r) >> 2) + ((r0 + r) & 3);
-            pv[r] = ((unsigned)a >> bit) & 1u ? pv[r] : 0.0f;
+            for (int r = 0; r < 8; ++r) {
+                const int bit = 8 * ((r0 + r) >> 2) + ((r0 + r) & 3);
+                pv[r] = ((unsigned)a >> bit) & 1u ? pv[r] : 0.0f;
+            }
         }
     }
     return pack_operand(pv);
@@ -154,6 +157,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     // window only: keys every live row of the wave sees [full_lo, full_hi), and
     // keys some live row of the wave sees [any_lo, any_hi)
     int full_lo = 0, full_hi = 0, any_lo = 0, any_hi = 0;
+    int f0 = 0, f1 = 0, f2 = 0;  // func: this lane's first endpoints, kept for the whole walk
     if constexpr (WINDOW) {
         const int L = p.win_left, R = p.win_right;
         const int last = min(m0 + BM, sb.lq) - 1;
@@ -170,6 +174,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
         // keys between the smallest and the largest visible key of any row of the block
         int rlo = 0x7fffffff, rhi = 0;
         if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
+        const int frow = sb.q0 + min(my_row, sb.lq - 1);
+        f0 = p.func[frow];
+        if (p.func_n > 1) {
+            f1 = p.func[(int64_t)p.func_ld + frow];
+            f2 = p.func[2 * (int64_t)p.func_ld + frow];
+        }
         rlo = wave_min(rlo);
         rhi = wave_max(rhi);
         if (lane == 0) {
@@ -255,16 +265,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
                 // between skipping the tile, the unmasked code and the bit-masked code
                 if (wave_live) {
                     const bool live = my_row < sb.lq;
-                    const uint64_t bits =
-                        func_bits64(p.func, p.func_ld, p.func_n, sb.q0 + min(my_row, sb.lq - 1), n0, sb.lk);
+                    const uint64_t bits = func_bits64_pre(f0, f1, f2, p.func, p.func_ld, p.func_n,
+                                                          sb.q0 + min(my_row, sb.lq - 1), n0, sb.lk);
                     const uint64_t seen = __ballot(live && bits != 0);
-                    const uint64_t cut = __ballot(live && bits != ~0ull);
-                    if (cut == 0) {
-                        fwd_tile<D, kNoMask, cur, cur>(qf, oacc, koff, voff, n0, 0, 0, 0, 0, g);
-                    } else if (seen != 0) {
+                    const int cut = __ballot(live && bits != ~0ull) != 0;
+                    if (seen != 0) {
                         const uint64_t sh = bits >> (4 * g);
-                        fwd_tile<D, kBits, cur, cur>(qf, oacc, koff, voff, n0, (int)(uint32_t)sh, 0,
-                                                     (int)(uint32_t)(sh >> 32), 0, g);
+                        fwd_tile<D, kBits, cur, cur>(qf, oacc, koff, voff, n0, (int)(uint32_t)sh, cut,
+                                                     (int)(uint32_t)(sh >> 32), cut, g);
                     }
                 }
             } else {
