@@ -38,6 +38,10 @@ __all__ = [
     "named_workload",
     "func_target_mask",
     "func_random_mask",
+    "LmsdWorkload",
+    "make_lmsd_workload",
+    "lmsd_named_workload",
+    "LMSD_WORKLOAD_NAMES",
     "WORKLOAD_NAMES",
 ]
 
@@ -293,3 +297,65 @@ def named_workload(name: str) -> Workload:
         lens = rng.integers(8192, 16384, size=4, endpoint=True)
         return make_workload(name, 3, lens, 8, 128, False, 0.5, rng=rng, with_do=True, window=(1024, 0))
     raise KeyError(f"unknown workload {name!r}; known: {WORKLOAD_NAMES}")
+
+
+# ---------------------------------------------------------------------------
+# HSTU LMSD (LayerNorm, affine, times SiLU(u)) inputs
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class LmsdWorkload:
+    """One synthetic LMSD problem: N rows of D values (host copies, bf16 bits)."""
+
+    name: str
+    seed: int
+    x: np.ndarray        # (N, D) uint16
+    u: np.ndarray        # (N, D) uint16
+    weight: np.ndarray   # (D,) uint16
+    bias: np.ndarray     # (D,) uint16
+    dy: Optional[np.ndarray]  # (N, S D) uint16, backward only
+    eps: float
+    silu_u: bool
+    concat_u: bool
+    concat_x: bool
+
+    @property
+    def n(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def d(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def segments(self) -> int:
+        return 1 + int(self.concat_u) + int(self.concat_x)
+
+
+def make_lmsd_workload(name: str, seed: int, n: int, d: int, silu_u: bool = True, concat_u: bool = True,
+                       concat_x: bool = True, eps: float = 1e-6, with_dy: bool = True) -> LmsdWorkload:
+    """Recipe: ``default_rng(seed)``; x, u ~ N(0, 1); weight ~ 1 + 0.1 N(0, 1);
+    bias ~ 0.1 N(0, 1); then dy ~ N(0, 1) over the (N, S D) output; all float32
+    draws rounded to bf16 (nearest, ties to even), in that order."""
+    rng = np.random.default_rng(seed)
+    x = _normal_bf16(rng, (n, d), 1.0)
+    u = _normal_bf16(rng, (n, d), 1.0)
+    w = f32_to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32))
+    b = f32_to_bf16_bits(0.1 * rng.standard_normal(d, dtype=np.float32))
+    s = 1 + int(concat_u) + int(concat_x)
+    dy = _normal_bf16(rng, (n, s * d), 1.0) if with_dy else None
+    return LmsdWorkload(name, seed, x, u, w, b, dy, float(eps), bool(silu_u), bool(concat_u), bool(concat_x))
+
+
+# The LMSD workloads: the HSTU layer's normalisation of the attention output, one
+# row per token of the Zipf workload (T = 23460) and D = H x d = 4 x 128 = 512,
+# with both auxiliary segments (the page's first example's flags); and the
+# page's own example shape (N = 257, D = 128).
+LMSD_WORKLOAD_NAMES = ("lmsd_n23460_d512", "lmsd_n257_d128")
+
+
+def lmsd_named_workload(name: str) -> LmsdWorkload:
+    if name == "lmsd_n23460_d512":
+        return make_lmsd_workload(name, 7, 23460, 512)
+    if name == "lmsd_n257_d128":
+        return make_lmsd_workload(name, 8, 257, 128)
+    raise KeyError(f"unknown LMSD workload {name!r}; known: {LMSD_WORKLOAD_NAMES}")

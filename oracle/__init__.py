@@ -1,11 +1,12 @@
-"""fp64 CPU oracle for HSTU attention -- test infrastructure only.
+"""fp64 CPU oracle for HSTU attention and HSTU LMSD -- test infrastructure only.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  The product path (the HIP library and its Python binding) never
 does, and this package imports nothing from it.
 
-The arithmetic lives in ``hstu_oracle.c`` (plain C, fp64, libm ``exp``, gcc
-``-O2`` without fast-math, OpenMP over independent output rows).  This module
+The arithmetic lives in ``hstu_oracle.c`` (attention) and ``lmsd_oracle.c``
+(LayerNorm-multiply-SiLU), plain C, fp64, libm ``exp``/``sqrt``, gcc ``-O2``
+without fast-math, OpenMP over independent output rows.  This module
 only builds and loads that file and marshals numpy arrays into it.  bf16 inputs
 are widened exactly to fp64 here (``widen``); the score scale is passed as the
 fp64 widening of the fp32 value the GPU receives.
@@ -31,20 +32,24 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "hstu_oracle.c")
+_SRCS = [os.path.join(_HERE, "hstu_oracle.c"), os.path.join(_HERE, "lmsd_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle_hstu.so")
 _lock = threading.Lock()
 _lib = None
 
 
+def _stale() -> bool:
+    return not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(src) for src in _SRCS)
+
+
 def build(force: bool = True) -> str:
-    """Compile ``hstu_oracle.c`` with gcc into ``liboracle_hstu.so``."""
+    """Compile the oracle's C sources with gcc into ``liboracle_hstu.so``."""
     global _lib
     with _lock:
-        if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if force or _stale():
             tmp = _LIB + f".tmp{os.getpid()}"
             cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                   "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+                   "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"]
             subprocess.run(cmd, check=True)
             os.replace(tmp, _LIB)
             _lib = None
@@ -54,7 +59,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if _stale():
             build(force=False)
         with _lock:
             lib = ctypes.CDLL(_LIB)
@@ -73,6 +78,13 @@ def _load():
             lib.oracle_hstu_bwd_dkdv.argtypes = [i64, i32p, i32p, i64, i64, f64p, f64p, f64p, f64p,
                                                  ctypes.c_double, ctypes.c_double, i64, i64, i32p, i64, i64,
                                                  i64p, i64, f64p, f64p]
+            ci = ctypes.c_int
+            lib.oracle_lmsd_fwd.restype = None
+            lib.oracle_lmsd_fwd.argtypes = [i64, i64, f64p, i64, f64p, i64, f64p, f64p, ctypes.c_double,
+                                            ci, ci, ci, f64p, f64p, f64p]
+            lib.oracle_lmsd_bwd.restype = None
+            lib.oracle_lmsd_bwd.argtypes = [i64, i64, f64p, i64, f64p, i64, f64p, i64, f64p, f64p, f64p, f64p,
+                                            ci, ci, ci, f64p, f64p, f64p, f64p]
             _lib = lib
     return _lib
 
@@ -222,3 +234,58 @@ def bwd_workload(wl, rows_q=None, rows_k=None):
 
 if __name__ == "__main__":  # pragma: no cover - manual build helper
     print(build(force=True), file=sys.stderr)
+
+
+# ---------------------------------------------------------------------------
+# HSTU LMSD (LayerNorm, affine, times SiLU(u) or u; dropout off)
+# ---------------------------------------------------------------------------
+def _rows(a: np.ndarray, name: str) -> np.ndarray:
+    a = _f64(a)
+    if a.ndim != 2:
+        raise ValueError(f"{name} must be (N, D)")
+    return np.ascontiguousarray(a)
+
+
+def lmsd_fwd(x, u, weight, bias, eps: float, silu_u: bool = True, concat_u: bool = False,
+             concat_x: bool = False):
+    """(y, mean, rstd) in fp64; y is (N, S D) with S = 1 + concat_u + concat_x."""
+    x, u = _rows(x, "x"), _rows(u, "u")
+    if x.shape != u.shape:
+        raise ValueError("x and u must match")
+    n, d = x.shape
+    w, b = np.ascontiguousarray(_f64(weight)), np.ascontiguousarray(_f64(bias))
+    if w.shape != (d,) or b.shape != (d,):
+        raise ValueError("weight and bias must be (D,)")
+    s = 1 + int(bool(concat_u)) + int(bool(concat_x))
+    y = np.empty((n, s * d))
+    mean, rstd = np.empty(n), np.empty(n)
+    _load().oracle_lmsd_fwd(n, d, _ptr(x, ctypes.c_double), d, _ptr(u, ctypes.c_double), d,
+                            _ptr(w, ctypes.c_double), _ptr(b, ctypes.c_double), float(eps), int(bool(silu_u)),
+                            int(bool(concat_u)), int(bool(concat_x)), _ptr(y, ctypes.c_double),
+                            _ptr(mean, ctypes.c_double), _ptr(rstd, ctypes.c_double))
+    return y, mean, rstd
+
+
+def lmsd_bwd(dy, x, u, weight, bias, mean, rstd, silu_u: bool = True, concat_u: bool = False,
+             concat_x: bool = False):
+    """(dx, du, dweight, dbias) in fp64 from the upstream gradient dy (N, S D) and the
+    saved statistics."""
+    x, u = _rows(x, "x"), _rows(u, "u")
+    n, d = x.shape
+    dy = _rows(dy, "dy")
+    s = 1 + int(bool(concat_u)) + int(bool(concat_x))
+    if dy.shape != (n, s * d):
+        raise ValueError("dy must be (N, S D)")
+    w, b = np.ascontiguousarray(_f64(weight)), np.ascontiguousarray(_f64(bias))
+    mean = np.ascontiguousarray(mean, dtype=np.float64)
+    rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+    if mean.shape != (n,) or rstd.shape != (n,):
+        raise ValueError("mean and rstd must be (N,)")
+    dx, du = np.empty((n, d)), np.empty((n, d))
+    dw, db = np.empty(d), np.empty(d)
+    _load().oracle_lmsd_bwd(n, d, _ptr(dy, ctypes.c_double), s * d, _ptr(x, ctypes.c_double), d,
+                            _ptr(u, ctypes.c_double), d, _ptr(w, ctypes.c_double), _ptr(b, ctypes.c_double),
+                            _ptr(mean, ctypes.c_double), _ptr(rstd, ctypes.c_double), int(bool(silu_u)),
+                            int(bool(concat_u)), int(bool(concat_x)), _ptr(dx, ctypes.c_double),
+                            _ptr(du, ctypes.c_double), _ptr(dw, ctypes.c_double), _ptr(db, ctypes.c_double))
+    return dx, du, dw, db
