@@ -237,6 +237,102 @@ def cpu_baseline(wl, max_pairs: int):
     }
 
 
+def lmsd_bytes(n: int, d: int, segs: int) -> dict:
+    """Algorithmic HBM bytes of one LMSD forward and backward (bf16 matrices, fp32
+    statistics; weight and bias read once): fwd reads x, u, writes y (S segments),
+    mean, rstd; bwd reads dy, x, u, mean, rstd, writes dx, du (the workspace of
+    column partials is not algorithmic)."""
+    fwd = 2 * n * d * 2 + segs * n * d * 2 + 8 * n + 4 * d
+    bwd = segs * n * d * 2 + 2 * n * d * 2 + 8 * n + 2 * n * d * 2 + 8 * d
+    return {"fwd": fwd, "bwd": bwd}
+
+
+def run_lmsd(args, name: str) -> int:
+    """One step = hstu_lmsd_fwd + hstu_lmsd_bwd on an LMSD workload; HBM-bound, so the
+    line reports effective bandwidth (algorithmic bytes / time) against 8 TB/s."""
+    import torch
+
+    from generative_recommender_attention_amd import hstu
+    from generative_recommender_attention_amd.workloads import lmsd_named_workload
+
+    dev = torch.device("cuda:0")
+    wl = lmsd_named_workload(name)
+    print(f"[bench] LMSD workload {name}: N={wl.n} D={wl.d} segments={wl.segments}", file=sys.stderr, flush=True)
+
+    def td(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, u, w, b, dy = td(wl.x), td(wl.u), td(wl.weight), td(wl.bias), td(wl.dy)
+    flags = dict(apply_u_silu=wl.silu_u, concat_u=wl.concat_u, concat_x=wl.concat_x)
+    y = torch.empty((wl.n, wl.segments * wl.d), dtype=torch.bfloat16, device=dev)
+    mean = torch.empty(wl.n, dtype=torch.float32, device=dev)
+    rstd = torch.empty_like(mean)
+    dx, du = torch.empty_like(x), torch.empty_like(u)
+    dw, db = torch.empty_like(w), torch.empty_like(b)
+    ws = torch.empty(hstu.lmsd_bwd_workspace_size(x, u, eps=wl.eps, **flags), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        hstu.lmsd_fwd(x, u, w, b, eps=wl.eps, y=y, mean=mean, rstd=rstd, stream=stream, **flags)
+        if ev is not None:
+            ev[1].record(stream)
+        hstu.lmsd_bwd(dy, x, u, w, b, mean, rstd, eps=wl.eps, dx=dx, du=du, dweight=dw, dbias=db, workspace=ws,
+                      stream=stream, **flags)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    nbytes = lmsd_bytes(wl.n, wl.d, wl.segments)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = (nbytes["fwd"] + nbytes["bwd"]) / (ms_per_step * 1e-3) / 1e9
+    dominant = "bwd" if bwd_ms >= fwd_ms else "fwd"
+    dom_ms = bwd_ms if dominant == "bwd" else fwd_ms
+    achieved = nbytes[dominant] / (dom_ms * 1e-3) / 1e9
+    result = {
+        "metric": "HSTU LMSD fwd+bwd effective HBM bandwidth (algorithmic bytes / time)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "rows": wl.n, "hidden": wl.d, "segments": wl.segments,
+                   "apply_u_silu": wl.silu_u, "concat_u": wl.concat_u, "concat_x": wl.concat_x,
+                   "parallelism": "single GPU"},
+        "kernels": {"fwd": {"ms": round(fwd_ms, 5), "GB_s": round(nbytes["fwd"] / (fwd_ms * 1e-3) / 1e9, 1)},
+                    "bwd": {"ms": round(bwd_ms, 5), "GB_s": round(nbytes["bwd"] / (bwd_ms * 1e-3) / 1e9, 1)}},
+        "roofline": {"bound": "hbm", "kernel": f"lmsd_{dominant}", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": nbytes[dominant], "avg_launch_ms": round(dom_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        rows = wl.n  # the whole workload: the oracle takes well under a second
+        t0 = time.perf_counter()
+        yy, mm, rr = oracle.lmsd_fwd(wl.x[:rows], wl.u[:rows], wl.weight, wl.bias, wl.eps, wl.silu_u, wl.concat_u,
+                                     wl.concat_x)
+        oracle.lmsd_bwd(wl.dy[:rows], wl.x[:rows], wl.u[:rows], wl.weight, wl.bias, mm, rr, wl.silu_u, wl.concat_u,
+                        wl.concat_x)
+        dt = time.perf_counter() - t0
+        sub = lmsd_bytes(rows, wl.d, wl.segments)
+        result["cpu_baseline"] = {"value": round((sub["fwd"] + sub["bwd"]) / dt / 1e9, 3), "unit": "GB/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"fp64 oracle fwd+bwd on all {rows} rows, {dt:.2f} s"}
+    print(json.dumps(result))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +366,8 @@ def main(argv=None) -> int:
         print(json.dumps({"error": "no GPU visible"}))
         return 1
     dev = torch.device("cuda:0")
+    if args.workload.startswith("lmsd_"):
+        return run_lmsd(args, args.workload)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20)

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "hstu_kernels.h"
+#include "lmsd_kernels.h"
 
 namespace {
 
@@ -272,6 +273,142 @@ hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, co
     st = run_dq(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dq, stream);
     if (st != HSTU_OK) return st;
     return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// LMSD: scalar checks and the kernel parameter block (pointers filled by the caller).
+hstu_status_t lmsd_common(const hstu_lmsd_args_t* a, hstu::LmsdParams& p) {
+    if (a == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args is null");
+    if (a->d < 8 || a->d >= 1024 || a->d % 8 != 0)
+        return fail(HSTU_ERR_UNSUPPORTED, "d %d is not a multiple of 8 in [8, 1024)", a->d);
+    if (a->n < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "n %lld < 0", (long long)a->n);
+    if (a->n * (int64_t)a->d > (int64_t(1) << 31))
+        return fail(HSTU_ERR_UNSUPPORTED, "n * d exceeds 2^31");
+    if (!(a->eps > 0.0f) || !std::isfinite(a->eps)) return fail(HSTU_ERR_INVALID_ARGUMENT, "eps must be positive and finite");
+    if (!std::isfinite(a->dropout_ratio) || a->dropout_ratio < 0.0f || a->dropout_ratio >= 1.0f)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "dropout_ratio must be in [0, 1)");
+    if (a->dropout_ratio != 0.0f) return fail(HSTU_ERR_UNSUPPORTED, "dropout is not built (dropout_ratio must be 0)");
+    std::memset(&p, 0, sizeof(p));
+    p.n = a->n;
+    p.d = a->d;
+    p.segs = 1 + (a->concat_u != 0) + (a->concat_x != 0);
+    p.eps = a->eps;
+    p.inv_d = 1.0f / (float)a->d;
+    p.silu_u = a->apply_u_silu != 0;
+    p.concat_u = a->concat_u != 0;
+    p.concat_x = a->concat_x != 0;
+    return HSTU_OK;
+}
+
+// A (rows, d) bf16 matrix with a row stride (0 = packed `packed`).
+hstu_status_t lmsd_matrix(const char* name, const void* ptr, int64_t stride, int64_t packed, int64_t width,
+                          int64_t rows, int64_t& out) {
+    out = stride == 0 ? packed : stride;
+    if (rows == 0) return HSTU_OK;
+    if (ptr == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "%s is null", name);
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+    if (out < width || out % 8 != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "%s row stride %lld must be >= %lld and a multiple of 8", name,
+                    (long long)out, (long long)width);
+    return HSTU_OK;
+}
+
+hstu_status_t lmsd_vector(const char* name, const void* ptr, int64_t align) {
+    if (ptr == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "%s is null", name);
+    if (reinterpret_cast<uintptr_t>(ptr) % align != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "%s is not %lld-byte aligned", name, (long long)align);
+    return HSTU_OK;
+}
+
+size_t lmsd_workspace(const hstu_lmsd_args_t* a) {
+    if (a->n == 0) return 0;
+    const int parts = hstu::lmsd_bwd_parts(a->n, a->d);
+    const int slices = (parts + hstu::kLmsdSlice - 1) / hstu::kLmsdSlice;
+    return (size_t)(parts + slices) * (size_t)a->d * (a->compute_dweight ? 2u : 1u) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_lmsd_fwd(const hstu_lmsd_args_t* a, const void* x, const void* u, const void* weight,
+                            const void* bias, void* y, float* mean, float* rstd, hipStream_t stream) {
+    hstu::LmsdParams p;
+    hstu_status_t st = lmsd_common(a, p);
+    if (st != HSTU_OK) return st;
+    if (a->n == 0) return ok();
+    int64_t ys;
+    if ((st = lmsd_matrix("x", x, a->x_stride, a->d, a->d, a->n, p.x_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_matrix("u", u, a->u_stride, a->d, a->d, a->n, p.u_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_matrix("y", y, 0, (int64_t)p.segs * a->d, (int64_t)p.segs * a->d, a->n, ys)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("weight", weight, 16)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("bias", bias, 16)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("mean", mean, 4)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("rstd", rstd, 4)) != HSTU_OK) return st;
+    p.x = static_cast<const uint16_t*>(x);
+    p.u = static_cast<const uint16_t*>(u);
+    p.weight = static_cast<const uint16_t*>(weight);
+    p.bias = static_cast<const uint16_t*>(bias);
+    p.y = static_cast<uint16_t*>(y);
+    p.mean = mean;
+    p.rstd = rstd;
+    return launched(hstu::launch_lmsd_fwd(p, stream), "hstu_lmsd_fwd");
+}
+
+hstu_status_t hstu_lmsd_bwd_workspace_size(const hstu_lmsd_args_t* a, size_t* bytes) {
+    if (bytes == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "bytes is null");
+    hstu::LmsdParams p;
+    hstu_status_t st = lmsd_common(a, p);
+    if (st != HSTU_OK) return st;
+    *bytes = lmsd_workspace(a);
+    return ok();
+}
+
+hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const void* x, const void* u,
+                            const void* weight, const void* bias, const float* mean, const float* rstd, void* dx,
+                            void* du, void* dweight, void* dbias, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    hstu::LmsdParams p;
+    hstu_status_t st = lmsd_common(a, p);
+    if (st != HSTU_OK) return st;
+    const size_t need = lmsd_workspace(a);
+    if (workspace_bytes < need)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (need > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is null or not 256-byte aligned");
+    const int64_t sd = (int64_t)p.segs * a->d;
+    if ((st = lmsd_matrix("dy", dy, a->dy_stride, sd, sd, a->n, p.dy_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_matrix("x", x, a->x_stride, a->d, a->d, a->n, p.x_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_matrix("u", u, a->u_stride, a->d, a->d, a->n, p.u_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_matrix("dx", dx, a->dx_stride, a->d, a->d, a->n, p.dx_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_matrix("du", du, a->du_stride, a->d, a->d, a->n, p.du_stride)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("weight", weight, 16)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("bias", bias, 16)) != HSTU_OK) return st;
+    if ((st = lmsd_vector("dbias", dbias, 16)) != HSTU_OK) return st;
+    if (a->compute_dweight && (st = lmsd_vector("dweight", dweight, 16)) != HSTU_OK) return st;
+    if (a->n > 0) {
+        if ((st = lmsd_vector("mean", mean, 4)) != HSTU_OK) return st;
+        if ((st = lmsd_vector("rstd", rstd, 4)) != HSTU_OK) return st;
+    }
+    p.dy = static_cast<const uint16_t*>(dy);
+    p.x = static_cast<const uint16_t*>(x);
+    p.u = static_cast<const uint16_t*>(u);
+    p.weight = static_cast<const uint16_t*>(weight);
+    p.bias = static_cast<const uint16_t*>(bias);
+    p.mean = const_cast<float*>(mean);
+    p.rstd = const_cast<float*>(rstd);
+    p.dx = static_cast<uint16_t*>(dx);
+    p.du = static_cast<uint16_t*>(du);
+    p.dweight = a->compute_dweight ? static_cast<uint16_t*>(dweight) : nullptr;
+    p.dbias = static_cast<uint16_t*>(dbias);
+    p.work = static_cast<float*>(workspace);
+    p.part_stride = (int64_t)a->d * (a->compute_dweight ? 2 : 1);
+    // no rows: only the column-sum kernel runs, over zero partials, and writes zeros
+    return launched(hstu::launch_lmsd_bwd(p, a->n == 0 ? 0 : hstu::lmsd_bwd_parts(a->n, a->d), stream),
+                    "hstu_lmsd_bwd");
 }
 
 const char* hstu_last_error(void) { return g_last_error.c_str(); }

@@ -43,6 +43,10 @@ __all__ = [
     "HSTU_MASK_CAUSAL",
     "HSTU_MASK_WINDOW",
     "HSTU_MASK_FUNC",
+    "HstuLmsdArgs",
+    "lmsd_fwd",
+    "lmsd_bwd",
+    "lmsd_bwd_workspace_size",
 ]
 
 HSTU_OK = 0
@@ -53,7 +57,7 @@ HSTU_MASK_NONE = 0
 HSTU_MASK_CAUSAL = 1
 HSTU_MASK_WINDOW = 2
 HSTU_MASK_FUNC = 3
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -98,6 +102,26 @@ class HstuArgs(ctypes.Structure):
     ]
 
 
+class HstuLmsdArgs(ctypes.Structure):
+    """Mirror of ``hstu_lmsd_args_t`` in include/hstu.h."""
+
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("x_stride", ctypes.c_int64),
+        ("u_stride", ctypes.c_int64),
+        ("dy_stride", ctypes.c_int64),
+        ("dx_stride", ctypes.c_int64),
+        ("du_stride", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("dropout_ratio", ctypes.c_float),
+        ("apply_u_silu", ctypes.c_int32),
+        ("concat_u", ctypes.c_int32),
+        ("concat_x", ctypes.c_int32),
+        ("compute_dweight", ctypes.c_int32),
+    ]
+
+
 class HstuError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{_status_name(status)}: {message}")
@@ -132,6 +156,13 @@ def library() -> ctypes.CDLL:
             lib.hstu_bwd_dq.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_bwd_dkdv.restype = ctypes.c_int
             lib.hstu_bwd_dkdv.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            largp = ctypes.POINTER(HstuLmsdArgs)
+            lib.hstu_lmsd_fwd.restype = ctypes.c_int
+            lib.hstu_lmsd_fwd.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_lmsd_bwd_workspace_size.restype = ctypes.c_int
+            lib.hstu_lmsd_bwd_workspace_size.argtypes = [largp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.hstu_lmsd_bwd.restype = ctypes.c_int
+            lib.hstu_lmsd_bwd.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
             lib.hstu_last_error.restype = ctypes.c_char_p
             lib.hstu_last_error.argtypes = []
             lib.hstu_status_string.restype = ctypes.c_char_p
@@ -333,3 +364,108 @@ def hstu_bwd_dkdv(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
                                    v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(),
                                    _stream(stream, q.device)))
     return dk, dv
+
+
+# ---------------------------------------------------------------------------
+# HSTU LMSD (HSTU LMSD page: hstu_lmsd_forward / hstu_lmsd_backward)
+# ---------------------------------------------------------------------------
+def _rowmat(name: str, t: torch.Tensor, n: Optional[int], d: int) -> int:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bfloat16 tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dim() != 2 or t.shape[1] != d or (n is not None and t.shape[0] != n):
+        raise ValueError(f"{name} must have shape ({n if n is not None else 'N'}, {d}), got {tuple(t.shape)}")
+    if t.shape[0] > 0 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return int(t.stride(0)) if t.shape[0] > 1 else d
+
+
+def _vec(name: str, t: torch.Tensor, d: int, dtype=torch.bfloat16) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != 1 or t.shape[0] != d or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous ({d},) {dtype} tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+
+
+def _lmsd_args(x, u, eps, dropout_ratio, apply_u_silu, concat_u, concat_x, compute_dweight=True) -> HstuLmsdArgs:
+    if x.dim() != 2:
+        raise ValueError("x must be (N, D)")
+    n, d = int(x.shape[0]), int(x.shape[1])
+    a = HstuLmsdArgs()
+    a.n, a.d = n, d
+    a.eps, a.dropout_ratio = float(eps), float(dropout_ratio)
+    a.apply_u_silu, a.concat_u, a.concat_x = int(bool(apply_u_silu)), int(bool(concat_u)), int(bool(concat_x))
+    a.compute_dweight = int(bool(compute_dweight))
+    a.x_stride = _rowmat("x", x, n, d)
+    a.u_stride = _rowmat("u", u, n, d)
+    return a
+
+
+def lmsd_fwd(x: torch.Tensor, u: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, eps: float = 1e-6,
+             dropout_ratio: float = 0.0, apply_u_silu: bool = True, concat_u: bool = True, concat_x: bool = True,
+             y: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None,
+             rstd: Optional[torch.Tensor] = None, stream=None):
+    """(y, mean, rstd): y = [a, x, LayerNorm(x) * a] per row (segments as flagged),
+    a = SiLU(u) or u; mean and rstd are the fp32 row statistics the backward needs."""
+    a = _lmsd_args(x, u, eps, dropout_ratio, apply_u_silu, concat_u, concat_x)
+    n, d = a.n, a.d
+    _vec("weight", weight, d)
+    _vec("bias", bias, d)
+    segs = 1 + a.concat_u + a.concat_x
+    y = torch.empty((n, segs * d), dtype=torch.bfloat16, device=x.device) if y is None else y
+    if y.shape != (n, segs * d) or y.dtype != torch.bfloat16 or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous ({n}, {segs * d}) bfloat16 tensor")
+    mean = torch.empty(n, dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty(n, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _vec("mean", mean, n, torch.float32)
+    _vec("rstd", rstd, n, torch.float32)
+    _check(library().hstu_lmsd_fwd(ctypes.byref(a), x.data_ptr(), u.data_ptr(), weight.data_ptr(), bias.data_ptr(),
+                                   y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), _stream(stream, x.device)))
+    return y, mean, rstd
+
+
+def lmsd_bwd_workspace_size(x, u, eps=1e-6, dropout_ratio=0.0, apply_u_silu=True, concat_u=True, concat_x=True,
+                            compute_dweight=True) -> int:
+    a = _lmsd_args(x, u, eps, dropout_ratio, apply_u_silu, concat_u, concat_x, compute_dweight)
+    need = ctypes.c_size_t(0)
+    _check(library().hstu_lmsd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    return int(need.value)
+
+
+def lmsd_bwd(dy: torch.Tensor, x: torch.Tensor, u: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
+             mean: torch.Tensor, rstd: torch.Tensor, dropout_ratio: float = 0.0, apply_u_silu: bool = True,
+             concat_u: bool = True, concat_x: bool = True, compute_dweight: bool = True, eps: float = 1e-6,
+             dx=None, du=None, dweight=None, dbias=None, workspace=None, stream=None):
+    """(dx, du, dweight or None, dbias) from the upstream gradient dy of y and the
+    forward's saved mean and rstd (the same flags as the forward)."""
+    a = _lmsd_args(x, u, eps, dropout_ratio, apply_u_silu, concat_u, concat_x, compute_dweight)
+    n, d = a.n, a.d
+    segs = 1 + a.concat_u + a.concat_x
+    a.dy_stride = _rowmat("dy", dy, n, segs * d)
+    _vec("weight", weight, d)
+    _vec("bias", bias, d)
+    _vec("mean", mean, n, torch.float32)
+    _vec("rstd", rstd, n, torch.float32)
+    dx = torch.empty((n, d), dtype=torch.bfloat16, device=x.device) if dx is None else dx
+    du = torch.empty((n, d), dtype=torch.bfloat16, device=x.device) if du is None else du
+    a.dx_stride = _rowmat("dx", dx, n, d)
+    a.du_stride = _rowmat("du", du, n, d)
+    dbias = torch.empty(d, dtype=torch.bfloat16, device=x.device) if dbias is None else dbias
+    _vec("dbias", dbias, d)
+    if compute_dweight:
+        dweight = torch.empty(d, dtype=torch.bfloat16, device=x.device) if dweight is None else dweight
+        _vec("dweight", dweight, d)
+    else:
+        dweight = None
+    need = ctypes.c_size_t(0)
+    _check(library().hstu_lmsd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().hstu_lmsd_bwd(ctypes.byref(a), dy.data_ptr(), x.data_ptr(), u.data_ptr(), weight.data_ptr(),
+                                   bias.data_ptr(), mean.data_ptr(), rstd.data_ptr(), dx.data_ptr(), du.data_ptr(),
+                                   dweight.data_ptr() if dweight is not None else None, dbias.data_ptr(), ws_ptr,
+                                   ws_bytes, _stream(stream, x.device)))
+    return dx, du, dweight, dbias

@@ -107,7 +107,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 4
+#define HSTU_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define HSTU_API __attribute__((visibility("default")))
@@ -193,6 +193,66 @@ HSTU_API hstu_status_t hstu_bwd_dkdv(const hstu_args_t* args, const void* dout,
                             const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                             void* dk, void* dv, hipStream_t stream);
+
+/* ==========================================================================
+ * HSTU LMSD: LayerNorm, affine, times SiLU(u) (HSTU LMSD page, "Overview").
+ *
+ * For each of N rows of D values:
+ *     mean = sum x / D,  rstd = 1 / sqrt(sum (x - mean)^2 / D + eps),
+ *     xh = (x - mean) rstd,  l = xh weight + bias,  a = SiLU(u) or u,
+ *     y = [a (if concat_u), x (if concat_x), l a]     (segments of D values)
+ * and the page's explicit backward, from dy and the saved mean and rstd:
+ *     dl = g a,  da = g l (+ the a segment's gradient),  du = da SiLU'(u) or da,
+ *     dx = rstd (dl weight - mean_D(dl weight) - xh mean_D(dl weight xh))
+ *          (+ the x segment's gradient),
+ *     dweight = sum_rows dl xh,  dbias = sum_rows dl,
+ * where g is dy's l a segment.  Dropout is not built: dropout_ratio must be 0
+ * (HSTU_ERR_UNSUPPORTED otherwise; the page fixes no random stream that a
+ * result could be checked against), so no keep mask is produced or read.
+ *
+ * Tensors ("Tensor shapes and layouts" table): x, u, dx, du (N, D) bf16 with
+ * row strides in elements (0 = D), multiples of 8; weight, bias, dweight, dbias
+ * (D) bf16; y (N, S D) bf16 contiguous, S = 1 + concat_u + concat_x; dy (N, S D)
+ * bf16 with row stride dy_stride (0 = S D), a multiple of 8; mean, rstd (N)
+ * fp32.  All device pointers, 16-byte aligned (mean, rstd: 4-byte).  Limits
+ * ("Supported configurations"): N >= 0 with N D <= 2^31, 8 <= D < 1024, D % 8
+ * == 0, eps positive and finite.  Outputs must not overlap inputs or each
+ * other.  Validation, errors, streams and ownership as for attention above;
+ * the backward's workspace (hstu_lmsd_bwd_workspace_size bytes, 256-byte
+ * aligned) holds per-workgroup column partials, so dweight and dbias are
+ * deterministic.  compute_dweight = 0 skips dweight (its pointer may be null).
+ * ========================================================================== */
+typedef struct hstu_lmsd_args {
+    int64_t n;                /* rows N >= 0                                            */
+    int64_t x_stride;         /* row strides in elements; 0 = packed                    */
+    int64_t u_stride;
+    int64_t dy_stride;        /* 0 = S D                                                */
+    int64_t dx_stride;
+    int64_t du_stride;
+    int32_t d;                /* D: 8 <= D < 1024, D % 8 == 0                           */
+    float eps;                /* > 0, finite                                            */
+    float dropout_ratio;      /* must be 0                                              */
+    int32_t apply_u_silu;     /* nonzero: a = SiLU(u); zero: a = u                      */
+    int32_t concat_u;         /* nonzero: y starts with the a segment                   */
+    int32_t concat_x;         /* nonzero: y then has the x segment                      */
+    int32_t compute_dweight;  /* backward: nonzero computes dweight                     */
+} hstu_lmsd_args_t;
+
+/* Forward: y, mean, rstd from x, u, weight, bias. */
+HSTU_API hstu_status_t hstu_lmsd_fwd(const hstu_lmsd_args_t* args, const void* x, const void* u,
+                            const void* weight, const void* bias, void* y, float* mean, float* rstd,
+                            hipStream_t stream);
+
+/* Bytes of device workspace hstu_lmsd_bwd needs (written to *bytes). */
+HSTU_API hstu_status_t hstu_lmsd_bwd_workspace_size(const hstu_lmsd_args_t* args, size_t* bytes);
+
+/* Backward: dx, du, dbias and (if compute_dweight) dweight, from dy, the forward's
+ * inputs and its saved mean and rstd.  Two kernels on `stream`: rows, then the
+ * column sums of the workgroup partials. */
+HSTU_API hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* args, const void* dy, const void* x, const void* u,
+                            const void* weight, const void* bias, const float* mean, const float* rstd,
+                            void* dx, void* du, void* dweight, void* dbias, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 HSTU_API const char* hstu_last_error(void);

@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dq", "hstu_bwd_workspace_size", "hstu_fwd",
-        "hstu_last_error", "hstu_status_string"])
+        "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd", "hstu_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -156,3 +156,55 @@ def test_binding_rejects_host_tensors():
         hstu.hstu_fwd(q, q, q, cu, cu, 4, 4)
     with pytest.raises(TypeError):
         hstu.hstu_fwd(q.float(), q, q, cu, cu, 4, 4)
+
+
+# ---------------------------------------------------------------------------- LMSD
+def test_lmsd_struct_layout():
+    assert ctypes.sizeof(hstu.HstuLmsdArgs) == 6 * 8 + 7 * 4 + 4  # padded to 8 bytes
+    assert hstu.HstuLmsdArgs.d.offset == 48 and hstu.HstuLmsdArgs.compute_dweight.offset == 72
+
+
+def lmsd_args(**kw):
+    a = hstu.HstuLmsdArgs()
+    a.n, a.d, a.eps, a.dropout_ratio = 16, 64, 1e-6, 0.0
+    a.apply_u_silu, a.concat_u, a.concat_x, a.compute_dweight = 1, 1, 1, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+LMSD_REJECT = [
+    ("d 12", dict(d=12), hstu.HSTU_ERR_UNSUPPORTED),
+    ("d 1024", dict(d=1024), hstu.HSTU_ERR_UNSUPPORTED),
+    ("d 0", dict(d=0), hstu.HSTU_ERR_UNSUPPORTED),
+    ("n < 0", dict(n=-1), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("n d above 2^31", dict(n=(1 << 28) + 1, d=8), hstu.HSTU_ERR_UNSUPPORTED),
+    ("eps 0", dict(eps=0.0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("eps inf", dict(eps=float("inf")), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("dropout 0.1", dict(dropout_ratio=0.1), hstu.HSTU_ERR_UNSUPPORTED),
+    ("dropout 1", dict(dropout_ratio=1.0), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("x stride below d", dict(x_stride=56), hstu.HSTU_ERR_INVALID_ARGUMENT),
+    ("u stride not multiple of 8", dict(u_stride=68), hstu.HSTU_ERR_INVALID_ARGUMENT),
+]
+
+
+@pytest.mark.parametrize("desc,over,want", LMSD_REJECT, ids=[r[0] for r in LMSD_REJECT])
+def test_lmsd_rejections(lib, desc, over, want):
+    st = lib.hstu_lmsd_fwd(ctypes.byref(lmsd_args(**over)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == want, (desc, lib.hstu_last_error())
+
+
+def test_lmsd_pointer_and_workspace_rejections(lib):
+    a = lmsd_args()
+    assert lib.hstu_lmsd_fwd(ctypes.byref(a), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_lmsd_fwd(ctypes.byref(a), FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) \
+        == hstu.HSTU_ERR_INVALID_ARGUMENT
+    need = ctypes.c_size_t(0)
+    assert lib.hstu_lmsd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)) == hstu.HSTU_OK
+    assert need.value > 0
+    st = lib.hstu_lmsd_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, need.value - 4, None)
+    assert st == hstu.HSTU_ERR_INVALID_ARGUMENT and b"workspace" in lib.hstu_last_error()
+    half = ctypes.c_size_t(0)
+    assert lib.hstu_lmsd_bwd_workspace_size(ctypes.byref(lmsd_args(compute_dweight=0)), ctypes.byref(half)) == 0
+    assert 2 * half.value == need.value  # no dweight partials
