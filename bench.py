@@ -144,14 +144,24 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
 
     kernels = list(ALG_TENSORS)
     copy = ["copyBuffer"]
-    from generative_recommender_attention_amd.workloads import named_workload
+    from generative_recommender_attention_amd.workloads import lmsd_named_workload, named_workload
 
-    wl = named_workload(workload)
+    if workload.startswith("lmsd_"):
+        lw = lmsd_named_workload(workload)
+        title = "HSTU LMSD fwd + bwd"
+        what = (f"Workload: N={lw.n} rows, D={lw.d}, {lw.segments} output segments (SiLU(u), x, LN(x) SiLU(u)), "
+                "bf16, seeded synthetic inputs; one bench step = hstu_lmsd_fwd + hstu_lmsd_bwd (row kernel, "
+                "column sums).")
+        kernels = ["lmsd_fwd_kernel", "lmsd_bwd_kernel", "lmsd_colsum_kernel"]
+    else:
+        wl = named_workload(workload)
+        title = "HSTU attention fwd + bwd"
+        what = (f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
+                f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
+                "hstu_bwd_dq + hstu_bwd_dkdv.")
     stats = rows("kt", "*kernel_stats.csv")
-    out = [f"# rocprofv3 kernel trace: HSTU attention fwd + bwd, workload {workload}", "",
-           f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
-           f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
-           "hstu_bwd_dq + hstu_bwd_dkdv.", "", "Command (GPU box, from the repository root):",
+    out = [f"# rocprofv3 kernel trace: {title}, workload {workload}", "", what, "",
+           "Command (GPU box, from the repository root):",
            "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir, w=workload), "",
            f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):

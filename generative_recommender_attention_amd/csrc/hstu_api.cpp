@@ -326,8 +326,7 @@ hstu_status_t lmsd_vector(const char* name, const void* ptr, int64_t align) {
 size_t lmsd_workspace(const hstu_lmsd_args_t* a) {
     if (a->n == 0) return 0;
     const int parts = hstu::lmsd_bwd_parts(a->n, a->d);
-    const int slices = (parts + hstu::kLmsdSlice - 1) / hstu::kLmsdSlice;
-    return (size_t)(parts + slices) * (size_t)a->d * (a->compute_dweight ? 2u : 1u) * sizeof(float);
+    return (size_t)parts * (size_t)a->d * (a->compute_dweight ? 2u : 1u) * sizeof(float);
 }
 
 }  // namespace

@@ -24,9 +24,9 @@
 // grid of G workgroups (G fixed by N and D on the host) walks the row groups;
 // each lane accumulates its columns' dweight / dbias terms over its rows in
 // registers, the workgroup sums its waves through LDS and writes one partial
-// row per workgroup to the caller's workspace; two small kernels then add the G
-// partials column by column, first in slices of kLmsdSlice rows (every load of a
-// slice in flight), then the slice sums, each in a fixed order (deterministic).
+// row per workgroup to the caller's workspace; a second kernel adds the G
+// partials column by column, spread over 16 waves per column block, in a fixed
+// order (deterministic).
 #include "hstu_device.h"
 #include "lmsd_kernels.h"
 
@@ -231,39 +231,36 @@ __global__ __launch_bounds__(256) void lmsd_bwd_kernel(LmsdParams p) {
     }
 }
 
-// dbias / dweight, first level: slice s of kLmsdSlice partial rows, column c
-// (one lane per column, every load of the slice in flight at once) -> sum row s
-// after the parts rows of the workspace.
-__global__ __launch_bounds__(64) void lmsd_colsum_slices_kernel(LmsdParams p, int parts) {
-    const int c = blockIdx.x * 64 + threadIdx.x;
-    const int s = blockIdx.y;
+// dbias / dweight: column c of the partial rows (c < d: dbias, else dweight
+// column c - d) is summed by one lane of each of the 16 waves of a workgroup --
+// wave w takes the rows j = w (mod 16) in increasing order, eight loads in
+// flight -- and the 16 wave sums are added in wave order through LDS.
+__global__ __launch_bounds__(1024) void lmsd_colsum_kernel(LmsdParams p, int parts) {
+    __shared__ float red[16][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
     const int pw = (int)p.part_stride;  // d, or 2 d with dweight
-    if (c >= pw) return;
-    const int j0 = s * kLmsdSlice, j1 = min(parts, j0 + kLmsdSlice);
-    float acc[kLmsdSlice];
+    float acc = 0.0f;
+    if (c < pw) {
+        int j = w;
+        for (; j + 7 * 16 < parts; j += 8 * 16) {
+            float v[8];
 #pragma unroll
-    for (int j = 0; j < kLmsdSlice; ++j) acc[j] = j0 + j < j1 ? p.work[(int64_t)(j0 + j) * pw + c] : 0.0f;
+            for (int t = 0; t < 8; ++t) v[t] = p.work[(int64_t)(j + 16 * t) * pw + c];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc += v[t];
+        }
+        for (; j < parts; j += 16) acc += p.work[(int64_t)j * pw + c];
+    }
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w != 0 || c >= pw) return;
     float sum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kLmsdSlice; ++j) sum += acc[j];
-    p.work[(int64_t)(parts + s) * pw + c] = sum;
-}
-
-// Second level: column c is the sum of the slice sums, in order; rounded to bf16.
-__global__ __launch_bounds__(256) void lmsd_colsum_final_kernel(LmsdParams p, int parts) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= p.d) return;
-    const int pw = (int)p.part_stride;
-    const int slices = (parts + kLmsdSlice - 1) / kLmsdSlice;
-    float sb = 0.0f, sw = 0.0f;
-    for (int s = 0; s < slices; ++s) {
-        const float* row = p.work + (int64_t)(parts + s) * pw;
-        sb += row[c];
-        if (p.dweight) sw += row[p.d + c];
-    }
-    const uint32_t wb = pack_bf16x2(sb, sw);
-    p.dbias[c] = (uint16_t)(wb & 0xffffu);
-    if (p.dweight) p.dweight[c] = (uint16_t)(wb >> 16);
+    for (int i = 0; i < 16; ++i) sum += red[i][lane];
+    const uint32_t h = pack_bf16x2(sum, 0.0f) & 0xffffu;
+    if (c < p.d) p.dbias[c] = (uint16_t)h;
+    else p.dweight[c - p.d] = (uint16_t)h;
 }
 
 template <int LPR, int VPL>
@@ -278,13 +275,9 @@ hipError_t launch_pair(const LmsdParams& p, bool bwd, int parts, hipStream_t str
         hipLaunchKernelGGL((lmsd_bwd_kernel<LPR, VPL>), dim3((unsigned)parts), dim3(256), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const unsigned slices = (unsigned)((parts + kLmsdSlice - 1) / kLmsdSlice);
-        hipLaunchKernelGGL(lmsd_colsum_slices_kernel, dim3((unsigned)((p.part_stride + 63) / 64), slices), dim3(64), 0,
-                           stream, p, parts);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(lmsd_colsum_final_kernel, dim3((unsigned)((p.d + 255) / 256)), dim3(256), 0, stream, p, parts);
+    hipLaunchKernelGGL(lmsd_colsum_kernel, dim3((unsigned)((p.part_stride + 63) / 64)), dim3(1024), 0, stream, p,
+                       parts);
     return hipGetLastError();
 }
 

@@ -30,14 +30,12 @@ struct LmsdParams {
     int64_t dx_stride, du_stride;
     uint16_t* dweight;         // (d) bf16, or null when not computed
     uint16_t* dbias;           // (d) bf16
-    float* work;               // parts + slices rows of part_stride fp32: [dbias partial | dweight partial]
+    float* work;               // parts rows of part_stride fp32: [dbias partial | dweight partial]
     int64_t part_stride;
 };
 
-// Largest number of workgroup partials of the backward's column sums, and the
-// rows one first-level column-sum slice adds.
+// Largest number of workgroup partials of the backward's column sums.
 constexpr int kLmsdMaxParts = 1024;
-constexpr int kLmsdSlice = 16;
 
 // Workgroups (= partial rows) the backward launches for n rows of d values.
 int lmsd_bwd_parts(int64_t n, int d);
