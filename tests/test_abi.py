@@ -208,3 +208,27 @@ def test_lmsd_pointer_and_workspace_rejections(lib):
     half = ctypes.c_size_t(0)
     assert lib.hstu_lmsd_bwd_workspace_size(ctypes.byref(lmsd_args(compute_dweight=0)), ctypes.byref(half)) == 0
     assert 2 * half.value == need.value  # no dweight partials
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: with the library missing, the binding raises instead of computing."""
+    import torch
+
+    monkeypatch.setattr(hstu, "_lib", None)
+    monkeypatch.setattr(hstu, "library_path", lambda: str(tmp_path / "libhstu.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        hstu.library()
+    q = torch.zeros(4, 1, 16, dtype=torch.bfloat16)
+    with pytest.raises((RuntimeError, ValueError)):
+        hstu.hstu_fwd(q, q, q, torch.tensor([0, 4], dtype=torch.int32), torch.tensor([0, 4], dtype=torch.int32), 4, 4)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package and the binding import nothing from oracle/ (test infrastructure only)."""
+    import pathlib
+
+    pkg = pathlib.Path(ROOT) / "generative_recommender_attention_amd"
+    for path in list(pkg.glob("*.py")) + list((pkg / "csrc").glob("*")):
+        text = path.read_text(errors="replace")
+        assert "import oracle" not in text and "from oracle" not in text, path
+        assert "hstu_oracle" not in text and "lmsd_oracle" not in text, path
