@@ -112,7 +112,11 @@ PROFILE_COMMANDS = {
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cfetch -o run -- python3 bench.py --calibrate-copy-mib 256",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cwrite -o run -- python3 bench.py --calibrate-copy-mib 256",
+    "mfma": ("rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS "
+             "SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv "
+             "-d {d}/mfma -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}"),
 }
+MFMA_FLOPS = 2 * 32 * 32 * 16  # one v_mfma_f32_32x32x16_bf16 (the only MFMA the attention kernels issue)
 ALG_TENSORS = {"fwd_kernel": 4, "bwd_dq_kernel": 5, "bwd_dkdv_kernel": 6}  # (T, H, D) bf16 tensors read + written
 
 
@@ -171,6 +175,41 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
                    f"{float(r['MaxNs']):11.0f}{float(r['Percentage']):7.1f}%")
     with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(out) + "\n")
+    if os.path.isdir(os.path.join(prof_dir, "mfma")) and not workload.startswith("lmsd_"):
+        avg_ns = {k: float(r["AverageNs"]) for r in stats for k in kernels if k in r["Name"]}
+        ctr = {}
+        for r in rows("mfma", "*counter_collection.csv"):
+            name = next((k for k in kernels if k in r["Kernel_Name"]), None)
+            if name and "<128," in r["Kernel_Name"]:
+                ctr.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        mean = {k: {c: float(np.mean(v)) for c, v in d.items()} for k, d in ctr.items()}
+        m = [f"# rocprofv3 MFMA / VALU / LDS counters per dispatch, workload {workload}", "",
+             "Command (GPU box, repository root; one pass, 8 SQ counters and GRBM_GUI_ACTIVE):",
+             "    " + PROFILE_COMMANDS["mfma"].format(d=prof_dir, w=workload), "",
+             "Executed MFMA flops = SQ_INSTS_MFMA x 32768 (every MFMA the kernels issue is "
+             "v_mfma_f32_32x32x16_bf16); utilisation against the dense bf16 peak (2500 TFLOP/s) uses",
+             "the kernel's average duration from the kernel trace of the same workload.", "",
+             "MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES), the fraction of the cycles in which a",
+             "CU was busy that a SIMD's matrix core was busy (the MFMA counter sums the 4 SIMDs of a CU).", "",
+             f"{'kernel':18s}{'MFMA insts':>12s}{'exec TFLOP':>11s}{'avg us':>9s}{'exec TF/s':>10s}{'of peak':>9s}"
+             f"{'MFMA busy':>11s}{'VALU/MFMA':>10s}{'LDS/MFMA':>9s}{'bank confl/LDS':>15s}"]
+        for k in kernels:
+            if k not in mean or k not in avg_ns:
+                continue
+            c = mean[k]
+            flops = c["SQ_INSTS_MFMA"] * MFMA_FLOPS
+            tfs = flops / (avg_ns[k] * 1e-9) / 1e12
+            m.append(f"{k:18s}{c['SQ_INSTS_MFMA']:12.4g}{flops / 1e12:11.3f}{avg_ns[k] / 1e3:9.1f}{tfs:10.1f}"
+                     f"{tfs / PEAK_BF16_TFLOPS:9.1%}{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * c['SQ_BUSY_CU_CYCLES']):11.1%}"
+                     f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:10.2f}{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:9.2f}"
+                     f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1):15.3f}")
+        m += ["", "Raw means per dispatch:"]
+        for k in kernels:
+            if k in mean:
+                m.append(f"  {k}: " + ", ".join(f"{c}={v:.4g}" for c, v in sorted(mean[k].items())))
+        with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_mfma_counters.txt"), "w") as f:
+            f.write("\n".join(m) + "\n")
+        print(f"wrote the MFMA counter summary for {workload}")
     if not os.path.isdir(os.path.join(prof_dir, "fetch")):
         print(f"wrote the kernel-trace summary for {workload} (no PMC passes under {prof_dir})")
         return
