@@ -14,8 +14,8 @@
 // final store.
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
-// same tile walk and mask handling as the forward, two workgroups per CU (so the exponent work of
-// one overlaps the products of the other).  Per 64-key tile K and V are staged
+// same tile walk and mask handling as the forward, two workgroups per CU (so the
+// exponent work of one overlaps the products of the other).  Per 64-key tile K and V are staged
 // row-major in LDS; each wave computes S^T = K Q^T and dA^T = V dO^T (A operands:
 // K, V rows), forms dS^T in registers and accumulates dQ^T += K^T dS^T (A
 // operand: K read transposed).
@@ -29,7 +29,12 @@
 // the sequence (rows before it see none of these keys); under a token window
 // (left, right) they walk rows [first key - right, last key + left], the rows
 // whose band meets the block, and each wave tests per 32-row block whether the
-// band covers, misses or cuts it, as the forward does.  Per 64-row query tile
+// band covers, misses or cuts it, as the forward does.  Under the arbitrary
+// interval mask they walk the rows between the first and the last row of the
+// sequence that sees a key of the block (a scan of its rows' endpoints), and
+// 256 threads turn each query tile's endpoints into 64 x 4 visibility words in
+// LDS (32 keys each, double-buffered beside the tile) that each wave reads to
+// classify its 32-row block and, when cut, to test each score.  Per 64-row query tile
 // Q and dO are staged row-major; each wave computes S = Q K^T and dA = dO V^T
 // (A operands: Q, dO rows; B operands: K, V rows), forms A' and dS in registers
 // and accumulates dV^T += dO^T A' and dK^T += Q^T dS (A operands: dO, Q read

@@ -18,7 +18,11 @@
 // two tiles; a token window (left, right) walks the tiles that meet the band of
 // its rows, [first row - left, last row + right], and each wave decides per tile
 // whether the band covers the tile for all its rows (no test), misses it for all
-// (skip) or cuts it (test each score against the row's own interval).
+// (skip) or cuts it (test each score against the row's own interval).  The
+// arbitrary interval mask walks the tiles between the smallest and the largest
+// visible key of the block's rows; per tile each lane forms its row's 64-bit
+// key mask from the row's endpoints, and two ballots over the wave's live rows
+// choose skip, no test, or a bit test per score.
 //
 // K and V tiles (64 keys x D, row-major, swizzled) are staged into LDS with
 // direct global->LDS loads issued from inline assembly, double-buffered: the
