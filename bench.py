@@ -78,15 +78,27 @@ def workload_pairs(wl) -> int:
     return visible_pairs(wl.lengths_q, wl.lengths_k, wl.window_size)
 
 
+def _code_only(text: str) -> str:
+    """C/C++/HIP source with comments removed and whitespace collapsed, so that a
+    comment edit does not count as a kernel change."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest() -> str:
-    """Digest of the kernel sources and of the build script that sets their compile flags."""
+    """Digest of the kernel sources (code only) and of the build script that sets
+    their compile flags."""
     pkg = os.path.join(ROOT, "generative_recommender_attention_amd")
     csrc = os.path.join(pkg, "csrc")
-    files = [os.path.join(csrc, name) for name in sorted(os.listdir(csrc))] + [os.path.join(pkg, "build.py")]
     h = hashlib.sha256()
-    for path in files:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), encoding="utf-8", errors="replace") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(b"build.py\0" + f.read())
     return h.hexdigest()[:16]
 
 

@@ -53,3 +53,9 @@ def test_func_pairs_match_window_and_random_brute_force():
             want += len(keys)
         r0 += lq
     assert bench.func_visible_pairs(f, lens_q, lens_k) == want
+
+
+def test_source_digest_ignores_comments():
+    code = "int f(int x) { // add one\n  return x + 1; /* done */ }\n"
+    assert bench._code_only(code) == bench._code_only("int f(int x) {\n return x + 1; }")
+    assert bench._code_only(code) != bench._code_only("int f(int x) { return x + 2; }")
