@@ -108,6 +108,25 @@ def test_random_shapes_fwd_bwd(oracle_lib, case):
     run_bwd_check(wl)
 
 
+@pytest.mark.parametrize("mask", ["causal", "full", "window", "func"])
+def test_more_than_64_sequences(oracle_lib, mask):
+    """B > 64: the live-block numbering sums the sequences' block counts over
+    several 64-sequence chunks; zero-length sequences sit in every chunk."""
+    rng = np.random.default_rng(170)
+    lens = rng.integers(0, 300, size=150)
+    lens[::17] = 0
+    lens[5] = 700
+    if mask == "func":
+        f = func_random_mask(np.random.default_rng(171), lens, lens, 3)
+        wl = make_workload("b150f", 172, lens, 2, 64, False, 1.0, with_do=True, func=f)
+    elif mask == "window":
+        wl = make_workload("b150w", 173, lens, 2, 64, False, 1.0, with_do=True, window=(40, 7))
+    else:
+        wl = make_workload("b150", 174, lens, 2, 64, mask == "causal", 1.0, with_do=True)
+    run_fwd_check(wl)
+    run_bwd_check(wl)
+
+
 def test_explicit_scaling_seqlen_and_alpha(oracle_lib):
     wl = make_workload("ls", 110, [90, 33], 2, 64, True, 1.0, with_do=True, alpha=0.3, scaling_seqlen=7)
     run_fwd_check(wl)
