@@ -266,6 +266,41 @@ def test_func_invalid_arguments_raise():
         dw.fwd(func=torch.zeros(1, 10, dtype=torch.int32, device="cuda"), window_size=(1, 1))
 
 
+# ------------------------------------------------------------------ limits and degenerate cases
+def test_alpha_zero_gives_exact_zeros():
+    """alpha = 0: every score is 0 and SiLU(0) = 0, so O, dV, dQ and dK are exactly 0."""
+    wl = make_workload("a0", 180, [70, 150, 1], 2, 64, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    say("alpha = 0")
+    o = dw.fwd(alpha=0.0)
+    dq, dk, dv = dw.bwd(alpha=0.0)
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.all(t == 0), name
+
+
+def test_largest_token_stride(oracle_lib):
+    """A key tensor with the largest token stride the library accepts (2^24 elements):
+    the 64-row tile copies address it with 32-bit byte offsets up to 2 (63 * 2^24 + 120)."""
+    wl = make_workload("maxstride", 181, [100, 30], 1, 16, True, 1.0, with_do=True)
+    dw = DeviceWorkload(wl)
+    stride = 1 << 24
+    say(f"largest token stride: k viewed with token stride {stride} ({wl.total_k * stride * 2 / 2**30:.1f} GiB)")
+    big = torch.zeros(wl.total_k * stride, dtype=torch.bfloat16, device="cuda")
+    k_view = big.as_strided((wl.total_k, 1, 16), (stride, 16, 1))
+    k_view.copy_(dw.k)
+    kw = dw.kw()
+    o = hstu.hstu_fwd(dw.q, k_view, dw.v, dw.cu_q, dw.cu_k, **kw)
+    dq, dk, dv = hstu.hstu_bwd(dw.do, dw.q, k_view, dw.v, dw.cu_q, dw.cu_k, **kw)
+    torch.cuda.synchronize()
+    del big
+    check_close("O", to_f64(o), oracle.fwd_workload(wl), wl.cu_seqlens_q)
+    rq, rk, rv = oracle.bwd_workload(wl)
+    check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q)
+    check_close("dK", to_f64(dk), rk, wl.cu_seqlens_k)
+    check_close("dV", to_f64(dv), rv, wl.cu_seqlens_k)
+
+
 # ------------------------------------------------------------------ invariants
 def test_zero_queries_give_exact_zeros():
     wl = make_workload("zq", 120, [70, 150], 2, 128, True, with_do=True)
