@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark: HSTU attention forward + backward on one MI355X.
 
-One step = the whole path over one batch of synthetic input: hstu_fwd,
-hstu_bwd_dq, hstu_bwd_dkdv (all three launched through the C ABI on the current
-stream).  Default workload: B=32 sequences with Zipf(1.2) lengths clipped to
-[16, 4096] (T = 23460), H=4, D=128, causal, bf16, plus an upstream gradient.
+One step = the whole path over one batch of synthetic input, launched through
+the C ABI on the current stream: hstu_fwd, then the backward as hstu_bwd runs it
+-- under no mask or the causal mask hstu_bwd_dkdv_ds (dK, dV, and dS stored in a
+workspace allocated before the timed region) then hstu_bwd_dq_ds; under the
+other masks, or with --recompute-dq, hstu_bwd_dq then hstu_bwd_dkdv.  Default
+workload: B=32 sequences with Zipf(1.2) lengths clipped to [16, 4096]
+(T = 23460), H=4, D=128, causal, bf16, plus an upstream gradient.
 
 Metric: useful TFLOP/s = useful flops / time, counting only visible (query,
 key) pairs P: forward 4*D*H*P, backward 10*D*H*P (five matmul-equivalents,
@@ -36,10 +39,19 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "zipf_b32_h4_d128_causal_fwdbwd"
 # Algorithmic flops per visible (query, key) pair and head, per unit of D:
 # forward: S (2) + A.V (2); dq kernel: S (2) + dO.V^T (2) + dS.K (2);
-# dk/dv kernel: S (2) + dO.V^T (2) + A^T.dO (2) + dS^T.Q (2).
-FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+# dk/dv kernel: S (2) + dO.V^T (2) + A^T.dO (2) + dS^T.Q (2) (also when it stores
+# dS); dq from stored dS: dS.K (2).
+FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8, "bwd_dkdv_ds": 8, "bwd_dq_ds": 2}
 USEFUL_PER_PAIR_D = {"fwd": 4, "bwd": 10}
-KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel"}
+KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                 "bwd_dkdv_ds": "bwd_dkdv_kernel", "bwd_dq_ds": "bwd_dq_ds_kernel"}
+
+
+def dq_ds_bytes(wl, pairs: int) -> int:
+    """Algorithmic HBM bytes of one dq-from-stored-dS launch: the bf16 dS of every
+    visible pair and head, K read once and dQ written once."""
+    h, d = wl.num_heads, wl.head_dim
+    return 2 * h * pairs + 2 * h * d * (wl.total_k + wl.total_q)
 
 
 def visible_pairs(lengths_q, lengths_k, window) -> int:
@@ -130,6 +142,17 @@ PROFILE_COMMANDS = {
 }
 MFMA_FLOPS = 2 * 32 * 32 * 16  # one v_mfma_f32_32x32x16_bf16 (the only MFMA the attention kernels issue)
 ALG_TENSORS = {"fwd_kernel": 4, "bwd_dq_kernel": 5, "bwd_dkdv_kernel": 6}  # (T, H, D) bf16 tensors read + written
+PROFILED_KERNELS = ["fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_dq_ds_kernel"]
+
+
+def alg_bytes(kernel: str, wl, pairs: int, stored: bool) -> int:
+    """Algorithmic HBM bytes of one launch: each (T, H, D) bf16 tensor the kernel
+    reads or writes once, plus the bf16 dS of every visible pair and head that the
+    dk/dv kernel stores (stored route) or the dq kernel reads back."""
+    tensor = wl.total_q * wl.num_heads * wl.head_dim * 2
+    if kernel == "bwd_dq_ds_kernel":
+        return dq_ds_bytes(wl, pairs)
+    return ALG_TENSORS[kernel] * tensor + (2 * wl.num_heads * pairs if stored and kernel == "bwd_dkdv_kernel" else 0)
 
 
 def summarize_profiles(prof_dir: str, workload: str) -> None:
@@ -158,7 +181,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
                 vals.setdefault(name, []).append(float(r["Counter_Value"]))
         return {k: float(np.mean(v)) for k, v in vals.items()}
 
-    kernels = list(ALG_TENSORS)
+    kernels = list(PROFILED_KERNELS)
     copy = ["copyBuffer"]
     from generative_recommender_attention_amd.workloads import lmsd_named_workload, named_workload
 
@@ -172,9 +195,11 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     else:
         wl = named_workload(workload)
         title = "HSTU attention fwd + bwd"
+        stored = wl.mask_name in ("causal", "none")
         what = (f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
-                f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + "
-                "hstu_bwd_dq + hstu_bwd_dkdv.")
+                f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + " +
+                ("hstu_bwd_dkdv_ds (bwd_dkdv_kernel storing dS) + hstu_bwd_dq_ds." if stored else
+                 "hstu_bwd_dq + hstu_bwd_dkdv."))
     stats = rows("kt", "*kernel_stats.csv")
     out = [f"# rocprofv3 kernel trace: {title}, workload {workload}", "", what, "",
            "Command (GPU box, from the repository root):",
@@ -230,6 +255,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     copy_kib = 256 * 1024.0
     ff, wf = copy_kib / cfetch["copyBuffer"], copy_kib / cwrite["copyBuffer"]
     tensor_bytes = wl.total_q * wl.num_heads * wl.head_dim * 2
+    pairs = workload_pairs(wl)
     traffic = {"source_digest": kernel_source_digest(), "workload": workload, "fetch_factor": ff, "write_factor": wf,
                "kernels": {}}
     lines = [f"# HBM traffic per dispatch (rocprofv3 PMC), workload {workload}", "",
@@ -240,14 +266,17 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
               f"{'':48s}WRITE_SIZE reads {cwrite['copyBuffer']:.1f} KiB -> write factor {wf:.4f}", "",
               f"{'kernel':18s}{'FETCH KiB':>12s}{'WRITE KiB':>12s}{'HBM MB (scaled)':>18s}{'algorithmic MB':>16s}{'ratio':>8s}"]
     for k in kernels:
+        if k not in fetch or k not in write:
+            continue
         hbm = (fetch[k] * ff + write[k] * wf) * 1024.0
-        alg = ALG_TENSORS[k] * tensor_bytes
+        alg = alg_bytes(k, wl, pairs, stored)
         traffic["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write[k], "hbm_bytes_per_launch": int(hbm),
                                  "algorithmic_bytes_per_launch": alg}
         lines.append(f"{k:18s}{fetch[k]:12.1f}{write[k]:12.1f}{hbm / 1e6:18.1f}{alg / 1e6:16.1f}{hbm / alg:8.2f}")
     lines += ["", "Algorithmic bytes: fwd reads q, k, v and writes o (4 tensors); dq kernel reads q, do, k, v and",
-              "writes dq (5); dk/dv kernel reads q, do, k, v and writes dk, dv (6); each tensor T*H*D*2 = "
-              f"{tensor_bytes} bytes."]
+              "writes dq (5); dk/dv kernel reads q, do, k, v and writes dk, dv (6), and on the stored-dS route",
+              "also writes 2 bytes of dS per visible pair and head; the dq-from-dS kernel reads that dS and k and",
+              f"writes dq; each tensor T*H*D*2 = {tensor_bytes} bytes, {pairs} visible pairs per head."]
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
     with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_hbm_traffic.txt"), "w") as f:
@@ -401,6 +430,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute-dq", action="store_true",
+                    help="time the backward route without stored dS (hstu_bwd_dq + hstu_bwd_dkdv)")
     ap.add_argument("--cpu-max-pairs", type=int, default=0,
                     help="bound on the oracle sample in visible pairs per head (0: the whole workload, "
                          "about 15 s on 16 host threads for the default workload)")
@@ -461,7 +492,13 @@ def main(argv=None) -> int:
               scaling_seqlen=wl.scaling_seqlen, causal=wl.causal, window_size=wl.window,
               func=torch.from_numpy(wl.func).to(dev) if wl.func is not None else None)
     stream = torch.cuda.current_stream(dev)
-    kernels = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if has_bwd else [])
+    ws_bytes = hstu.hstu_bwd_workspace_size(do, q, k, v, cu_q, cu_k, **kw) if has_bwd else 0
+    stored = has_bwd and ws_bytes > 0 and not args.recompute_dq
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if stored else None
+    if stored:
+        print(f"[bench] backward through stored dS: workspace {ws_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
+    kernels = ["fwd"] + ((["bwd_dkdv_ds", "bwd_dq_ds"] if stored else ["bwd_dq", "bwd_dkdv"]) if has_bwd else [])
+    dskw = {key: val for key, val in kw.items() if key != "func"}
 
     def step(events=None):
         if events is not None:
@@ -469,7 +506,14 @@ def main(argv=None) -> int:
         hstu.hstu_fwd(q, k, v, cu_q, cu_k, out=o, stream=stream, **kw)
         if events is not None:
             events[1].record(stream)
-        if has_bwd:
+        if stored:
+            hstu.hstu_bwd_dkdv_ds(do, q, k, v, cu_q, cu_k, ds=ws, dk=dk, dv=dv, stream=stream, **dskw)
+            if events is not None:
+                events[2].record(stream)
+            hstu.hstu_bwd_dq_ds(q, k, cu_q, cu_k, ds=ws, dq=dq, stream=stream, **dskw)
+            if events is not None:
+                events[3].record(stream)
+        elif has_bwd:
             hstu.hstu_bwd_dq(do, q, k, v, cu_q, cu_k, dq=dq, stream=stream, **kw)
             if events is not None:
                 events[2].record(stream)
@@ -512,6 +556,10 @@ def main(argv=None) -> int:
         tf = f / (per_kernel_ms[name] * 1e-3) / 1e12
         detail[name] = {"ms": round(per_kernel_ms[name], 5), "alg_tflops": round(tf, 2),
                         "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if name == "bwd_dq_ds":  # a stream of stored dS: its HBM rate is the telling figure
+            gbs = dq_ds_bytes(wl, pairs) / (per_kernel_ms[name] * 1e-3) / 1e9
+            detail[name].update({"alg_bytes": dq_ds_bytes(wl, pairs), "alg_gbs": round(gbs, 1),
+                                 "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
     fwd_useful_tf = USEFUL_PER_PAIR_D["fwd"] * unit_pd / (per_kernel_ms["fwd"] * 1e-3) / 1e12
     result = {
         "metric": "HSTU attn fwd/bwd useful TFLOP/s @H=4,D=128 causal jagged; % of BF16 MFMA peak",
@@ -529,7 +577,9 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "batch": wl.batch, "total_tokens": wl.total_q,
                    "heads": wl.num_heads, "head_dim": wl.head_dim, "mask": wl.mask_name,
                    "max_seqlen": wl.max_seqlen_q, "visible_pairs_per_head": pairs,
-                   "useful_flops_per_step": useful, "parallelism": "single GPU"},
+                   "useful_flops_per_step": useful, "parallelism": "single GPU",
+                   "backward": "stored dS" if stored else "recompute" if has_bwd else None,
+                   "workspace_bytes": ws_bytes if stored else 0},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_useful_tflops": round(fwd_useful_tf, 2),
         "fwd_frac_of_peak": round(fwd_useful_tf / PEAK_BF16_TFLOPS, 4),

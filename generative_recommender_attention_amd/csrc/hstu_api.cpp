@@ -184,11 +184,71 @@ hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, cons
     return launched(hstu::launch_bwd_dq(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq");
 }
 
-hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
-                       const int32_t* cu_q, const int32_t* cu_k, void* dk, void* dv, hipStream_t stream) {
+// Bytes of stored dS for validated args: 0 unless the mask is none or causal (and
+// both sides have tokens); else one 2 KB block per (head, row-block slot, key group).
+hstu_status_t ds_bytes(const hstu_args_t& a, size_t& bytes) {
+    bytes = 0;
+    const hstu::MaskKind mk = mask_kind(a);
+    if ((mk != hstu::MaskKind::None && mk != hstu::MaskKind::Causal) || a.total_q == 0 || a.total_k == 0)
+        return HSTU_OK;
+    const int64_t nb = ((int64_t)a.total_q + 31 * (int64_t)a.batch) / 32;
+    const int64_t kg = 4 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN);
+    // the dq kernel addresses a row block's groups by 32-bit byte offsets
+    if (kg * 2 * hstu::kDsBlockElems > (int64_t)hstu::kMaxDsRowBlockBytes) return HSTU_OK;
+    const double approx = (double)a.num_heads * (double)nb * (double)kg * 2.0 * hstu::kDsBlockElems;
+    if (approx > 9.0e18)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "stored dS would need %.3g bytes", approx);
+    bytes = (size_t)a.num_heads * (size_t)nb * (size_t)kg * 2 * hstu::kDsBlockElems;
+    return HSTU_OK;
+}
+
+// Checks a dS workspace against the args and points the parameter block at it.
+hstu_status_t bind_ds(const hstu_args_t& a, void* ds, size_t ds_bytes_given, hstu::AttnParams& p) {
+    const hstu::MaskKind mk = mask_kind(a);
+    if (mk != hstu::MaskKind::None && mk != hstu::MaskKind::Causal)
+        return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs the full or causal mask");
+    if (8 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN) * hstu::kDsBlockElems >
+        (int64_t)hstu::kMaxDsRowBlockBytes)
+        return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs max_seqlen_k below 2^25");
+    size_t need = 0;
+    hstu_status_t st = ds_bytes(a, need);
+    if (st != HSTU_OK) return st;
+    if (ds_bytes_given < need)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "dS workspace of %zu bytes < %zu needed", ds_bytes_given, need);
+    if (need > 0 && (ds == nullptr || reinterpret_cast<uintptr_t>(ds) % 256 != 0))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "dS workspace is null or not 256-byte aligned");
+    p.ds = static_cast<uint16_t*>(ds);
+    p.ds_nb = ((int64_t)a.total_q + 31 * (int64_t)a.batch) / 32;
+    p.ds_kg = 4 * (int32_t)(((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN);
+    return HSTU_OK;
+}
+
+// dQ from stored dS: reads k and the workspace only.
+hstu_status_t run_dq_ds(const hstu_args_t* a, const void* k, const int32_t* cu_q, const int32_t* cu_k, void* ds,
+                        size_t ds_given, void* dq, hipStream_t stream) {
     hstu::AttnParams p;
     hstu_status_t st = check_common(a, cu_q, cu_k, p);
     if (st != HSTU_OK) return st;
+    Operand ops[] = {{"k", k, a->k, a->total_k}, {"dq", dq, a->dq, a->total_q}};
+    for (Operand& o : ops)
+        if ((st = check_operand(*a, o)) != HSTU_OK) return st;
+    if ((st = bind_ds(*a, ds, ds_given, p)) != HSTU_OK) return st;
+    p.k = ref(ops[0]);
+    p.dq = out(ops[1]);
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if (a->total_q == 0) return ok();
+    // with no keys the kernel writes dQ = 0 without touching the (empty) workspace
+    return launched(hstu::launch_bwd_dq_ds(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq_ds");
+}
+
+// dK and dV; with `store_ds`, the kernel also stores dS in the workspace `ds`.
+hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                       const int32_t* cu_q, const int32_t* cu_k, void* dk, void* dv, hipStream_t stream,
+                       bool store_ds = false, void* ds = nullptr, size_t ds_given = 0) {
+    hstu::AttnParams p;
+    hstu_status_t st = check_common(a, cu_q, cu_k, p);
+    if (st != HSTU_OK) return st;
+    if (store_ds && (st = bind_ds(*a, ds, ds_given, p)) != HSTU_OK) return st;
     Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q},
                      {"k", k, a->k, a->total_k},          {"v", v, a->v, a->total_k},
                      {"dk", dk, a->dk, a->total_k},       {"dv", dv, a->dv, a->total_k}};
@@ -242,9 +302,27 @@ hstu_status_t hstu_bwd_dkdv(const hstu_args_t* a, const void* dout, const void* 
     return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream);
 }
 
+hstu_status_t hstu_bwd_dkdv_ds(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dk, void* dv,
+                               void* ds, size_t ds_bytes_given, hipStream_t stream) {
+    return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream, true, ds, ds_bytes_given);
+}
+
+hstu_status_t hstu_bwd_dq_ds(const hstu_args_t* a, const void* k, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, const void* ds, size_t ds_bytes_given, void* dq,
+                             hipStream_t stream) {
+    return run_dq_ds(a, k, cu_seqlens_q, cu_seqlens_k, const_cast<void*>(ds), ds_bytes_given, dq, stream);
+}
+
 hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* a, size_t* bytes) {
     if (a == nullptr || bytes == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args or bytes is null");
-    *bytes = 0;  // the two-kernel backward keeps everything in registers and LDS
+    hstu::AttnParams p;
+    const int32_t zero[1] = {0};
+    hstu_status_t st = check_common(a, zero, zero, p);  // scalar checks only; the pointers are not used
+    if (st != HSTU_OK) return st;
+    size_t n = 0;
+    if ((st = ds_bytes(*a, n)) != HSTU_OK) return st;
+    *bytes = n;
     return ok();
 }
 
@@ -256,11 +334,12 @@ hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, co
     hstu_status_t st = check_common(a, cu_seqlens_q, cu_seqlens_k, p);
     if (st != HSTU_OK) return st;
     size_t need = 0;
-    if ((st = hstu_bwd_workspace_size(a, &need)) != HSTU_OK) return st;
-    if (workspace_bytes < need)
+    if ((st = ds_bytes(*a, need)) != HSTU_OK) return st;
+    const bool stored = need > 0 && workspace != nullptr;  // else dQ recomputes the scores
+    if (stored && workspace_bytes < need)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
-    if (need > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
-        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is null or not 256-byte aligned");
+    if (stored && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q},
                      {"k", k, a->k, a->total_k},          {"v", v, a->v, a->total_k},
                      {"dq", dq, a->dq, a->total_q},       {"dk", dk, a->dk, a->total_k},
@@ -270,6 +349,12 @@ hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, co
     if (a->total_k > 0 && dk == dv) return fail(HSTU_ERR_INVALID_ARGUMENT, "dk and dv are the same buffer");
     if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
     if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN)) != HSTU_OK) return st;
+    if (stored) {
+        st = run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream, true, workspace,
+                      workspace_bytes);
+        if (st != HSTU_OK) return st;
+        return run_dq_ds(a, k, cu_seqlens_q, cu_seqlens_k, workspace, workspace_bytes, dq, stream);
+    }
     st = run_dq(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dq, stream);
     if (st != HSTU_OK) return st;
     return run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream);

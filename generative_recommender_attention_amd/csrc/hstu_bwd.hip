@@ -1,4 +1,7 @@
-// HSTU attention backward on gfx950: two deterministic kernels, no workspace.
+// HSTU attention backward on gfx950: deterministic kernels, no atomics.  Two
+// routes: a dq kernel and a dk/dv kernel that both recompute the scores (no
+// workspace), or -- under no mask or the causal mask, given a workspace -- the
+// dk/dv kernel storing dS and a dq kernel that reads it (described last).
 //
 // The backward receives dO and q, k, v only (HSTU Attention page, "High-level
 // functions"), so both kernels recompute the scores.  With s = alpha q_i.k_j,
@@ -46,6 +49,17 @@
 // their MFMAs.  Splitting the gradients over two kernels executes 14 D flops
 // per visible pair against 10 D for a single pass, but needs no atomics and no
 // workspace and is bit-for-bit reproducible.
+//
+// Stored dS: the dk/dv kernel also writes each 32 x 32 block of bf16 dS it forms
+// (the dS^T operand of its dK product, as it sits in the registers: 2 bytes per
+// visible pair, streamed past the caches), and the second dq kernel computes
+// dQ^T = K^T dS^T from those blocks: 2 D flops per pair instead of 6 D, no
+// exponentials, and no Q, dO or V reads, for 4 bytes of HBM traffic per pair
+// (written once, read once).  The blocks keep the dk/dv kernel's orientation
+// (a row per key); the dq kernel stages them in LDS and transposes them with the
+// same transposing read it uses for K.  dK and dV are those of the recompute
+// route bit for bit; dQ differs only in rounding (its dS comes from the scores
+// as the dk/dv kernel forms them).
 #include "hstu_kernels.h"
 
 namespace hstu {
@@ -333,18 +347,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     }
 }
 
+// Where a wave of the dk/dv kernel stores the dS of its 32 x 32 block: `p` is
+// the lane's destination (the 64-byte row of its key, element 8 g); `kdead`
+// (read when the wave-uniform `kcut` is set) whether the lane's key lies past
+// the sequence (stored as 0); nothing is stored unless the wave-uniform `on` is set.
+struct DsOut {
+    uint16_t* p;
+    bool on, kcut, kdead;
+};
+
+// Query row held at position c (0..31) of a stored dS key row, and the reverse:
+// the dk/dv lane (key, g) stores its operand half h (rows 16 h + 8 (t / 4) +
+// 4 g + t % 4, t = 0..7) at positions 16 h + 8 g + t, i.e. bits 2 and 3 trade places.
+__device__ __forceinline__ int ds_pos_row(int c) { return (c & 0x13) | ((c & 4) << 1) | ((c & 8) >> 1); }
+
 // One 32-row block for one wave: S = Q K^T and dA = dO V^T (A operands: Q, dO
 // rows of the block; B operands: the wave's K, V rows), then dV^T += dO^T A' and
 // dK^T += Q^T dS over the block's two contraction steps.  When `mask` (wave-
 // uniform): MT = kInterval zeroes the rows outside this lane's [lo, hi); kBits
 // tests row 8 k + 4 g + j of the block (accumulator register 4 k + j) against
-// bit l32 of the LDS word at mw + 32 k + 4 j.
+// bit l32 of the LDS word at mw + 32 k + 4 j.  The bf16 dS goes to `ds` as it is
+// formed (the operand of dK^T itself is left as computed).
 template <int D, int MT>
 __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t drow, uint32_t krow, uint32_t vrow, uint32_t qtr,
                                             uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
                                             const uint2 (&toff)[(D < 32 ? 32 : D) / 32], int row0, int lo, int hi,
-                                            int g, uint32_t mw) {
+                                            int g, uint32_t mw, const DsOut& ds) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // reads for S and dA: step kk, (Q, K, dO, V)
@@ -411,6 +440,19 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     }
     const uint4 a[2] = {pack_operand(av), pack_operand(av + 8)};
     const uint4 d[2] = {pack_operand(dv), pack_operand(dv + 8)};
+    if (ds.on) {
+        // the two dS^T operand halves as they are: rows past the sequence hold 0 (masked above)
+        uint4 s0 = d[0], s1 = d[1];
+        if (ds.kcut) {
+            keep_branch();
+            if (ds.kdead) s0 = s1 = make_uint4(0, 0, 0, 0);
+        }
+        // streaming stores: dS is read once, by the dq kernel, and must not push the
+        // Q and dO rows that the other key blocks re-read out of the caches
+        const u32x4 v0 = {s0.x, s0.y, s0.z, s0.w}, v1 = {s1.x, s1.y, s1.z, s1.w};
+        __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(ds.p));
+        __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(ds.p + 16));
+    }
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         const int half = j / (2 * NDB), db = (j / 2) % NDB;
@@ -425,6 +467,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr bool FUNC = MK == MaskKind::Func;
+    // stored dS (no mask or causal: the row blocks of the walk start on multiples of 32)
+    constexpr bool DS = MK == MaskKind::None || MK == MaskKind::Causal;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
     // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1 | K rows of the block | V rows of the block]
@@ -454,6 +498,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int key0 = n0 + 32 * kw;
     const int my_key = key0 + l32;
     const bool wave_live = key0 < sb.lk;
+    // stored dS: this lane's element of the wave's key group in the first row block
+    // (block rows are keys here: lane l32 writes the row of its key)
+    uint16_t* ds_base = nullptr;
+    if (DS && p.ds != nullptr) {
+        const int64_t slot = ((int64_t)sb.q0 + 31 * (int64_t)b) >> 5;
+        ds_base = p.ds + (((int64_t)h * p.ds_nb + slot) * p.ds_kg + (key0 >> 5)) * kDsBlockElems +
+                  l32 * kDsRowElems + 8 * g;
+    }
 
     // the block's K (times c) and V rows into LDS; rows past the sequence repeat its last row
     for (int u = tid; u < BNK * 16; u += 512) {
@@ -599,15 +651,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     // rows past the sequence (copies of its last row) must be masked out too
                     if (seen != 0)
                         dkdv_block<D, kBits>(cut != 0 || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
-                                             roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g));
+                                             roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g),
+                                             DsOut{nullptr, false, false, false});
                 }
             } else {
                 // waves whose keys no row of the block sees, or that lie past the sequence, skip it
                 const bool run = WINDOW ? row0 + 32 > any_lo && row0 < any_hi : !(CAUSAL && row0 + 31 < key0);
                 if (wave_live && run && row0 < sb.lq) {
+                    DsOut ds{nullptr, false, false, false};
+                    if (DS && ds_base != nullptr) {
+                        ds.on = true;
+                        ds.p = ds_base + (int64_t)(row0 >> 5) * p.ds_kg * kDsBlockElems;
+                        ds.kcut = key0 + 32 > sb.lk;
+                        ds.kdead = my_key >= sb.lk;
+                    }
                     // rows outside those that see every key of the wave, or past the sequence, need the mask
                     dkdv_block<D, kInterval>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
-                                             roff, toff, row0, lo, hi, g, 0);
+                                             roff, toff, row0, lo, hi, g, 0, ds);
                 }
             }
             wait_global_loads();
@@ -668,6 +728,201 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     }
 }
 
+// dq from stored dS (no mask or causal): one workgroup per (128-row block,
+// sequence, head), 32 rows per wave, as the dq kernel above.  Per 64-key tile K
+// is staged row-major in LDS (two slots, one tile ahead, shared by the four
+// waves) and each wave copies its rows' dS blocks into its own LDS ring of three
+// slots, two tiles ahead (the stream from HBM needs the longer lead), reads its
+// dS^T operands from there and accumulates dQ^T += K^T dS^T (A operand: K read
+// transposed).  Both copies are direct global->LDS loads that the compiler does
+// not track, so the only waits in the loop are the counted ones below.  A wave
+// uses the key groups the dk/dv kernel stored for its row block: every group of
+// a sequence's keys without a mask, groups G <= R (row block R) under the causal
+// mask; entries outside the mask or past the sequence's keys are stored as 0.
+template <int D>
+__device__ __forceinline__ void dq_ds_tile(uint32_t kt, const uint4 (&dsop)[4],
+                                           f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
+                                           const uint2 (&toff)[(D < 32 ? 32 : D) / 32]) {
+    constexpr int NDB = (D < 32 ? 32 : D) / 32;
+    constexpr int NQ = 4 * NDB;  // block kb = i / (2 NDB), step s = i / NDB, column block i % NDB
+    constexpr int PF = 4;
+    uint4 rd[NQ];
+    auto read = [&](int i) {
+        if (i < NQ) {
+            const int s4 = i / NDB, db = i % NDB;
+            rd[i] = ds_read_tr16x2(toff[db].x + kt + 4096 * s4, toff[db].y + kt + 4096 * s4);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) read(i);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        acc[i % NDB] = mfma32x32x16(rd[i], dsop[i / NDB], acc[i % NDB]);
+        read(i + PF);
+    }
+}
+
+// One dS slot of a wave: its two key groups' 32 x 32 blocks as stored, 2 KB each
+// (64 bytes per key).
+constexpr uint32_t kDsSlotBytes = 2 * 2 * kDsBlockElems;
+// Byte offsets of the transposing reads of lane `lane` in a stored block: keys
+// 4 g .. 4 g + 3 (.x) and 8 + 4 g .. (.y) at position l32, i.e. the dS^T operand
+// half 0 of query row ds_pos_row(l32); half 1 is 16 keys (1 KB) further.
+__device__ __forceinline__ uint2 ds_tr_offsets(int lane) {
+    const int grp = lane >> 4, j = lane & 15;
+    const int r = 4 * (grp >> 1) + (j >> 2);
+    const int c = 16 * (grp & 1) + 4 * (j & 3);
+    return make_uint2((uint32_t)(r * 64 + 2 * c), (uint32_t)((r + 8) * 64 + 2 * c));
+}
+
+template <int D, MaskKind MK>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(AttnParams p) {
+    static_assert(MK == MaskKind::None || MK == MaskKind::Causal, "stored dS exists for these masks only");
+    constexpr bool CAUSAL = MK == MaskKind::Causal;
+    constexpr int DM = D < 32 ? 32 : D;
+    // [K slot 0 | K slot 1 | wave 0: dS slots 0-2 | wave 1 | wave 2 | wave 3]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kTileElems + 4 * 3 * kDsSlotBytes / 2];
+    const uint32_t lds0 = lds_addr(smem);
+    constexpr uint32_t K0 = 0, K1 = kTileBytes;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const uint32_t dsl = lds0 + 2 * kTileBytes + (uint32_t)wave * 3 * kDsSlotBytes;
+
+    const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
+    BlockItem item;
+    if (!find_block<true>(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int b = item.b, m = item.m;
+    const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
+    const int m0 = m * BM;
+    if (m0 >= sb.lq) return;
+
+    const int row0 = m0 + 32 * wave;
+    const int my_row = row0 + ds_pos_row(l32);  // the query row of this lane's products
+    const bool wave_live = row0 < sb.lq;
+    // keys the block walks, and the key groups whose dS this wave uses: [0, ngw)
+    int kv_end = min(sb.lk, 32 * p.ds_kg);
+    if (CAUSAL) kv_end = min(kv_end, m0 + BM);
+    const int ng = (kv_end + 31) >> 5;
+    const int ngw = __builtin_amdgcn_readfirstlane(!wave_live ? 0 : CAUSAL ? min(ng, (row0 >> 5) + 1) : ng);
+    const int t1 = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
+    // The wave's row block in the workspace (block 0 when the wave has none: its
+    // copies then fetch in-bounds data that is never used, so that every tile
+    // issues the same four copies); each copy moves 1 KB of a block as it is.
+    int64_t blk0 = 0;
+    if (wave_live) {
+        const int64_t slot = ((int64_t)sb.q0 + 31 * (int64_t)b) >> 5;
+        blk0 = ((int64_t)h * p.ds_nb + slot + (row0 >> 5)) * p.ds_kg;
+    }
+    const uint16_t* dsg = static_cast<const uint16_t*>(uniform_ptr(p.ds + blk0 * kDsBlockElems));
+    const uint32_t cpy_off = 16u * (uint32_t)lane;
+    auto copy_ds = [&](int t) {
+        const uint32_t dst = dsl + (uint32_t)(t % 3) * kDsSlotBytes;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int grp = 2 * t + kb;
+            const uint32_t src = grp < ngw ? (uint32_t)grp * (2u * kDsBlockElems) : 0u;  // bytes from dsg
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dma16_lds_stream(dst + (uint32_t)kb * (2u * kDsBlockElems) + 1024u * c, dsg, src + 1024u * c + cpy_off);
+        }
+    };
+    const uint2 dtr = ds_tr_offsets(lane);
+
+    uint2 toff[DM / 32];
+#pragma unroll
+    for (int db = 0; db < DM / 32; ++db) {
+        toff[db] = tr_offsets(32 * db, lane);
+        toff[db].x += lds0;
+        toff[db].y += lds0;
+    }
+    f32x16 acc[DM / 32];
+#pragma unroll
+    for (int db = 0; db < DM / 32; ++db) acc[db] = f32x16{};
+
+    if (t1 > 0) {
+        const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
+        TileDma<D> kdma;
+        kdma.init(wave, lane, p.k.tok);
+        if constexpr (D < 32) {
+            // columns D..31 of the K slots are read by the 32-wide transposed blocks
+            for (int u = tid; u < 2 * kTileRows * (32 - D) / 8; u += 256) {
+                const int sl = u / (kTileRows * (32 - D) / 8), v = u % (kTileRows * (32 - D) / 8);
+                const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
+                ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
+            }
+        }
+        // Wait until all copies but the four dS copies of tile t (if issued) have landed.
+        // Issue order: K(0), dS(0), dS(1), then per tile t: K(t + 1), dS(t + 2).
+        auto wait_copies = [&](int t) {
+            if (t < t1) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+            else __builtin_amdgcn_s_waitcnt(0x0f70);         // vmcnt(0)
+        };
+        kdma.issue(lds0 + K0, kbase, p.k.tok, 0, kv_end);
+        copy_ds(0);
+        if (1 < t1) copy_ds(1);
+        wait_copies(1);  // K(0) and dS(0) have landed
+        __syncthreads();
+
+        for (int t = 0; t < t1; ++t) {
+            const uint32_t kc = (t & 1) ? K1 : K0, kn = (t & 1) ? K0 : K1;
+            if (t + 1 < t1) kdma.issue(lds0 + kn, kbase, p.k.tok, (t + 1) * BN, kv_end);
+            if (t + 2 < t1) copy_ds(t + 2);
+            if (2 * t < ngw) {
+                const uint32_t sl = dsl + (uint32_t)(t % 3) * kDsSlotBytes;
+                uint4 op[4];
+                op[0] = ds_read_tr16x2(sl + dtr.x, sl + dtr.y);
+                op[1] = ds_read_tr16x2(sl + 1024u + dtr.x, sl + 1024u + dtr.y);
+                if (2 * t + 1 < ngw) {
+                    op[2] = ds_read_tr16x2(sl + 2048u + dtr.x, sl + 2048u + dtr.y);
+                    op[3] = ds_read_tr16x2(sl + 3072u + dtr.x, sl + 3072u + dtr.y);
+                } else {
+                    op[2] = op[3] = make_uint4(0, 0, 0, 0);  // the second group is not used
+                }
+                dq_ds_tile<D>(kc, op, acc, toff);  // toff holds lds0
+            }
+            wait_copies(t + 2);
+            __syncthreads();
+        }
+    }
+
+    if (my_row < sb.lq) {
+        uint16_t* dst = p.dq.base + (int64_t)(sb.q0 + my_row) * p.dq.tok + (int64_t)h * p.dq.head;
+        const float sc = p.out_scale;
+#pragma unroll
+        for (int db = 0; db < DM / 32; ++db) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d0 = db * 32 + 8 * rq + 4 * g;
+                if (d0 < D) {
+                    const f32x16& a = acc[db];
+                    *reinterpret_cast<uint2*>(dst + d0) =
+                        make_uint2(pack_bf16x2(a[4 * rq] * sc, a[4 * rq + 1] * sc),
+                                   pack_bf16x2(a[4 * rq + 2] * sc, a[4 * rq + 3] * sc));
+                }
+            }
+        }
+    }
+}
+
+template <int D, MaskKind MK>
+hipError_t launch_dq_ds(const AttnParams& p, hipStream_t stream) {
+    const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, MK>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_ds_mask(const AttnParams& p, MaskKind mask, hipStream_t stream) {
+    switch (mask) {
+        case MaskKind::None: return launch_dq_ds<D, MaskKind::None>(p, stream);
+        case MaskKind::Causal: return launch_dq_ds<D, MaskKind::Causal>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int D, MaskKind MK>
 hipError_t launch_dq(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
@@ -718,6 +973,16 @@ hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipSt
 
 hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
     return launch_dir<true>(p, head_dim, mask, stream);
+}
+
+hipError_t launch_bwd_dq_ds(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
+    switch (head_dim) {
+        case 16: return launch_dq_ds_mask<16>(p, mask, stream);
+        case 32: return launch_dq_ds_mask<32>(p, mask, stream);
+        case 64: return launch_dq_ds_mask<64>(p, mask, stream);
+        case 128: return launch_dq_ds_mask<128>(p, mask, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace hstu

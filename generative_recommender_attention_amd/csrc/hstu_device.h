@@ -169,6 +169,12 @@ __device__ __forceinline__ void dma16_lds(uint32_t lds, const void* gbase, uint3
                      :
                      : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase)));
 }
+// The same for data read once (streaming, non-temporal cache policy).
+__device__ __forceinline__ void dma16_lds_stream(uint32_t lds, const void* gbase, uint32_t voff) {
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase)));
+}
 
 // Staging of one 64-row tile of a (T, H, D) tensor by NW waves with
 // dma16_lds: each instruction fills one contiguous 1 KB chunk (4 tile rows),

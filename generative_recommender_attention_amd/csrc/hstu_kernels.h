@@ -36,7 +36,22 @@ struct AttnParams {
     int32_t func_ld;
     TensorRef q, k, v, dout;
     TensorOut o, dq, dk, dv;
+    // Backward through stored dS (no mask or causal only): the dk/dv kernel writes, and
+    // the dS-reading dq kernel reads, bf16 dS in 2 KB blocks of 32 query rows x 32 keys.
+    // Block (head h, row block R of batch entry b, key group G) sits at block index
+    // (h ds_nb + (cu_q[b] + 31 b) / 32 + R) ds_kg + G; null: the dk/dv kernel writes none.
+    uint16_t* ds;
+    int64_t ds_nb;         // row-block slots per head: (T_q + 31 B) / 32
+    int32_t ds_kg;         // key groups per row block: 4 ceil(max_seqlen_k / 128)
 };
+
+// Elements of one stored dS block (32 x 32 bf16, 2 KB) and of one of its rows.
+constexpr int kDsBlockElems = 32 * 32;
+constexpr int kDsRowElems = 32;
+// Largest byte span of one row block's key groups (4 ceil(max_seqlen_k / 128)
+// blocks): the dS-reading dq kernel fetches them by 32-bit byte offsets, so
+// max_seqlen_k <= 2^25 (2^32 bytes / 2 KB per 32 keys, less a margin).
+constexpr int64_t kMaxDsRowBlockBytes = (int64_t(1) << 32) - 4096;
 
 // Tile shapes (rows per workgroup) used to size the grids.
 constexpr int kFwdBlockM = 128;   // query rows per forward / dQ workgroup
@@ -53,5 +68,7 @@ constexpr int32_t kMaxWindowSeqlen = 1 << 29;
 hipError_t launch_fwd(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
+// dQ from the dS the dk/dv kernel stored (p.ds); mask None or Causal.
+hipError_t launch_bwd_dq_ds(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 
 }  // namespace hstu

@@ -35,6 +35,8 @@ __all__ = [
     "hstu_bwd_workspace_size",
     "hstu_bwd_dq",
     "hstu_bwd_dkdv",
+    "hstu_bwd_dkdv_ds",
+    "hstu_bwd_dq_ds",
     "HSTU_OK",
     "HSTU_ERR_INVALID_ARGUMENT",
     "HSTU_ERR_UNSUPPORTED",
@@ -57,7 +59,7 @@ HSTU_MASK_NONE = 0
 HSTU_MASK_CAUSAL = 1
 HSTU_MASK_WINDOW = 2
 HSTU_MASK_FUNC = 3
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
@@ -156,6 +158,10 @@ def library() -> ctypes.CDLL:
             lib.hstu_bwd_dq.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_bwd_dkdv.restype = ctypes.c_int
             lib.hstu_bwd_dkdv.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hstu_bwd_dkdv_ds.restype = ctypes.c_int
+            lib.hstu_bwd_dkdv_ds.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            lib.hstu_bwd_dq_ds.restype = ctypes.c_int
+            lib.hstu_bwd_dq_ds.argtypes = [argp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
             largp = ctypes.POINTER(HstuLmsdArgs)
             lib.hstu_lmsd_fwd.restype = ctypes.c_int
             lib.hstu_lmsd_fwd.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -299,11 +305,15 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              scaling_seqlen: Optional[int] = None, causal: bool = True,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-             window_size: Optional[Tuple[int, int]] = None, func: Optional[torch.Tensor] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.  ``workspace``
-    (a device byte tensor) is allocated here when the library asks for one and
-    none is given."""
+             window_size: Optional[Tuple[int, int]] = None, func: Optional[torch.Tensor] = None,
+             store_ds: bool = True) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.
+
+    With ``store_ds`` (and no mask or the causal mask) the dk/dv kernel stores dS
+    in ``workspace`` (a device byte tensor of ``hstu_bwd_workspace_size`` bytes,
+    allocated here when not given) and dq is computed from it; with
+    ``store_ds=False``, or under the other masks, the dq kernel recomputes the
+    scores and no workspace is used."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
@@ -315,14 +325,23 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     a.dq, a.dk, a.dv = _stride(dq), _stride(dk), _stride(dv)
     need = ctypes.c_size_t(0)
     _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
-    if workspace is None and need.value > 0:
+    if not store_ds or need.value == 0:
+        workspace = None
+    elif workspace is None:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(library().hstu_bwd(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                               pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
                               _stream(stream, q.device)))
     return dq, dk, dv
+
+
+def _workspace(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def hstu_bwd_workspace_size(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
@@ -469,3 +488,38 @@ def lmsd_bwd(dy: torch.Tensor, x: torch.Tensor, u: torch.Tensor, weight: torch.T
                                    dweight.data_ptr() if dweight is not None else None, dbias.data_ptr(), ws_ptr,
                                    ws_bytes, _stream(stream, x.device)))
     return dx, du, dweight, dbias
+
+
+def hstu_bwd_dkdv_ds(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ds,
+                     alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None,
+                     window_size=None):
+    """(dk, dv), storing dS in ``ds`` (``hstu_bwd_workspace_size`` bytes) for
+    ``hstu_bwd_dq_ds``; no mask or the causal mask only."""
+    H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _thd("dk", dk, int(k.shape[0]), H, D)
+    _thd("dv", dv, int(k.shape[0]), H, D)
+    a.dk, a.dv = _stride(dk), _stride(dv)
+    ws_ptr, ws_bytes = _workspace(ds)
+    _check(library().hstu_bwd_dkdv_ds(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                      v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
+                                      _stream(stream, q.device)))
+    return dk, dv
+
+
+def hstu_bwd_dq_ds(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ds, alpha=1.0,
+                   scaling_seqlen=None, causal=True, dq=None, stream=None, window_size=None):
+    """dq from the dS that ``hstu_bwd_dkdv_ds`` stored in ``ds`` for the same
+    problem (``q`` gives the shape and strides of dq only; it is not read)."""
+    H, D, pq, pk = _inputs(q, k, k, cu_seqlens_q, cu_seqlens_k)
+    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, None)
+    a.q, a.k = _stride(q), _stride(k)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    _thd("dq", dq, int(q.shape[0]), H, D)
+    a.dq = _stride(dq)
+    ws_ptr, ws_bytes = _workspace(ds)
+    _check(library().hstu_bwd_dq_ds(ctypes.byref(a), k.data_ptr(), pq, pk, ws_ptr, ws_bytes, dq.data_ptr(),
+                                    _stream(stream, q.device)))
+    return dq

@@ -107,7 +107,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 5
+#define HSTU_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define HSTU_API __attribute__((visibility("default")))
@@ -165,16 +165,25 @@ HSTU_API hstu_status_t hstu_fwd(const hstu_args_t* args,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                        void* o, hipStream_t stream);
 
-/* Device workspace, in bytes, that hstu_bwd needs for the problem in `args`
- * (written to *bytes).  Reads scalars only.  The backward built here (two
- * kernels, no atomics) needs none and reports 0; the call exists so that
- * callers size and pass a workspace the same way for every backward variant. */
+/* Bytes of device workspace that lets hstu_bwd store dS instead of recomputing
+ * the scores for dQ (written to *bytes).  Reads the scalars of `args` only (the
+ * pointers in it are not used).  dS (above) is the factor that dQ and dK share;
+ * the workspace holds it in bf16 without the 1 / L_scale, which the dQ kernel
+ * applies with alpha.  Under no mask or the causal mask the result is
+ * H x ((T_q + 31 B) / 32) x 4 ceil(max_seqlen_k / 128) blocks of 2 KB (a bf16 dS
+ * block of 32 query rows x 32 keys per row-block slot and key group, whatever
+ * the sequence lengths turn out to be); under a window or arbitrary mask it is
+ * 0 (those backwards always recompute). */
 HSTU_API hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* args, size_t* bytes);
 
-/* Backward, all three gradients: enqueues hstu_bwd_dq then hstu_bwd_dkdv.
- * `workspace` is caller-owned device memory of at least
- * hstu_bwd_workspace_size() bytes, 256-byte aligned; it may be null when that
- * size is 0.  A smaller `workspace_bytes` is HSTU_ERR_INVALID_ARGUMENT. */
+/* Backward, all three gradients.  With a workspace of at least
+ * hstu_bwd_workspace_size() bytes (256-byte aligned, caller-owned device
+ * memory, contents on entry ignored) and a nonzero size, enqueues
+ * hstu_bwd_dkdv_ds then hstu_bwd_dq_ds on it; with `workspace` null, or a
+ * size of 0, enqueues hstu_bwd_dq then hstu_bwd_dkdv, which need none.  A
+ * non-null workspace smaller than the size is HSTU_ERR_INVALID_ARGUMENT.  The
+ * two routes round differently (dQ from the bf16 dS of the dk/dv kernel, or
+ * from its own recomputed scores) and both meet the same accuracy. */
 HSTU_API hstu_status_t hstu_bwd(const hstu_args_t* args, const void* dout,
                        const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -193,6 +202,26 @@ HSTU_API hstu_status_t hstu_bwd_dkdv(const hstu_args_t* args, const void* dout,
                             const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                             void* dk, void* dv, hipStream_t stream);
+
+/* hstu_bwd_dkdv that also writes the bf16 dS of every 32 x 32 (rows x keys)
+ * block it computes to `ds` (hstu_bwd_workspace_size() bytes, 256-byte aligned;
+ * null allowed only when that size is 0), entries outside the mask as 0.  dK
+ * and dV are bit-identical to hstu_bwd_dkdv's.  Mask none or causal only
+ * (else HSTU_ERR_UNSUPPORTED). */
+HSTU_API hstu_status_t hstu_bwd_dkdv_ds(const hstu_args_t* args, const void* dout,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               void* dk, void* dv, void* ds, size_t ds_bytes,
+                               hipStream_t stream);
+
+/* dQ = alpha / L_scale * dS K from the dS that hstu_bwd_dkdv_ds stored in `ds`
+ * for the same args and cu_seqlens (enqueue it first on the same stream, or
+ * order the two otherwise).  Reads k and ds only; writes dq.  Mask none or
+ * causal only. */
+HSTU_API hstu_status_t hstu_bwd_dq_ds(const hstu_args_t* args, const void* k,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             const void* ds, size_t ds_bytes, void* dq,
+                             hipStream_t stream);
 
 /* ==========================================================================
  * HSTU LMSD: LayerNorm, affine, times SiLU(u) (HSTU LMSD page, "Overview").

@@ -58,9 +58,22 @@ class DeviceWorkload:
         kw.update(over)
         return hstu.hstu_fwd(self.q, self.k, self.v, self.cu_q, self.cu_k, **kw)
 
-    def bwd(self, **over):
+    def workspace(self, fill=0xFF, **over):
+        """A dS workspace for hstu_bwd, or None when the mask has none; filled with
+        bf16 NaN by default, so that a read of an entry no kernel wrote shows."""
         kw = self.kw()
         kw.update(over)
+        kw.pop("store_ds", None)
+        need = hstu.hstu_bwd_workspace_size(self.do, self.q, self.k, self.v, self.cu_q, self.cu_k, **kw)
+        return torch.full((need,), fill, dtype=torch.uint8, device=self.q.device) if need else None
+
+    def bwd(self, **over):
+        """hstu_bwd; on the stored-dS path (the default where the mask allows it)
+        with a NaN-filled workspace unless one is given."""
+        kw = self.kw()
+        kw.update(over)
+        if kw.get("store_ds", True) and "workspace" not in kw:
+            kw["workspace"] = self.workspace(**over)
         return hstu.hstu_bwd(self.do, self.q, self.k, self.v, self.cu_q, self.cu_k, **kw)
 
 

@@ -33,7 +33,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
-        "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dq", "hstu_bwd_workspace_size", "hstu_fwd",
+        "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dkdv_ds", "hstu_bwd_dq", "hstu_bwd_dq_ds",
+        "hstu_bwd_workspace_size", "hstu_fwd",
         "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd", "hstu_status_string"])
 
 
@@ -139,12 +140,53 @@ def test_backward_rejections(lib):
     assert st == hstu.HSTU_ERR_UNSUPPORTED
 
 
-def test_backward_workspace_query(lib):
+def ws_size(lib, a):
     need = ctypes.c_size_t(123)
-    assert lib.hstu_bwd_workspace_size(ctypes.byref(good_args()), ctypes.byref(need)) == hstu.HSTU_OK
-    assert need.value == 0  # the two-kernel backward needs no workspace
+    st = lib.hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need))
+    return st, need.value
+
+
+@pytest.mark.parametrize("over,blocks", [
+    # 2 KB blocks: H x (T_q + 31 B) / 32 row-block slots x 4 ceil(max_seqlen_k / 128) key groups
+    (dict(), 2 * 2 * 4),                                                   # causal, B = 2, T_q = 32
+    (dict(mask=0), 2 * 2 * 4),                                             # no mask
+    (dict(mask=2, window_left=-1, window_right=0), 2 * 2 * 4),            # the causal window
+    (dict(batch=5, total_q=300, total_k=300, max_seqlen_q=129, max_seqlen_k=129, num_heads=3),
+     3 * ((300 + 31 * 5) // 32) * 8),
+    (dict(mask=2, window_left=4, window_right=0), 0),                     # window: recompute only
+    (dict(mask=3, func_n=1, func_ld=32, func=FAKE), 0),                   # arbitrary mask: likewise
+    (dict(total_k=0, max_seqlen_q=0, max_seqlen_k=0, scaling_seqlen=8), 0),  # no keys
+])
+def test_backward_workspace_query(lib, over, blocks):
+    st, need = ws_size(lib, good_args(**over))
+    assert st == hstu.HSTU_OK, lib.hstu_last_error()
+    assert need == 2048 * blocks
+
+
+def test_backward_workspace_rejections(lib):
+    need = ctypes.c_size_t(0)
     assert lib.hstu_bwd_workspace_size(None, ctypes.byref(need)) == hstu.HSTU_ERR_INVALID_ARGUMENT
     assert lib.hstu_bwd_workspace_size(ctypes.byref(good_args()), None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert ws_size(lib, good_args(head_dim=24))[0] == hstu.HSTU_ERR_UNSUPPORTED
+    a = good_args()
+    size = ws_size(lib, a)[1]
+    ws = FAKE + 4096  # 256-byte aligned
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, FAKE + 32, FAKE + 48)
+    # a non-null workspace below the size, or misaligned, is refused; null selects the recompute path
+    assert lib.hstu_bwd(ctypes.byref(a), *args, ws, size - 1, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert b"workspace" in lib.hstu_last_error()
+    assert lib.hstu_bwd(ctypes.byref(a), *args, ws + 16, size, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    dkdv = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, FAKE + 32)
+    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(a), *dkdv, None, size, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(a), *dkdv, ws, size - 2048, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_dq_ds(ctypes.byref(a), FAKE, FAKE, FAKE, None, size, FAKE, None) == \
+        hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_dq_ds(ctypes.byref(a), FAKE, FAKE, FAKE, ws + 128, size, FAKE, None) == \
+        hstu.HSTU_ERR_INVALID_ARGUMENT
+    # stored dS exists for the full and causal masks only
+    w = good_args(mask=2, window_left=4, window_right=0)
+    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(w), *dkdv, ws, size, None) == hstu.HSTU_ERR_UNSUPPORTED
+    assert lib.hstu_bwd_dq_ds(ctypes.byref(w), FAKE, FAKE, FAKE, ws, size, FAKE, None) == hstu.HSTU_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

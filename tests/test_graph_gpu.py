@@ -40,6 +40,7 @@ def test_attention_fwd_bwd_graph_replays(mask):
     kw = dw.kw()
     o = torch.empty_like(dw.q)
     dq, dk, dv = torch.empty_like(dw.q), torch.empty_like(dw.k), torch.empty_like(dw.v)
+    ws = dw.workspace()  # stored dS under the causal mask; None (recompute) under the others
     say(f"graph capture: attention fwd + bwd, mask {mask}")
     o_ref = dw.fwd()
     g_ref = dw.bwd()
@@ -51,7 +52,7 @@ def test_attention_fwd_bwd_graph_replays(mask):
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
             hstu.hstu_fwd(dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, out=o, **kw)
-            hstu.hstu_bwd(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, dq=dq, dk=dk, dv=dv, **kw)
+            hstu.hstu_bwd(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(3):
         for t in (o, dq, dk, dv):

@@ -38,20 +38,26 @@ def run_fwd_check(wl, rows=None, tag=""):
 
 
 def run_bwd_check(wl, rows_q=None, rows_k=None, tag=""):
+    """Both backward routes against one oracle evaluation: dQ from stored dS (for
+    no mask and the causal mask) and dQ from recomputed scores."""
     dw = DeviceWorkload(wl)
-    say(f"hstu_bwd {wl.name}{tag}: B={wl.batch} Tq={wl.total_q} Tk={wl.total_k} H={wl.num_heads} "
-        f"D={wl.head_dim} mask={wl.mask_name}")
-    dq, dk, dv = dw.bwd()
-    torch.cuda.synchronize()
+    routes = [True, False] if wl.mask_name in ("causal", "full") else [False]
     rq, rk, rv = oracle.bwd_workload(wl, rows_q, rows_k)
-    gq, gk, gv = to_f64(dq), to_f64(dk), to_f64(dv)
-    if rows_q is not None:
-        gq = gq[rows_q]
-    if rows_k is not None:
-        gk, gv = gk[rows_k], gv[rows_k]
-    return (check_close("dQ", gq, rq, wl.cu_seqlens_q, rows_q),
-            check_close("dK", gk, rk, wl.cu_seqlens_k, rows_k),
-            check_close("dV", gv, rv, wl.cu_seqlens_k, rows_k))
+    res = []
+    for store in routes:
+        say(f"hstu_bwd {wl.name}{tag} ({'stored dS' if store else 'recompute'}): B={wl.batch} Tq={wl.total_q} "
+            f"Tk={wl.total_k} H={wl.num_heads} D={wl.head_dim} mask={wl.mask_name}")
+        dq, dk, dv = dw.bwd(store_ds=store)
+        torch.cuda.synchronize()
+        gq, gk, gv = to_f64(dq), to_f64(dk), to_f64(dv)
+        if rows_q is not None:
+            gq = gq[rows_q]
+        if rows_k is not None:
+            gk, gv = gk[rows_k], gv[rows_k]
+        res.append((check_close("dQ", gq, rq, wl.cu_seqlens_q, rows_q),
+                    check_close("dK", gk, rk, wl.cu_seqlens_k, rows_k),
+                    check_close("dV", gv, rv, wl.cu_seqlens_k, rows_k)))
+    return res[0]
 
 
 # ---------------------------------------------------------------- the workloads
@@ -183,11 +189,13 @@ def test_windows_naming_full_and_causal_are_those_masks_bitwise():
     ow, gw = dw.fwd(window_size=(-1, 0)), dw.bwd(window_size=(-1, 0))
     of, gf = dw.fwd(causal=False), dw.bwd(causal=False)
     on, gn = dw.fwd(window_size=(-1, -1)), dw.bwd(window_size=(-1, -1))
+    # a real window always recomputes dQ, so it is compared with the full mask's recompute route
+    gfr = dw.bwd(causal=False, store_ds=False)
     ob, gb = dw.fwd(window_size=(500, 500)), dw.bwd(window_size=(500, 500))
     torch.cuda.synchronize()
     assert torch.equal(oc, ow) and all(torch.equal(a, b) for a, b in zip(gc, gw))
     assert torch.equal(of, on) and all(torch.equal(a, b) for a, b in zip(gf, gn))
-    assert torch.equal(of, ob) and all(torch.equal(a, b) for a, b in zip(gf, gb))
+    assert torch.equal(of, ob) and all(torch.equal(a, b) for a, b in zip(gfr, gb))
 
 
 def test_window_invalid_bounds_raise():
@@ -244,7 +252,8 @@ def test_func_spelling_causal_and_window_is_bitwise_those_masks():
     left, right = 70, 0
     win_f = torch.from_numpy(np.stack([np.zeros_like(i), i - left, i + right + 1]).astype(np.int32)).cuda()
     say("func spelling causal / window (70, 0) vs those kernels")
-    oc, gc = dw.fwd(causal=True), dw.bwd(causal=True)
+    # the arbitrary mask always recomputes dQ: compare with causal's recompute route
+    oc, gc = dw.fwd(causal=True), dw.bwd(causal=True, store_ds=False)
     of, gf = dw.fwd(func=causal_f), dw.bwd(func=causal_f)
     ow, gw = dw.fwd(window_size=(left, right)), dw.bwd(window_size=(left, right))
     ofw, gfw = dw.fwd(func=win_f), dw.bwd(func=win_f)
@@ -299,6 +308,45 @@ def test_largest_token_stride(oracle_lib):
     check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q)
     check_close("dK", to_f64(dk), rk, wl.cu_seqlens_k)
     check_close("dV", to_f64(dv), rv, wl.cu_seqlens_k)
+
+
+# ------------------------------------------------------------------ stored dS
+@pytest.mark.parametrize("D,causal", [(16, True), (64, False), (128, True)])
+def test_stored_ds_entry_points(oracle_lib, D, causal):
+    """hstu_bwd_dkdv_ds then hstu_bwd_dq_ds: dK and dV bit-identical to
+    hstu_bwd_dkdv's, dQ bit-identical to hstu_bwd's stored route; the workspace
+    starts as NaN, and a second, smaller problem reuses it as the first left it."""
+    big = make_workload(f"dsbig{D}", 190 + D, [300, 129, 64, 0, 33], 2, D, causal, with_do=True)
+    small = make_workload(f"dssmall{D}", 191 + D, [65, 1, 200], 2, D, causal, with_do=True)
+    ws = DeviceWorkload(big).workspace()
+    for wl in (big, small):
+        dw = DeviceWorkload(wl)
+        kw = dw.kw()
+        kw.pop("func")
+        say(f"stored dS entry points {wl.name}: lengths {list(wl.lengths_q)} D={D} mask={wl.mask_name}")
+        dk, dv = hstu.hstu_bwd_dkdv_ds(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, ds=ws, **kw)
+        dq = hstu.hstu_bwd_dq_ds(dw.q, dw.k, dw.cu_q, dw.cu_k, ds=ws, **kw)
+        dk_r, dv_r = hstu.hstu_bwd_dkdv(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, **kw)
+        g = dw.bwd()
+        torch.cuda.synchronize()
+        assert torch.equal(dk, dk_r) and torch.equal(dv, dv_r)
+        assert torch.equal(dq, g[0]) and torch.equal(dk, g[1]) and torch.equal(dv, g[2])
+        rq, rk, rv = oracle.bwd_workload(wl)
+        check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q)
+
+
+def test_stored_ds_needs_the_workspace_it_asks_for():
+    wl = make_workload("dsws", 195, [100, 40], 1, 32, True, with_do=True)
+    dw = DeviceWorkload(wl)
+    kw = dw.kw()
+    kw.pop("func")
+    ws = dw.workspace()
+    with pytest.raises(hstu.HstuError):
+        hstu.hstu_bwd(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, workspace=ws[:-256], **kw)
+    with pytest.raises(hstu.HstuError):
+        hstu.hstu_bwd_dq_ds(dw.q, dw.k, dw.cu_q, dw.cu_k, ds=ws[:2048], **kw)
+    with pytest.raises(NotImplementedError):
+        hstu.hstu_bwd_dkdv_ds(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, ds=ws, **dict(kw, window_size=(8, 0)))
 
 
 # ------------------------------------------------------------------ invariants
