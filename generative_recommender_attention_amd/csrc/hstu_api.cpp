@@ -235,7 +235,7 @@ hstu_status_t run_dq_ds(const hstu_args_t* a, const void* k, const int32_t* cu_q
     if ((st = bind_ds(*a, ds, ds_given, p)) != HSTU_OK) return st;
     p.k = ref(ops[0]);
     p.dq = out(ops[1]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kDqDsBlockM)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     // with no keys the kernel writes dQ = 0 without touching the (empty) workspace
     return launched(hstu::launch_bwd_dq_ds(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq_ds");

@@ -728,17 +728,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     }
 }
 
-// dq from stored dS (no mask or causal): one workgroup per (128-row block,
-// sequence, head), 32 rows per wave, as the dq kernel above.  Per 64-key tile K
-// is staged row-major in LDS (two slots, one tile ahead, shared by the four
+// dq from stored dS (no mask or causal): one workgroup per (256-row block,
+// sequence, head), 8 waves of 32 rows, one workgroup per CU.  Per 64-key tile K
+// is staged row-major in LDS (three slots, two tiles ahead, shared by the eight
 // waves) and each wave copies its rows' dS blocks into its own LDS ring of three
-// slots, two tiles ahead (the stream from HBM needs the longer lead), reads its
-// dS^T operands from there and accumulates dQ^T += K^T dS^T (A operand: K read
-// transposed).  Both copies are direct global->LDS loads that the compiler does
-// not track, so the only waits in the loop are the counted ones below.  A wave
-// uses the key groups the dk/dv kernel stored for its row block: every group of
-// a sequence's keys without a mask, groups G <= R (row block R) under the causal
-// mask; entries outside the mask or past the sequence's keys are stored as 0.
+// slots, also two tiles ahead (both stream from HBM: a one-tile lead left the
+// copy latency exposed at every tile), reads its dS^T operands from there and
+// accumulates dQ^T += K^T dS^T (A operand: K read transposed).  Both copies are
+// direct global->LDS loads that the compiler does not track, so the only waits
+// in the loop are the counted ones below.  A wave uses the key groups the dk/dv
+// kernel stored for its row block: every group of a sequence's keys without a
+// mask, groups G <= R (row block R) under the causal mask; entries outside the
+// mask or past the sequence's keys are stored as 0.
 template <int D>
 __device__ __forceinline__ void dq_ds_tile(uint32_t kt, const uint4 (&dsop)[4],
                                            f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
@@ -775,27 +776,29 @@ __device__ __forceinline__ uint2 ds_tr_offsets(int lane) {
     return make_uint2((uint32_t)(r * 64 + 2 * c), (uint32_t)((r + 8) * 64 + 2 * c));
 }
 
+constexpr int BMD = kDqDsBlockM;  // dq-from-dS kernel: query rows per workgroup (32 per wave)
+constexpr int NWD = BMD / 32;     // its waves
+
 template <int D, MaskKind MK>
-__global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(AttnParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
     static_assert(MK == MaskKind::None || MK == MaskKind::Causal, "stored dS exists for these masks only");
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr int DM = D < 32 ? 32 : D;
-    // [K slot 0 | K slot 1 | wave 0: dS slots 0-2 | wave 1 | wave 2 | wave 3]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kTileElems + 4 * 3 * kDsSlotBytes / 2];
+    // [K slots 0-2 | wave 0: dS slots 0-2 | wave 1 | ... | wave 7]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[3 * kTileElems + NWD * 3 * kDsSlotBytes / 2];
     const uint32_t lds0 = lds_addr(smem);
-    constexpr uint32_t K0 = 0, K1 = kTileBytes;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-    const uint32_t dsl = lds0 + 2 * kTileBytes + (uint32_t)wave * 3 * kDsSlotBytes;
+    const uint32_t dsl = lds0 + 3 * kTileBytes + (uint32_t)wave * 3 * kDsSlotBytes;
 
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
     BlockItem item;
-    if (!find_block<true>(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    if (!find_block<true>(p.cu_q, p.batch, BMD, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
-    const int m0 = m * BM;
+    const int m0 = m * BMD;
     if (m0 >= sb.lq) return;
 
     const int row0 = m0 + 32 * wave;
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(AttnParams p) {
     const bool wave_live = row0 < sb.lq;
     // keys the block walks, and the key groups whose dS this wave uses: [0, ngw)
     int kv_end = min(sb.lk, 32 * p.ds_kg);
-    if (CAUSAL) kv_end = min(kv_end, m0 + BM);
+    if (CAUSAL) kv_end = min(kv_end, m0 + BMD);
     const int ng = (kv_end + 31) >> 5;
     const int ngw = __builtin_amdgcn_readfirstlane(!wave_live ? 0 : CAUSAL ? min(ng, (row0 >> 5) + 1) : ng);
     const int t1 = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
@@ -843,32 +846,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(AttnParams p) {
 
     if (t1 > 0) {
         const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
-        TileDma<D> kdma;
+        TileDma<D, NWD> kdma;  // two 1 KB chunks of each K tile per wave
         kdma.init(wave, lane, p.k.tok);
         if constexpr (D < 32) {
             // columns D..31 of the K slots are read by the 32-wide transposed blocks
-            for (int u = tid; u < 2 * kTileRows * (32 - D) / 8; u += 256) {
+            for (int u = tid; u < 3 * kTileRows * (32 - D) / 8; u += 64 * NWD) {
                 const int sl = u / (kTileRows * (32 - D) / 8), v = u % (kTileRows * (32 - D) / 8);
                 const int r = v / ((32 - D) / 8), c = v % ((32 - D) / 8);
                 ds_write16(lds0 + sl * kTileBytes + tile_byte(r, D / 8 + c), make_uint4(0, 0, 0, 0));
             }
         }
-        // Wait until all copies but the four dS copies of tile t (if issued) have landed.
-        // Issue order: K(0), dS(0), dS(1), then per tile t: K(t + 1), dS(t + 2).
+        // Issue order: K(0), dS(0), K(1), dS(1), then per tile t: K(t + 2), dS(t + 2)
+        // (2 + 4 copies per wave).  After tile t's products, wait until all copies but
+        // those of tile t + 2 (if issued) have landed.
         auto wait_copies = [&](int t) {
-            if (t < t1) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+            if (t < t1) __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6)
             else __builtin_amdgcn_s_waitcnt(0x0f70);         // vmcnt(0)
         };
-        kdma.issue(lds0 + K0, kbase, p.k.tok, 0, kv_end);
+        auto kslot = [](int t) { return (uint32_t)(t % 3) * kTileBytes; };
+        kdma.issue(lds0, kbase, p.k.tok, 0, kv_end);
         copy_ds(0);
-        if (1 < t1) copy_ds(1);
+        if (1 < t1) {
+            kdma.issue(lds0 + kTileBytes, kbase, p.k.tok, BN, kv_end);
+            copy_ds(1);
+        }
         wait_copies(1);  // K(0) and dS(0) have landed
         __syncthreads();
 
         for (int t = 0; t < t1; ++t) {
-            const uint32_t kc = (t & 1) ? K1 : K0, kn = (t & 1) ? K0 : K1;
-            if (t + 1 < t1) kdma.issue(lds0 + kn, kbase, p.k.tok, (t + 1) * BN, kv_end);
-            if (t + 2 < t1) copy_ds(t + 2);
+            const uint32_t kc = kslot(t);
+            if (t + 2 < t1) {
+                kdma.issue(lds0 + kslot(t + 2), kbase, p.k.tok, (t + 2) * BN, kv_end);
+                copy_ds(t + 2);
+            }
             if (2 * t < ngw) {
                 const uint32_t sl = dsl + (uint32_t)(t % 3) * kDsSlotBytes;
                 uint4 op[4];
@@ -910,7 +920,7 @@ template <int D, MaskKind MK>
 hipError_t launch_dq_ds(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, MK>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, MK>), dim3((unsigned)grid), dim3(64 * NWD), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ constexpr int64_t kMaxDsRowBlockBytes = (int64_t(1) << 32) - 4096;
 // Tile shapes (rows per workgroup) used to size the grids.
 constexpr int kFwdBlockM = 128;   // query rows per forward / dQ workgroup
 constexpr int kBwdBlockN = 128;   // key rows per dK/dV workgroup
+constexpr int kDqDsBlockM = 256;  // query rows per workgroup of dQ from stored dS
 
 // Largest token stride (elements) the kernels accept: a 64-row tile spans at
 // most 64 strides, addressed by unsigned 32-bit byte offsets.
