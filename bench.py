@@ -3,9 +3,9 @@
 
 One step = the whole path over one batch of synthetic input, launched through
 the C ABI on the current stream: hstu_fwd, then the backward as hstu_bwd runs it
--- under no mask or the causal mask hstu_bwd_dkdv_ds (dK, dV, and dS stored in a
-workspace allocated before the timed region) then hstu_bwd_dq_ds; under the
-other masks, or with --recompute-dq, hstu_bwd_dq then hstu_bwd_dkdv.  Default
+-- under no mask, the causal mask or a window hstu_bwd_dkdv_ds (dK, dV, and dS
+stored in a workspace allocated before the timed region) then hstu_bwd_dq_ds;
+under the arbitrary mask, or with --recompute-dq, hstu_bwd_dq then hstu_bwd_dkdv.  Default
 workload: B=32 sequences with Zipf(1.2) lengths clipped to [16, 4096]
 (T = 23460), H=4, D=128, causal, bf16, plus an upstream gradient.
 
@@ -195,7 +195,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     else:
         wl = named_workload(workload)
         title = "HSTU attention fwd + bwd"
-        stored = wl.mask_name in ("causal", "none")
+        stored = wl.func is None
         what = (f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
                 f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + " +
                 ("hstu_bwd_dkdv_ds (bwd_dkdv_kernel storing dS) + hstu_bwd_dq_ds." if stored else

@@ -184,29 +184,54 @@ hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, cons
     return launched(hstu::launch_bwd_dq(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq");
 }
 
-// Bytes of stored dS for validated args: 0 unless the mask is none or causal (and
-// both sides have tokens); else one 2 KB block per (head, row-block slot, key group).
+// Layout of stored dS for validated args (stored = false where the backward always
+// recomputes): row-block slots per head, key-group slots per row block, the
+// window's relative offset (or -1) and the key groups the dk/dv grid covers.
+struct DsLayout {
+    bool stored;
+    int64_t nb, kg, kgr;
+    int32_t rel;
+};
+DsLayout ds_layout(const hstu_args_t& a) {
+    DsLayout l{false, 0, 0, 0, -1};
+    const hstu::MaskKind mk = mask_kind(a);
+    if (mk == hstu::MaskKind::Func || a.total_q == 0 || a.total_k == 0) return l;
+    l.kgr = 4 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN);
+    // the dq kernel addresses a row block's groups by 32-bit byte offsets
+    if (l.kgr * 2 * hstu::kDsBlockElems > (int64_t)hstu::kMaxDsRowBlockBytes) return l;
+    l.stored = true;
+    l.nb = ((int64_t)a.total_q + 31 * (int64_t)a.batch) / 32;
+    l.kg = l.kgr;
+    if (mk == hstu::MaskKind::Window) {
+        // row block R (rows 32 R ..) meets key groups R - ceil(left / 32) .. R + floor((31 + right) / 32)
+        auto side = [&](int32_t w) { return w < 0 || w > a.max_seqlen_k ? (int64_t)a.max_seqlen_k : (int64_t)w; };
+        const int64_t lo = (side(a.window_left) + 31) / 32, hi = (31 + side(a.window_right)) / 32;
+        if (lo + hi + 1 < l.kgr) {
+            l.kg = lo + hi + 1;
+            l.rel = (int32_t)lo;
+        }
+    }
+    return l;
+}
+
+// Bytes of stored dS for validated args: 0 where the mask has none (the arbitrary
+// mask) or a side has no tokens; else one 2 KB block per (head, row-block slot,
+// key-group slot).
 hstu_status_t ds_bytes(const hstu_args_t& a, size_t& bytes) {
     bytes = 0;
-    const hstu::MaskKind mk = mask_kind(a);
-    if ((mk != hstu::MaskKind::None && mk != hstu::MaskKind::Causal) || a.total_q == 0 || a.total_k == 0)
-        return HSTU_OK;
-    const int64_t nb = ((int64_t)a.total_q + 31 * (int64_t)a.batch) / 32;
-    const int64_t kg = 4 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN);
-    // the dq kernel addresses a row block's groups by 32-bit byte offsets
-    if (kg * 2 * hstu::kDsBlockElems > (int64_t)hstu::kMaxDsRowBlockBytes) return HSTU_OK;
-    const double approx = (double)a.num_heads * (double)nb * (double)kg * 2.0 * hstu::kDsBlockElems;
+    const DsLayout l = ds_layout(a);
+    if (!l.stored) return HSTU_OK;
+    const double approx = (double)a.num_heads * (double)l.nb * (double)l.kg * 2.0 * hstu::kDsBlockElems;
     if (approx > 9.0e18)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "stored dS would need %.3g bytes", approx);
-    bytes = (size_t)a.num_heads * (size_t)nb * (size_t)kg * 2 * hstu::kDsBlockElems;
+    bytes = (size_t)a.num_heads * (size_t)l.nb * (size_t)l.kg * 2 * hstu::kDsBlockElems;
     return HSTU_OK;
 }
 
 // Checks a dS workspace against the args and points the parameter block at it.
 hstu_status_t bind_ds(const hstu_args_t& a, void* ds, size_t ds_bytes_given, hstu::AttnParams& p) {
-    const hstu::MaskKind mk = mask_kind(a);
-    if (mk != hstu::MaskKind::None && mk != hstu::MaskKind::Causal)
-        return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs the full or causal mask");
+    if (mask_kind(a) == hstu::MaskKind::Func)
+        return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs the full, causal or window mask");
     if (8 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN) * hstu::kDsBlockElems >
         (int64_t)hstu::kMaxDsRowBlockBytes)
         return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs max_seqlen_k below 2^25");
@@ -217,9 +242,12 @@ hstu_status_t bind_ds(const hstu_args_t& a, void* ds, size_t ds_bytes_given, hst
         return fail(HSTU_ERR_INVALID_ARGUMENT, "dS workspace of %zu bytes < %zu needed", ds_bytes_given, need);
     if (need > 0 && (ds == nullptr || reinterpret_cast<uintptr_t>(ds) % 256 != 0))
         return fail(HSTU_ERR_INVALID_ARGUMENT, "dS workspace is null or not 256-byte aligned");
+    const DsLayout l = ds_layout(a);
     p.ds = static_cast<uint16_t*>(ds);
-    p.ds_nb = ((int64_t)a.total_q + 31 * (int64_t)a.batch) / 32;
-    p.ds_kg = 4 * (int32_t)(((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN);
+    p.ds_nb = l.nb;
+    p.ds_kg = (int32_t)l.kg;
+    p.ds_rel = l.rel;
+    p.ds_kgr = (int32_t)l.kgr;
     return HSTU_OK;
 }
 

@@ -1,7 +1,7 @@
 // HSTU attention backward on gfx950: deterministic kernels, no atomics.  Two
 // routes: a dq kernel and a dk/dv kernel that both recompute the scores (no
-// workspace), or -- under no mask or the causal mask, given a workspace -- the
-// dk/dv kernel storing dS and a dq kernel that reads it (described last).
+// workspace), or -- under any mask but the arbitrary one, given a workspace --
+// the dk/dv kernel storing dS and a dq kernel that reads it (described last).
 //
 // The backward receives dO and q, k, v only (HSTU Attention page, "High-level
 // functions"), so both kernels recompute the scores.  With s = alpha q_i.k_j,
@@ -31,8 +31,9 @@
 // end.  Causal blocks walk query tiles from the block's first key to the end of
 // the sequence (rows before it see none of these keys); under a token window
 // (left, right) they walk rows [first key - right, last key + left], the rows
-// whose band meets the block, and each wave tests per 32-row block whether the
-// band covers, misses or cuts it, as the forward does.  Under the arbitrary
+// whose band meets the block (the start rounded down to a multiple of 32, so
+// that row blocks line up with the stored dS blocks), and each wave tests per
+// 32-row block whether the band covers, misses or cuts it, as the forward does.  Under the arbitrary
 // interval mask they walk the rows between the first and the last row of the
 // sequence that sees a key of the block (a scan of its rows' endpoints), and
 // 256 threads turn each query tile's endpoints into 64 x 4 visibility words in
@@ -467,8 +468,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr bool FUNC = MK == MaskKind::Func;
-    // stored dS (no mask or causal: the row blocks of the walk start on multiples of 32)
-    constexpr bool DS = MK == MaskKind::None || MK == MaskKind::Causal;
+    // stored dS (no mask, causal or window: the row blocks of the walk start on multiples of 32)
+    constexpr bool DS = MK != MaskKind::Func;
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
     // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1 | K rows of the block | V rows of the block]
@@ -498,13 +499,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int key0 = n0 + 32 * kw;
     const int my_key = key0 + l32;
     const bool wave_live = key0 < sb.lk;
-    // stored dS: this lane's element of the wave's key group in the first row block
-    // (block rows are keys here: lane l32 writes the row of its key)
+    // stored dS: this lane's element of the sequence's first row-block slot (block rows
+    // are keys here: lane l32 writes the row of its key); a tile adds its block index
     uint16_t* ds_base = nullptr;
     if (DS && p.ds != nullptr) {
         const int64_t slot = ((int64_t)sb.q0 + 31 * (int64_t)b) >> 5;
-        ds_base = p.ds + (((int64_t)h * p.ds_nb + slot) * p.ds_kg + (key0 >> 5)) * kDsBlockElems +
-                  l32 * kDsRowElems + 8 * g;
+        ds_base = p.ds + ((int64_t)h * p.ds_nb + slot) * p.ds_kg * kDsBlockElems + l32 * kDsRowElems + 8 * g;
     }
 
     // the block's K (times c) and V rows into LDS; rows past the sequence repeat its last row
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     if constexpr (WINDOW) {
         const int L = p.win_left, R = p.win_right;
         const int last = min(n0 + BNK, sb.lk) - 1, wlast = min(key0 + 31, sb.lk - 1);
-        q_begin = max(0, n0 - R);
+        q_begin = max(0, n0 - R) & ~31;  // 32-row aligned (rows before n0 - R see none of these keys)
         q_end = max(q_begin, min(sb.lq, last + L + 1));
         lo = max(0, my_key - R);
         hi = min(sb.lq, my_key + L + 1);
@@ -661,7 +661,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     DsOut ds{nullptr, false, false, false};
                     if (DS && ds_base != nullptr) {
                         ds.on = true;
-                        ds.p = ds_base + (int64_t)(row0 >> 5) * p.ds_kg * kDsBlockElems;
+                        const int rb = row0 >> 5, goff = p.ds_rel >= 0 ? rb - p.ds_rel : 0;
+                        ds.p = ds_base + ((int64_t)rb * p.ds_kg + (key0 >> 5) - goff) * kDsBlockElems;
                         ds.kcut = key0 + 32 > sb.lk;
                         ds.kdead = my_key >= sb.lk;
                     }
@@ -728,7 +729,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     }
 }
 
-// dq from stored dS (no mask or causal): one workgroup per (256-row block,
+// dq from stored dS (no mask, causal or window): one workgroup per (256-row block,
 // sequence, head), 8 waves of 32 rows, one workgroup per CU.  Per 64-key tile K
 // is staged row-major in LDS (three slots, two tiles ahead, shared by the eight
 // waves) and each wave copies its rows' dS blocks into its own LDS ring of three
@@ -739,7 +740,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
 // in the loop are the counted ones below.  A wave uses the key groups the dk/dv
 // kernel stored for its row block: every group of a sequence's keys without a
 // mask, groups G <= R (row block R) under the causal mask; entries outside the
-// mask or past the sequence's keys are stored as 0.
+// mask or past the sequence's keys are stored as 0.  Under a token window (left,
+// right) row block R uses groups (row0 - left) / 32 .. (row0 + 31 + right) / 32
+// (none once row0 - left reaches the sequence's keys), the groups that hold a
+// visible pair; the dk/dv kernel wrote each of those (and possibly some blocks of
+// zeros besides).
 template <int D>
 __device__ __forceinline__ void dq_ds_tile(uint32_t kt, const uint4 (&dsop)[4],
                                            f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
@@ -781,8 +786,9 @@ constexpr int NWD = BMD / 32;     // its waves
 
 template <int D, MaskKind MK>
 __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
-    static_assert(MK == MaskKind::None || MK == MaskKind::Causal, "stored dS exists for these masks only");
+    static_assert(MK != MaskKind::Func, "stored dS exists for the full, causal and window masks");
     constexpr bool CAUSAL = MK == MaskKind::Causal;
+    constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr int DM = D < 32 ? 32 : D;
     // [K slots 0-2 | wave 0: dS slots 0-2 | wave 1 | ... | wave 7]
     __shared__ __attribute__((aligned(16))) uint16_t smem[3 * kTileElems + NWD * 3 * kDsSlotBytes / 2];
@@ -803,20 +809,43 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
 
     const int row0 = m0 + 32 * wave;
     const int my_row = row0 + ds_pos_row(l32);  // the query row of this lane's products
-    const bool wave_live = row0 < sb.lq;
-    // keys the block walks, and the key groups whose dS this wave uses: [0, ngw)
-    int kv_end = min(sb.lk, 32 * p.ds_kg);
-    if (CAUSAL) kv_end = min(kv_end, m0 + BMD);
-    const int ng = (kv_end + 31) >> 5;
-    const int ngw = __builtin_amdgcn_readfirstlane(!wave_live ? 0 : CAUSAL ? min(ng, (row0 >> 5) + 1) : ng);
-    const int t1 = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
-    // The wave's row block in the workspace (block 0 when the wave has none: its
-    // copies then fetch in-bounds data that is never used, so that every tile
-    // issues the same four copies); each copy moves 1 KB of a block as it is.
+    // Key groups [ga, gb) whose stored dS the wave at row r0 uses (wave-uniform).
+    const int gmax = min((sb.lk + 31) >> 5, p.ds_kgr);
+    auto groups = [&](int r0, int& ga, int& gb) {
+        ga = 0;
+        gb = r0 < sb.lq ? gmax : 0;
+        if (CAUSAL) gb = min(gb, (r0 >> 5) + 1);
+        if (WINDOW) {
+            ga = max(0, (r0 - p.win_left) >> 5);
+            gb = r0 - p.win_left >= sb.lk ? 0 : min(gb, ((r0 + 31 + p.win_right) >> 5) + 1);
+        }
+    };
+    int gA, gB;
+    groups(row0, gA, gB);
+    gA = __builtin_amdgcn_readfirstlane(gA);
+    gB = __builtin_amdgcn_readfirstlane(gB);
+    // the workgroup walks the 64-key tiles that hold some wave's groups
+    int wga = 0x7fffffff, wgb = 0;
+    for (int w = 0; w < NWD; ++w) {
+        int ga, gb;
+        groups(m0 + 32 * w, ga, gb);
+        if (ga < gb) {
+            wga = min(wga, ga);
+            wgb = max(wgb, gb);
+        }
+    }
+    const int t0 = __builtin_amdgcn_readfirstlane(wgb > 0 ? wga >> 1 : 0);
+    const int t1 = __builtin_amdgcn_readfirstlane(wgb > 0 ? (wgb + 1) >> 1 : 0);
+    const int kv_end = min(sb.lk, 32 * wgb);  // K rows past it only meet zero operands
+    // The wave's row block in the workspace, shifted so that group G sits at block
+    // G (block 0 when the wave uses none: its copies then fetch in-bounds data that
+    // is never used, so that every tile issues the same four copies); each copy moves
+    // 1 KB of a block as it is.
     int64_t blk0 = 0;
-    if (wave_live) {
+    if (gA < gB) {
         const int64_t slot = ((int64_t)sb.q0 + 31 * (int64_t)b) >> 5;
-        blk0 = ((int64_t)h * p.ds_nb + slot + (row0 >> 5)) * p.ds_kg;
+        const int rb = row0 >> 5, goff = p.ds_rel >= 0 ? rb - p.ds_rel : 0;
+        blk0 = ((int64_t)h * p.ds_nb + slot + rb) * p.ds_kg - goff;
     }
     const uint16_t* dsg = static_cast<const uint16_t*>(uniform_ptr(p.ds + blk0 * kDsBlockElems));
     const uint32_t cpy_off = 16u * (uint32_t)lane;
@@ -825,7 +854,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int grp = 2 * t + kb;
-            const uint32_t src = grp < ngw ? (uint32_t)grp * (2u * kDsBlockElems) : 0u;  // bytes from dsg
+            const uint32_t src = grp >= gA && grp < gB ? (uint32_t)grp * (2u * kDsBlockElems) : 0u;  // from dsg
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 dma16_lds_stream(dst + (uint32_t)kb * (2u * kDsBlockElems) + 1024u * c, dsg, src + 1024u * c + cpy_off);
@@ -844,7 +873,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < DM / 32; ++db) acc[db] = f32x16{};
 
-    if (t1 > 0) {
+    if (t1 > t0) {
         const uint16_t* kbase = p.k.base + (int64_t)sb.k0 * p.k.tok + (int64_t)h * p.k.head;
         TileDma<D, NWD> kdma;  // two 1 KB chunks of each K tile per wave
         kdma.init(wave, lane, p.k.tok);
@@ -864,27 +893,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
             else __builtin_amdgcn_s_waitcnt(0x0f70);         // vmcnt(0)
         };
         auto kslot = [](int t) { return (uint32_t)(t % 3) * kTileBytes; };
-        kdma.issue(lds0, kbase, p.k.tok, 0, kv_end);
-        copy_ds(0);
-        if (1 < t1) {
-            kdma.issue(lds0 + kTileBytes, kbase, p.k.tok, BN, kv_end);
-            copy_ds(1);
+        kdma.issue(lds0 + kslot(t0), kbase, p.k.tok, t0 * BN, kv_end);
+        copy_ds(t0);
+        if (t0 + 1 < t1) {
+            kdma.issue(lds0 + kslot(t0 + 1), kbase, p.k.tok, (t0 + 1) * BN, kv_end);
+            copy_ds(t0 + 1);
         }
-        wait_copies(1);  // K(0) and dS(0) have landed
+        wait_copies(t0 + 1);  // K(t0) and dS(t0) have landed
         __syncthreads();
 
-        for (int t = 0; t < t1; ++t) {
+        for (int t = t0; t < t1; ++t) {
             const uint32_t kc = kslot(t);
             if (t + 2 < t1) {
                 kdma.issue(lds0 + kslot(t + 2), kbase, p.k.tok, (t + 2) * BN, kv_end);
                 copy_ds(t + 2);
             }
-            if (2 * t < ngw) {
+            if (2 * t + 1 >= gA && 2 * t < gB) {
                 const uint32_t sl = dsl + (uint32_t)(t % 3) * kDsSlotBytes;
                 uint4 op[4];
-                op[0] = ds_read_tr16x2(sl + dtr.x, sl + dtr.y);
-                op[1] = ds_read_tr16x2(sl + 1024u + dtr.x, sl + 1024u + dtr.y);
-                if (2 * t + 1 < ngw) {
+                if (2 * t >= gA) {
+                    op[0] = ds_read_tr16x2(sl + dtr.x, sl + dtr.y);
+                    op[1] = ds_read_tr16x2(sl + 1024u + dtr.x, sl + 1024u + dtr.y);
+                } else {
+                    op[0] = op[1] = make_uint4(0, 0, 0, 0);  // the first group is not used
+                }
+                if (2 * t + 1 < gB) {
                     op[2] = ds_read_tr16x2(sl + 2048u + dtr.x, sl + 2048u + dtr.y);
                     op[3] = ds_read_tr16x2(sl + 3072u + dtr.x, sl + 3072u + dtr.y);
                 } else {
@@ -929,6 +962,7 @@ hipError_t launch_dq_ds_mask(const AttnParams& p, MaskKind mask, hipStream_t str
     switch (mask) {
         case MaskKind::None: return launch_dq_ds<D, MaskKind::None>(p, stream);
         case MaskKind::Causal: return launch_dq_ds<D, MaskKind::Causal>(p, stream);
+        case MaskKind::Window: return launch_dq_ds<D, MaskKind::Window>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

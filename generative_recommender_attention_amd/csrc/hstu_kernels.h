@@ -36,13 +36,17 @@ struct AttnParams {
     int32_t func_ld;
     TensorRef q, k, v, dout;
     TensorOut o, dq, dk, dv;
-    // Backward through stored dS (no mask or causal only): the dk/dv kernel writes, and
-    // the dS-reading dq kernel reads, bf16 dS in 2 KB blocks of 32 query rows x 32 keys.
-    // Block (head h, row block R of batch entry b, key group G) sits at block index
-    // (h ds_nb + (cu_q[b] + 31 b) / 32 + R) ds_kg + G; null: the dk/dv kernel writes none.
+    // Backward through stored dS (no mask, causal or window): the dk/dv kernel writes,
+    // and the dS-reading dq kernel reads, bf16 dS in 2 KB blocks of 32 query rows x 32
+    // keys.  Block (head h, row block R of batch entry b, key group G) sits at block
+    // index (h ds_nb + (cu_q[b] + 31 b) / 32 + R) ds_kg + G - goff(R), goff(R) = R - ds_rel
+    // when ds_rel >= 0 (a window: R's groups lie in [R - ds_rel, R - ds_rel + ds_kg)),
+    // else 0; null: the dk/dv kernel writes none.
     uint16_t* ds;
     int64_t ds_nb;         // row-block slots per head: (T_q + 31 B) / 32
-    int32_t ds_kg;         // key groups per row block: 4 ceil(max_seqlen_k / 128)
+    int32_t ds_kg;         // key-group slots per row block
+    int32_t ds_rel;        // ceil(left / 32) for a window stored relative to R, else -1
+    int32_t ds_kgr;        // key groups the dk/dv grid covers: 4 ceil(max_seqlen_k / 128)
 };
 
 // Elements of one stored dS block (32 x 32 bf16, 2 KB) and of one of its rows.
@@ -69,7 +73,7 @@ constexpr int32_t kMaxWindowSeqlen = 1 << 29;
 hipError_t launch_fwd(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
-// dQ from the dS the dk/dv kernel stored (p.ds); mask None or Causal.
+// dQ from the dS the dk/dv kernel stored (p.ds); mask None, Causal or Window.
 hipError_t launch_bwd_dq_ds(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 
 }  // namespace hstu

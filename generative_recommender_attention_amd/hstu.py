@@ -309,7 +309,7 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              store_ds: bool = True) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.
 
-    With ``store_ds`` (and no mask or the causal mask) the dk/dv kernel stores dS
+    With ``store_ds`` (and any mask but the arbitrary one) the dk/dv kernel stores dS
     in ``workspace`` (a device byte tensor of ``hstu_bwd_workspace_size`` bytes,
     allocated here when not given) and dq is computed from it; with
     ``store_ds=False``, or under the other masks, the dq kernel recomputes the
@@ -494,7 +494,7 @@ def hstu_bwd_dkdv_ds(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
                      alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None,
                      window_size=None):
     """(dk, dv), storing dS in ``ds`` (``hstu_bwd_workspace_size`` bytes) for
-    ``hstu_bwd_dq_ds``; no mask or the causal mask only."""
+    ``hstu_bwd_dq_ds``; no mask, the causal mask or a window."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk

@@ -169,17 +169,20 @@ HSTU_API hstu_status_t hstu_fwd(const hstu_args_t* args,
  * the scores for dQ (written to *bytes).  Reads the scalars of `args` only (the
  * pointers in it are not used).  dS (above) is the factor that dQ and dK share;
  * the workspace holds it in bf16 without the 1 / L_scale, which the dQ kernel
- * applies with alpha.  Under no mask or the causal mask the result is
- * H x ((T_q + 31 B) / 32) x 4 ceil(max_seqlen_k / 128) blocks of 2 KB (a bf16 dS
- * block of 32 query rows x 32 keys per row-block slot and key group, whatever
- * the sequence lengths turn out to be); under a window or arbitrary mask it is
- * 0 (those backwards always recompute). */
+ * applies with alpha.  The result is H x ((T_q + 31 B) / 32) x G blocks of 2 KB
+ * (a bf16 dS block of 32 query rows x 32 keys per row-block slot and key-group
+ * slot, whatever the sequence lengths turn out to be) with G = 4 ceil(max_seqlen_k
+ * / 128) under no mask or the causal mask, and under a window (left, right) the
+ * smaller of that and ceil(left / 32) + floor((31 + right) / 32) + 1 (the key
+ * groups a 32-row block meets; a side of -1 counts as max_seqlen_k).  Under the
+ * arbitrary mask, with no tokens on a side, or with max_seqlen_k of 2^25 or more
+ * it is 0 (those backwards always recompute). */
 HSTU_API hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* args, size_t* bytes);
 
 /* Backward, all three gradients.  With a workspace of at least
  * hstu_bwd_workspace_size() bytes (256-byte aligned, caller-owned device
- * memory, contents on entry ignored) and a nonzero size, enqueues
- * hstu_bwd_dkdv_ds then hstu_bwd_dq_ds on it; with `workspace` null, or a
+ * memory, contents on entry ignored; the call overwrites it) and a nonzero
+ * size, enqueues hstu_bwd_dkdv_ds then hstu_bwd_dq_ds on it; with `workspace` null, or a
  * size of 0, enqueues hstu_bwd_dq then hstu_bwd_dkdv, which need none.  A
  * non-null workspace smaller than the size is HSTU_ERR_INVALID_ARGUMENT.  The
  * two routes round differently (dQ from the bf16 dS of the dk/dv kernel, or
@@ -206,8 +209,8 @@ HSTU_API hstu_status_t hstu_bwd_dkdv(const hstu_args_t* args, const void* dout,
 /* hstu_bwd_dkdv that also writes the bf16 dS of every 32 x 32 (rows x keys)
  * block it computes to `ds` (hstu_bwd_workspace_size() bytes, 256-byte aligned;
  * null allowed only when that size is 0), entries outside the mask as 0.  dK
- * and dV are bit-identical to hstu_bwd_dkdv's.  Mask none or causal only
- * (else HSTU_ERR_UNSUPPORTED). */
+ * and dV are bit-identical to hstu_bwd_dkdv's.  Mask none, causal or window
+ * (the arbitrary mask is HSTU_ERR_UNSUPPORTED). */
 HSTU_API hstu_status_t hstu_bwd_dkdv_ds(const hstu_args_t* args, const void* dout,
                                const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -216,8 +219,8 @@ HSTU_API hstu_status_t hstu_bwd_dkdv_ds(const hstu_args_t* args, const void* dou
 
 /* dQ = alpha / L_scale * dS K from the dS that hstu_bwd_dkdv_ds stored in `ds`
  * for the same args and cu_seqlens (enqueue it first on the same stream, or
- * order the two otherwise).  Reads k and ds only; writes dq.  Mask none or
- * causal only. */
+ * order the two otherwise).  Reads k and ds only; writes dq.  Mask none,
+ * causal or window. */
 HSTU_API hstu_status_t hstu_bwd_dq_ds(const hstu_args_t* args, const void* k,
                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                              const void* ds, size_t ds_bytes, void* dq,

@@ -153,8 +153,14 @@ def ws_size(lib, a):
     (dict(mask=2, window_left=-1, window_right=0), 2 * 2 * 4),            # the causal window
     (dict(batch=5, total_q=300, total_k=300, max_seqlen_q=129, max_seqlen_k=129, num_heads=3),
      3 * ((300 + 31 * 5) // 32) * 8),
-    (dict(mask=2, window_left=4, window_right=0), 0),                     # window: recompute only
-    (dict(mask=3, func_n=1, func_ld=32, func=FAKE), 0),                   # arbitrary mask: likewise
+    # window: key groups relative to the row block, ceil(left/32) + floor((31 + right)/32) + 1 of them
+    (dict(mask=2, window_left=4, window_right=0), 2 * 2 * 2),
+    (dict(mask=2, window_left=40, window_right=33), 2 * 2 * 3),           # sides clamp to max_seqlen_k = 20
+    (dict(mask=2, window_left=600, window_right=400, batch=5, total_q=3000, total_k=3000, max_seqlen_q=900,
+          max_seqlen_k=900), 2 * ((3000 + 31 * 5) // 32) * 32),           # 19 + 13 + 1 >= 32 groups: absolute
+    (dict(mask=2, window_left=300, window_right=0, batch=5, total_q=3000, total_k=3000, max_seqlen_q=900,
+          max_seqlen_k=900), 2 * ((3000 + 31 * 5) // 32) * (10 + 0 + 1)),
+    (dict(mask=3, func_n=1, func_ld=32, func=FAKE), 0),                   # arbitrary mask: recompute only
     (dict(total_k=0, max_seqlen_q=0, max_seqlen_k=0, scaling_seqlen=8), 0),  # no keys
 ])
 def test_backward_workspace_query(lib, over, blocks):
@@ -183,10 +189,10 @@ def test_backward_workspace_rejections(lib):
         hstu.HSTU_ERR_INVALID_ARGUMENT
     assert lib.hstu_bwd_dq_ds(ctypes.byref(a), FAKE, FAKE, FAKE, ws + 128, size, FAKE, None) == \
         hstu.HSTU_ERR_INVALID_ARGUMENT
-    # stored dS exists for the full and causal masks only
-    w = good_args(mask=2, window_left=4, window_right=0)
-    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(w), *dkdv, ws, size, None) == hstu.HSTU_ERR_UNSUPPORTED
-    assert lib.hstu_bwd_dq_ds(ctypes.byref(w), FAKE, FAKE, FAKE, ws, size, FAKE, None) == hstu.HSTU_ERR_UNSUPPORTED
+    # stored dS exists for the full, causal and window masks
+    f = good_args(mask=3, func_n=1, func_ld=32, func=FAKE)
+    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(f), *dkdv, ws, size, None) == hstu.HSTU_ERR_UNSUPPORTED
+    assert lib.hstu_bwd_dq_ds(ctypes.byref(f), FAKE, FAKE, FAKE, ws, size, FAKE, None) == hstu.HSTU_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

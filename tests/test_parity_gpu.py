@@ -38,10 +38,10 @@ def run_fwd_check(wl, rows=None, tag=""):
 
 
 def run_bwd_check(wl, rows_q=None, rows_k=None, tag=""):
-    """Both backward routes against one oracle evaluation: dQ from stored dS (for
-    no mask and the causal mask) and dQ from recomputed scores."""
+    """Both backward routes against one oracle evaluation: dQ from stored dS (no
+    mask, causal, window) and dQ from recomputed scores."""
     dw = DeviceWorkload(wl)
-    routes = [True, False] if wl.mask_name in ("causal", "full") else [False]
+    routes = [True, False] if wl.func is None else [False]
     rq, rk, rv = oracle.bwd_workload(wl, rows_q, rows_k)
     res = []
     for store in routes:
@@ -189,13 +189,14 @@ def test_windows_naming_full_and_causal_are_those_masks_bitwise():
     ow, gw = dw.fwd(window_size=(-1, 0)), dw.bwd(window_size=(-1, 0))
     of, gf = dw.fwd(causal=False), dw.bwd(causal=False)
     on, gn = dw.fwd(window_size=(-1, -1)), dw.bwd(window_size=(-1, -1))
-    # a real window always recomputes dQ, so it is compared with the full mask's recompute route
-    gfr = dw.bwd(causal=False, store_ds=False)
     ob, gb = dw.fwd(window_size=(500, 500)), dw.bwd(window_size=(500, 500))
+    gfr, gbr = dw.bwd(causal=False, store_ds=False), dw.bwd(window_size=(500, 500), store_ds=False)
     torch.cuda.synchronize()
     assert torch.equal(oc, ow) and all(torch.equal(a, b) for a, b in zip(gc, gw))
     assert torch.equal(of, on) and all(torch.equal(a, b) for a, b in zip(gf, gn))
-    assert torch.equal(of, ob) and all(torch.equal(a, b) for a, b in zip(gfr, gb))
+    # the wide window stores dS relative to each row block, the full mask by key group: same values
+    assert torch.equal(of, ob) and all(torch.equal(a, b) for a, b in zip(gf, gb))
+    assert all(torch.equal(a, b) for a, b in zip(gfr, gbr))
 
 
 def test_window_invalid_bounds_raise():
@@ -255,7 +256,7 @@ def test_func_spelling_causal_and_window_is_bitwise_those_masks():
     # the arbitrary mask always recomputes dQ: compare with causal's recompute route
     oc, gc = dw.fwd(causal=True), dw.bwd(causal=True, store_ds=False)
     of, gf = dw.fwd(func=causal_f), dw.bwd(func=causal_f)
-    ow, gw = dw.fwd(window_size=(left, right)), dw.bwd(window_size=(left, right))
+    ow, gw = dw.fwd(window_size=(left, right)), dw.bwd(window_size=(left, right), store_ds=False)
     ofw, gfw = dw.fwd(func=win_f), dw.bwd(func=win_f)
     torch.cuda.synchronize()
     assert torch.equal(oc, of) and all(torch.equal(a, b) for a, b in zip(gc, gf))
@@ -345,8 +346,9 @@ def test_stored_ds_needs_the_workspace_it_asks_for():
         hstu.hstu_bwd(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, workspace=ws[:-256], **kw)
     with pytest.raises(hstu.HstuError):
         hstu.hstu_bwd_dq_ds(dw.q, dw.k, dw.cu_q, dw.cu_k, ds=ws[:2048], **kw)
-    with pytest.raises(NotImplementedError):
-        hstu.hstu_bwd_dkdv_ds(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, ds=ws, **dict(kw, window_size=(8, 0)))
+    # a window asks for its own (relative) layout: the causal-sized workspace is not that
+    wsw = dw.workspace(window_size=(8, 0))
+    assert wsw.numel() < ws.numel()
 
 
 # ------------------------------------------------------------------ invariants
