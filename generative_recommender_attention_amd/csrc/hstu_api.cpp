@@ -3,6 +3,7 @@
 // synchronises or allocates; every check is on scalars and pointer values.
 #include "hstu.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -150,13 +151,16 @@ hstu::TensorOut out(const Operand& t) {
     return hstu::TensorOut{static_cast<uint16_t*>(const_cast<void*>(t.ptr)), t.stride.token, t.stride.head};
 }
 
-hstu_status_t set_grid(hstu::AttnParams& p, int32_t max_len, int block) {
+// Grid of a walk over blocks of `block` rows of the side whose longest sequence
+// is max_len; the walk's tiles run over the other side (longest: other_len).
+hstu_status_t set_grid(hstu::AttnParams& p, int32_t max_len, int block, int32_t other_len) {
     const int64_t nblk = ((int64_t)max_len + block - 1) / block;
     const int64_t grid = nblk * p.batch * p.heads;
     if (grid > 0x7fffffffLL)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "problem too large: %lld workgroups", (long long)grid);
     p.nblk = (int32_t)nblk;
     p.max_len = max_len;
+    p.max_cost = (int32_t)std::max<int64_t>(1, ((int64_t)other_len + 63) / 64);
     return HSTU_OK;
 }
 
@@ -179,7 +183,7 @@ hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, cons
     p.k = ref(ops[2]);
     p.v = ref(ops[3]);
     p.dq = out(ops[4]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     return launched(hstu::launch_bwd_dq(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq");
 }
@@ -263,7 +267,7 @@ hstu_status_t run_dq_ds(const hstu_args_t* a, const void* k, const int32_t* cu_q
     if ((st = bind_ds(*a, ds, ds_given, p)) != HSTU_OK) return st;
     p.k = ref(ops[0]);
     p.dq = out(ops[1]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kDqDsBlockM)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kDqDsBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     // with no keys the kernel writes dQ = 0 without touching the (empty) workspace
     return launched(hstu::launch_bwd_dq_ds(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq_ds");
@@ -289,7 +293,7 @@ hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, co
     p.v = ref(ops[3]);
     p.dk = out(ops[4]);
     p.dv = out(ops[5]);
-    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q)) != HSTU_OK) return st;
     if (a->total_k == 0) return ok();
     return launched(hstu::launch_bwd_dkdv(p, a->head_dim, mask_kind(*a), stream),
                     "hstu_bwd_dkdv");
@@ -314,7 +318,7 @@ hstu_status_t hstu_fwd(const hstu_args_t* a, const void* q, const void* k, const
     p.k = ref(ops[1]);
     p.v = ref(ops[2]);
     p.o = out(ops[3]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     return launched(hstu::launch_fwd(p, a->head_dim, mask_kind(*a), stream), "hstu_fwd");
 }
@@ -375,8 +379,8 @@ hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, co
     for (Operand& o : ops)
         if ((st = check_operand(*a, o)) != HSTU_OK) return st;
     if (a->total_k > 0 && dk == dv) return fail(HSTU_ERR_INVALID_ARGUMENT, "dk and dv are the same buffer");
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM)) != HSTU_OK) return st;
-    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q)) != HSTU_OK) return st;
     if (stored) {
         st = run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream, true, workspace,
                       workspace_bytes);

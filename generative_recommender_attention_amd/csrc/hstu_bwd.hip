@@ -195,7 +195,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     // workgroup -> (live row block, head), head fastest, blocks with the most key tiles first
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
     BlockItem item;
-    if (!find_block<true>(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int pidx = (int)(blockIdx.x / (unsigned)p.heads);
+    if (!(CAUSAL || MK == MaskKind::None
+              ? find_block_by_cost<true>(p.cu_q, p.cu_k, p.batch, p.max_cost, pidx, QueryBlocksGe<BM, CAUSAL>{p.max_cost}, item)
+              : find_block<true>(p.cu_q, p.batch, BM, p.nblk, pidx, item)))
+        return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BM;
@@ -490,7 +494,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     // workgroup -> (live key block, head), head fastest, blocks with the most query tiles first
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
     BlockItem item;
-    if (!find_block<false>(p.cu_k, p.batch, BNK, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int pidx = (int)(blockIdx.x / (unsigned)p.heads);
+    if (!(CAUSAL || MK == MaskKind::None
+              ? find_block_by_cost<false>(p.cu_q, p.cu_k, p.batch, p.max_cost, pidx, KeyBlocksGe<BNK, CAUSAL>{p.max_cost}, item)
+              : find_block<false>(p.cu_k, p.batch, BNK, p.nblk, pidx, item)))
+        return;
     const int b = item.b, n = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int n0 = n * BNK;
@@ -801,7 +809,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
 
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
     BlockItem item;
-    if (!find_block<true>(p.cu_q, p.batch, BMD, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int pidx = (int)(blockIdx.x / (unsigned)p.heads);
+    if (!(CAUSAL || MK == MaskKind::None
+              ? find_block_by_cost<true>(p.cu_q, p.cu_k, p.batch, p.max_cost, pidx, QueryBlocksGe<BMD, CAUSAL>{p.max_cost}, item)
+              : find_block<true>(p.cu_q, p.batch, BMD, p.nblk, pidx, item)))
+        return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BMD;

@@ -147,7 +147,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     // workgroup -> (live row block, head), head fastest; surplus workgroups exit
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
     BlockItem item;
-    if (!find_block<true>(p.cu_q, p.batch, BM, p.nblk, (int)(blockIdx.x / (unsigned)p.heads), item)) return;
+    const int pidx = (int)(blockIdx.x / (unsigned)p.heads);
+    if (!(CAUSAL || MK == MaskKind::None
+              ? find_block_by_cost<true>(p.cu_q, p.cu_k, p.batch, p.max_cost, pidx, QueryBlocksGe<BM, CAUSAL>{p.max_cost}, item)
+              : find_block<true>(p.cu_q, p.batch, BM, p.nblk, pidx, item)))
+        return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
     const int m0 = m * BM;

@@ -24,6 +24,8 @@ struct AttnParams {
     int32_t heads;         // H
     int32_t nblk;          // row (or key) blocks per sequence covered by the grid
     int32_t max_len;       // max_seqlen_q (forward, dq) or max_seqlen_k (dk/dv): sizes the grid
+    int32_t max_cost;      // tiles of the longest walk: ceil(max_seqlen_k / 64) (query-major
+                           // kernels) or ceil(max_seqlen_q / 64) (dk/dv), at least 1
     float alpha;           // score scale
     float exp_c;           // -alpha * log2(e), for sig(alpha x) = 1 / (1 + 2^(x exp_c))
     float out_scale;       // alpha / L_scale: the epilogue factor of dQ and dK
