@@ -152,13 +152,17 @@ hstu::TensorOut out(const Operand& t) {
 }
 
 // Grid of a walk over blocks of `block` rows of the side whose longest sequence
-// is max_len; the walk's tiles run over the other side (longest: other_len).
-hstu_status_t set_grid(hstu::AttnParams& p, int32_t max_len, int block, int32_t other_len) {
+// is max_len and whose tokens number total; the walk's tiles run over the other
+// side (longest: other_len).  The live blocks number at most nblk B and at most
+// sum_b ceil(L_b / block) <= (total + (block - 1) B) / block.
+hstu_status_t set_grid(hstu::AttnParams& p, int32_t max_len, int block, int32_t other_len, int32_t total) {
     const int64_t nblk = ((int64_t)max_len + block - 1) / block;
-    const int64_t grid = nblk * p.batch * p.heads;
+    const int64_t items = std::min<int64_t>(nblk * p.batch, ((int64_t)total + (int64_t)(block - 1) * p.batch) / block);
+    const int64_t grid = items * p.heads;
     if (grid > 0x7fffffffLL)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "problem too large: %lld workgroups", (long long)grid);
     p.nblk = (int32_t)nblk;
+    p.items = (int32_t)items;
     p.max_len = max_len;
     p.max_cost = (int32_t)std::max<int64_t>(1, ((int64_t)other_len + 63) / 64);
     return HSTU_OK;
@@ -183,7 +187,7 @@ hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, cons
     p.k = ref(ops[2]);
     p.v = ref(ops[3]);
     p.dq = out(ops[4]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k, a->total_q)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     return launched(hstu::launch_bwd_dq(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq");
 }
@@ -267,7 +271,7 @@ hstu_status_t run_dq_ds(const hstu_args_t* a, const void* k, const int32_t* cu_q
     if ((st = bind_ds(*a, ds, ds_given, p)) != HSTU_OK) return st;
     p.k = ref(ops[0]);
     p.dq = out(ops[1]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kDqDsBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kDqDsBlockM, a->max_seqlen_k, a->total_q)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     // with no keys the kernel writes dQ = 0 without touching the (empty) workspace
     return launched(hstu::launch_bwd_dq_ds(p, a->head_dim, mask_kind(*a), stream), "hstu_bwd_dq_ds");
@@ -293,7 +297,7 @@ hstu_status_t run_dkdv(const hstu_args_t* a, const void* dout, const void* q, co
     p.v = ref(ops[3]);
     p.dk = out(ops[4]);
     p.dv = out(ops[5]);
-    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q, a->total_k)) != HSTU_OK) return st;
     if (a->total_k == 0) return ok();
     return launched(hstu::launch_bwd_dkdv(p, a->head_dim, mask_kind(*a), stream),
                     "hstu_bwd_dkdv");
@@ -318,7 +322,7 @@ hstu_status_t hstu_fwd(const hstu_args_t* a, const void* q, const void* k, const
     p.k = ref(ops[1]);
     p.v = ref(ops[2]);
     p.o = out(ops[3]);
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k, a->total_q)) != HSTU_OK) return st;
     if (a->total_q == 0) return ok();
     return launched(hstu::launch_fwd(p, a->head_dim, mask_kind(*a), stream), "hstu_fwd");
 }
@@ -379,8 +383,8 @@ hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, co
     for (Operand& o : ops)
         if ((st = check_operand(*a, o)) != HSTU_OK) return st;
     if (a->total_k > 0 && dk == dv) return fail(HSTU_ERR_INVALID_ARGUMENT, "dk and dv are the same buffer");
-    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k)) != HSTU_OK) return st;
-    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_q, hstu::kFwdBlockM, a->max_seqlen_k, a->total_q)) != HSTU_OK) return st;
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q, a->total_k)) != HSTU_OK) return st;
     if (stored) {
         st = run_dkdv(a, dout, q, k, v, cu_seqlens_q, cu_seqlens_k, dk, dv, stream, true, workspace,
                       workspace_bytes);

@@ -963,7 +963,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
 
 template <int D, MaskKind MK>
 hipError_t launch_dq_ds(const AttnParams& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
+    const int64_t grid = (int64_t)p.items * p.heads;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_ds_kernel<D, MK>), dim3((unsigned)grid), dim3(64 * NWD), 0, stream, p);
     return hipGetLastError();
@@ -981,7 +981,7 @@ hipError_t launch_dq_ds_mask(const AttnParams& p, MaskKind mask, hipStream_t str
 
 template <int D, MaskKind MK>
 hipError_t launch_dq(const AttnParams& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
+    const int64_t grid = (int64_t)p.items * p.heads;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_kernel<D, MK>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
@@ -989,7 +989,7 @@ hipError_t launch_dq(const AttnParams& p, hipStream_t stream) {
 
 template <int D, MaskKind MK>
 hipError_t launch_dkdv(const AttnParams& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
+    const int64_t grid = (int64_t)p.items * p.heads;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
 
 template <int D, MaskKind MK>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.nblk * p.batch * p.heads;
+    const int64_t grid = (int64_t)p.items * p.heads;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((fwd_kernel<D, MK>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();

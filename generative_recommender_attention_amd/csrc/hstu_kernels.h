@@ -22,7 +22,9 @@ struct AttnParams {
     const int32_t* cu_k;   // (B + 1) cumulative key lengths, device
     int32_t batch;         // B
     int32_t heads;         // H
-    int32_t nblk;          // row (or key) blocks per sequence covered by the grid
+    int32_t nblk;          // row (or key) blocks of the longest sequence
+    int32_t items;         // bound on the live blocks: min(nblk B, (T + (block - 1) B) / block);
+                           // the grid holds items x heads workgroups
     int32_t max_len;       // max_seqlen_q (forward, dq) or max_seqlen_k (dk/dv): sizes the grid
     int32_t max_cost;      // tiles of the longest walk: ceil(max_seqlen_k / 64) (query-major
                            // kernels) or ceil(max_seqlen_q / 64) (dk/dv), at least 1
