@@ -89,6 +89,16 @@ def test_zipf_workload_fwd_bwd_sampled(oracle_lib):
     print("zipf bwd (err/max, worst per-seq):", res)
 
 
+def test_long_workload_fwd_bwd_sampled(oracle_lib):
+    # the longest walks (up to 256 tiles of 64) through both backward routes, at full size
+    rng = np.random.default_rng(3)  # the long causal workload's lengths and inputs, plus dO
+    lens = rng.integers(8192, 16384, size=4, endpoint=True)
+    wl = make_workload("long_b4_h8_d128_causal_fwdbwd", 3, lens, 8, 128, True, 0.5, rng=rng, with_do=True)
+    rows = sample_rows(wl.cu_seqlens_q, per_seq=12, seed=6)
+    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    print("long bwd (err/max, worst per-seq):", res)
+
+
 # ------------------------------------------------------------ shapes and edges
 EDGE_LENGTHS = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 200]
 
