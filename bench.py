@@ -131,7 +131,8 @@ def load_traffic(kernel: str, workload: str):
 
 
 PROFILE_COMMANDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py --no-cpu-baseline --workload {w}",
+    "kt": ("rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py "
+           "--no-cpu-baseline --workload {w} --clock-out {d}/kt/clock.json"),
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cfetch -o run -- python3 bench.py --calibrate-copy-mib 256",
@@ -201,9 +202,17 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
                 ("hstu_bwd_dkdv_ds (bwd_dkdv_kernel storing dS) + hstu_bwd_dq_ds." if stored else
                  "hstu_bwd_dq + hstu_bwd_dkdv."))
     stats = rows("kt", "*kernel_stats.csv")
+    clock_note = []
+    cpath = os.path.join(prof_dir, "kt", "clock.json")
+    if os.path.exists(cpath):
+        with open(cpath) as f:
+            clk = json.load(f)
+        clock_note = [f"Shader clock over the timed steps of the same run: {clk['shader_mhz']} MHz (mean over XCDs; "
+                      f"per XCD {clk['per_xcd_mhz']}), from s_memtime / s_memrealtime samples taken just before "
+                      "and after them.", ""]
     out = [f"# rocprofv3 kernel trace: {title}, workload {workload}", "", what, "",
            "Command (GPU box, from the repository root):",
-           "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir, w=workload), "",
+           "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir, w=workload), ""] + clock_note + [
            f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"]
@@ -323,8 +332,87 @@ def cpu_baseline(wl, max_pairs: int):
                    f"{pairs} visible pairs x {wl.num_heads} heads = {pairs / workload_pairs(wl):.1%} "
                    f"of the workload's pairs), {dt:.1f} s"),
         "seconds": dt,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
+
+
+ORACLE_CONFIGS = [  # (workload, runs): the five configurations; the long ones once
+    ("tiny_b2_h1_d16_causal", 3), ("uniform_b8_h2_d64_full", 3), ("zipf_b32_h4_d128_causal", 3),
+    ("long_b4_h8_d128_causal", 1), ("zipf_b32_h4_d128_causal_fwdbwd", 1)]
+
+
+def time_oracle_configs() -> int:
+    """Wall time of the fp64 oracle on every configuration, whole workloads, on this
+    host's threads; written to profiles/oracle_cpu_baseline.txt."""
+    import oracle
+    from generative_recommender_attention_amd.workloads import named_workload
+
+    oracle.build(force=False)
+    lines = ["# fp64 CPU oracle on the five workload configurations (whole workloads)", "",
+             f"Host: {cpu_model()}, {os.cpu_count()} logical CPUs visible, oracle threads "
+             f"(OMP_NUM_THREADS) {oracle.num_threads()}.",
+             "Command (from the repository root): python3 bench.py --oracle-configs", "",
+             "The oracle is the plain fp64 definition (libm exp, no blocking), OpenMP over output rows; "
+             "useful flops count visible pairs only (fwd 4 D H P, bwd 10 D H P).", "",
+             f"{'workload':34s}{'runs':>5s}{'median s':>10s}{'useful GFLOP':>14s}{'GFLOP/s':>10s}"]
+    out = {}
+    for name, runs in ORACLE_CONFIGS:
+        wl = named_workload(name)
+        times = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            oracle.fwd_workload(wl)
+            if wl.do is not None:
+                oracle.bwd_workload(wl)
+            times.append(time.perf_counter() - t0)
+        t = float(np.median(times))
+        per_pair = USEFUL_PER_PAIR_D["fwd"] + (USEFUL_PER_PAIR_D["bwd"] if wl.do is not None else 0)
+        flops = per_pair * wl.head_dim * wl.num_heads * workload_pairs(wl)
+        out[name] = {"runs": runs, "median_s": t, "useful_gflop": flops / 1e9, "gflops": flops / t / 1e9}
+        lines.append(f"{name:34s}{runs:5d}{t:10.3f}{flops / 1e9:14.3f}{flops / t / 1e9:10.2f}")
+        print(f"[oracle] {name}: {t:.3f} s ({runs} runs)", file=sys.stderr, flush=True)
+    with open(os.path.join(ROOT, "profiles", "oracle_cpu_baseline.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"oracle_configs": out, "cpu": cpu_model(), "threads": oracle.num_threads()}))
+    return 0
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def clock_summary(before, after) -> dict:
+    """Average shader clock of each XCD between two clock_sample launches (rows of
+    (real time at 100 MHz, shader cycles, XCC id, HW_ID)): per XCD, the median
+    cycle and real-time readings of its workgroups in each launch give
+    MHz = d(cycles) / d(real time) x 100.  counter_spread_cycles is the largest
+    spread of one XCD's cycle readings inside one launch (its workgroups start
+    within microseconds of each other, so a small spread shows the counter is
+    common to the XCD)."""
+    b, a = np.asarray(before, dtype=np.int64), np.asarray(after, dtype=np.int64)
+    per, spread = {}, 0
+    for x in sorted(set(b[:, 2].tolist()) & set(a[:, 2].tolist())):
+        sb, sa = b[b[:, 2] == x], a[a[:, 2] == x]
+        spread = max(spread, int(np.ptp(sb[:, 1])), int(np.ptp(sa[:, 1])))
+        drt = float(np.median(sa[:, 0]) - np.median(sb[:, 0]))
+        dcy = float(np.median(sa[:, 1]) - np.median(sb[:, 1]))
+        if drt > 0:
+            per[int(x)] = dcy / drt * 100.0
+    vals = list(per.values())
+    region_us = float(np.median(a[:, 0]) - np.median(b[:, 0])) / 100.0
+    return {"shader_mhz": round(float(np.mean(vals)), 1) if vals else None,
+            "per_xcd_mhz": {str(k): round(v, 1) for k, v in per.items()},
+            "region_us_by_realtime": round(region_us, 1), "counter_spread_cycles": spread,
+            "method": "s_memtime / s_memrealtime deltas per XCD between samples taken just before and after "
+                      "the timed steps on the same stream"}
 
 
 def lmsd_bytes(n: int, d: int, segs: int) -> dict:
@@ -439,11 +527,17 @@ def main(argv=None) -> int:
                     help="only write profiles/ from the rocprofv3 outputs under DIR (see PROFILE_COMMANDS)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC byte-counter calibration)")
+    ap.add_argument("--clock-out", metavar="PATH", help="also write the shader-clock reading to PATH (JSON)")
+    ap.add_argument("--oracle-configs", action="store_true",
+                    help="only time the CPU oracle on every workload configuration (median of 3 runs for the "
+                         "small ones, one run for the long ones) and write profiles/oracle_cpu_baseline.txt")
     args = ap.parse_args(argv)
 
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
         return 0
+    if args.oracle_configs:
+        return time_oracle_configs()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
                                    "(every (sequence, head) pair is independent; see the sharding design notes)"}))
@@ -528,12 +622,21 @@ def main(argv=None) -> int:
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()  # barrier: one rank
+    clk0 = hstu.clock_sample(64, dev, stream)
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(ev[s])
+    clk1 = hstu.clock_sample(64, dev, stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    clock = clock_summary(clk0.cpu().numpy(), clk1.cpu().numpy())
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s; shader clock {clock['shader_mhz']} MHz "
+          f"(per XCD {clock['per_xcd_mhz']}, counter spread {clock['counter_spread_cycles']} cycles, "
+          f"region {clock['region_us_by_realtime']} us by the real-time counter)", file=sys.stderr, flush=True)
+    if args.clock_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.clock_out)), exist_ok=True)
+        with open(args.clock_out, "w") as f:
+            json.dump(clock, f)
 
     per_kernel_ms = {}
     for i, name in enumerate(kernels):
@@ -594,7 +697,10 @@ def main(argv=None) -> int:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_max_pairs)
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
-                        "gcn_arch": getattr(props, "gcnArchName", "")}
+                        "gcn_arch": getattr(props, "gcnArchName", ""), "shader_clock": clock,
+                        "peak_basis": "2500 TFLOP/s = 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU (published); "
+                                      "at the measured clock the same CUs peak at "
+                                      f"{256 * 4096 * (clock['shader_mhz'] or 0) / 1e6:.0f} TFLOP/s"}
     print(json.dumps(result))
     return 0
 

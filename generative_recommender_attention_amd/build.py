@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "libhstu")
 LIB_PATH = os.path.join(PKG, "libhstu.so")
 
-SOURCES = ["hstu_api.cpp", "hstu_fwd.hip", "hstu_bwd.hip", "lmsd.hip"]
+SOURCES = ["hstu_api.cpp", "hstu_fwd.hip", "hstu_bwd.hip", "lmsd.hip", "clock.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are kept out of the device code.

@@ -128,7 +128,6 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
     p.alpha = a->alpha;
     p.exp_c = -a->alpha * 1.4426950408889634f;
     p.out_scale = ls >= 1 ? a->alpha / (float)ls : 0.0f;
-    p.pre_scale = p.exp_c != 0.0f ? p.out_scale / p.exp_c : 0.0f;
     if (mask_kind(*a) == hstu::MaskKind::Window) {
         // an unbounded side, or one reaching past every sequence, becomes max_seqlen_k:
         // no row index or key index differs from another by more than that
@@ -487,10 +486,15 @@ hstu_status_t hstu_lmsd_bwd_workspace_size(const hstu_lmsd_args_t* a, size_t* by
     return ok();
 }
 
-hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const void* x, const void* u,
-                            const void* weight, const void* bias, const float* mean, const float* rstd, void* dx,
-                            void* du, void* dweight, void* dbias, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The LMSD backward on the caller's column-partial buffer `workspace`.
+hstu_status_t run_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const void* x, const void* u,
+                           const void* weight, const void* bias, const float* mean, const float* rstd, void* dx,
+                           void* du, void* dweight, void* dbias, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, const char* what) {
     hstu::LmsdParams p;
     hstu_status_t st = lmsd_common(a, p);
     if (st != HSTU_OK) return st;
@@ -527,8 +531,26 @@ hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const voi
     p.work = static_cast<float*>(workspace);
     p.part_stride = (int64_t)a->d * (a->compute_dweight ? 2 : 1);
     // no rows: only the column-sum kernel runs, over zero partials, and writes zeros
-    return launched(hstu::launch_lmsd_bwd(p, a->n == 0 ? 0 : hstu::lmsd_bwd_parts(a->n, a->d), stream),
-                    "hstu_lmsd_bwd");
+    return launched(hstu::launch_lmsd_bwd(p, a->n == 0 ? 0 : hstu::lmsd_bwd_parts(a->n, a->d), stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const void* x, const void* u,
+                            const void* weight, const void* bias, const float* mean, const float* rstd, void* dx,
+                            void* du, void* dweight, void* dbias, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    return run_lmsd_bwd(a, dy, x, u, weight, bias, mean, rstd, dx, du, dweight, dbias, workspace, workspace_bytes,
+                        stream, "hstu_lmsd_bwd");
+}
+
+hstu_status_t hstu_clock_sample(uint64_t* samples, int32_t count, hipStream_t stream) {
+    if (count < 1 || count > 65536) return fail(HSTU_ERR_INVALID_ARGUMENT, "count %d is not in [1, 65536]", count);
+    if (samples == nullptr || reinterpret_cast<uintptr_t>(samples) % 8 != 0)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "samples is null or not 8-byte aligned");
+    return launched(hstu::launch_clock_sample(samples, count, stream), "hstu_clock_sample");
 }
 
 const char* hstu_last_error(void) { return g_last_error.c_str(); }

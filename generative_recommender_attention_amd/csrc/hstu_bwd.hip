@@ -11,10 +11,9 @@
 //     dQ_i = alpha sum_j M_ij dA_ij SiLU'(s_ij) / L_scale k_j
 //     dK_j = alpha sum_i M_ij dA_ij SiLU'(s_ij) / L_scale q_i
 // SiLU'(s) = sig(s) (1 + s (1 - sig(s))).  As in the forward, the score MFMAs
-// run on Q (dq kernel) or K (dk/dv kernel) pre-multiplied by c = -alpha log2 e,
-// so they produce y = c x (x = q_i.k_j): sig(s) = 1 / (1 + 2^y) and
-// s = alpha x = -y / log2 e; alpha / L_scale (and 1/c for dV) is applied at the
-// final store.
+// run on the exact bf16 q and k, so they produce x = q_i.k_j to fp32 rounding,
+// and alpha is applied in fp32: sig(s) = 1 / (1 + 2^(c x)) with c = -alpha log2 e;
+// alpha / L_scale is applied at the final stores of dQ, dK and dV.
 //
 // dq kernel: query-major, one workgroup per (128-row block, sequence, head), the
 // same tile walk and mask handling as the forward, two workgroups per CU (so the
@@ -24,7 +23,7 @@
 // operand: K read transposed).
 //
 // dk/dv kernel: key-major, one 8-wave workgroup per (128-key block, sequence,
-// head).  The block's K (times c) and V rows sit in LDS for the whole walk;
+// head).  The block's K and V rows sit in LDS for the whole walk;
 // waves w and w + 4 own the same 32 keys and take the first and second 32 rows
 // of every query tile, so each wave holds only its dK^T and dV^T accumulators
 // and two waves fit per SIMD; their partial sums are added through LDS at the
@@ -71,14 +70,10 @@ constexpr int BN = kTileRows;    // dq kernel: keys per tile
 constexpr int BNK = kBwdBlockN;  // dk/dv kernel: keys per workgroup (32 per wave pair)
 constexpr int BMQ = kTileRows;   // dk/dv kernel: query rows per tile
 
-constexpr float kNegLn2 = -0.69314718055994531f;  // s = y * kNegLn2 for y = c x
-
-// sig(s) from a pre-scaled score y.
-__device__ __forceinline__ float sig_pre(float y) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y)); }
-// SiLU'(s) = sig (1 + s (1 - sig)) from a = y sig: with s = y (-ln 2),
-// SiLU'(s) = sig + s sig (1 - sig) = sig + (-ln 2)(a - a sig), two fused multiply-adds.
-__device__ __forceinline__ float dsilu_from(float a, float sig) {
-    return __builtin_fmaf(kNegLn2, __builtin_fmaf(-a, sig, a), sig);
+// SiLU'(s) = sig (1 + s (1 - sig)) at s = alpha x, from a = x sig: s sig = alpha a,
+// so SiLU'(s) = sig + alpha (a - a sig), two fused multiply-adds.
+__device__ __forceinline__ float dsilu_from(float a, float sig, float alpha) {
+    return __builtin_fmaf(alpha, __builtin_fmaf(-a, sig, a), sig);
 }
 
 constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
@@ -95,12 +90,12 @@ enum DqMask : int { kNoMask = 0, kInterval = 1, kBand = 2, kBits = 3 };
 // as MT says.
 template <int MT>
 __device__ __forceinline__ void dq_ds_op(const f32x16& sacc, const f32x16& dacc, int key0, int lo, int span, int wlo,
-                                         int wlim, int g, uint4& d0, uint4& d1) {
+                                         int wlim, int g, float c, float alpha, uint4& d0, uint4& d1) {
     float dv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float sg = sig_pre(sacc[r]);
-        dv[r] = dacc[r] * dsilu_from(sacc[r] * sg, sg);
+        const float sg = sig_x(sacc[r], c);
+        dv[r] = dacc[r] * dsilu_from(sacc[r] * sg, sg, alpha);
     }
     if constexpr (MT == kBits) {
         if (span) {
@@ -130,7 +125,8 @@ template <int D, int MT>
 __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&qf)[D / 16],
                                            const uint4 (&dof)[D / 16], f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
                                            const uint32_t (&koff)[D / 16], const uint2 (&toff)[(D < 32 ? 32 : D) / 32],
-                                           int n0, int lo, int span, int wlo, int wlim, int lo1, int g) {
+                                           int n0, int lo, int span, int wlo, int wlim, int lo1, int g, float c,
+                                           float alpha) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // S and dA products: block kb, step kk, operand (K, V)
@@ -165,7 +161,7 @@ __device__ __forceinline__ void dq_tile(uint32_t kt, uint32_t vt, const uint4 (&
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         uint4 d0, d1;
-        dq_ds_op<MT>(sa[kb], da[kb], n0 + 32 * kb, kb ? lo1 : lo, span, wlo, wlim, g, d0, d1);
+        dq_ds_op<MT>(sa[kb], da[kb], n0 + 32 * kb, kb ? lo1 : lo, span, wlo, wlim, g, c, alpha, d0, d1);
 #pragma unroll
         for (int j = 0; j < 2 * NDB; ++j) {
             const int i = kb * 2 * NDB + j;
@@ -260,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
         const uint16_t* dsrc = p.dout.base + (int64_t)(sb.q0 + r) * p.dout.tok + (int64_t)h * p.dout.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            qf[kk] = scale_bf16x8(ld_global16(qsrc + 16 * kk), p.exp_c);  // fold c into Q
+            qf[kk] = ld_global16(qsrc + 16 * kk);
             dof[kk] = ld_global16(dsrc + 16 * kk);
         }
     }
@@ -315,14 +311,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
                     const uint64_t sh = bits >> (4 * g);
                     if (seen != 0)
                         dq_tile<D, kBits>(kc, vc, qf, dof, acc, koff, toff, n0, (int)(uint32_t)sh, cut, 0, 0,
-                                          (int)(uint32_t)(sh >> 32), g);
+                                          (int)(uint32_t)(sh >> 32), g, p.exp_c, p.alpha);
                 }
             } else {
                 // waves that see no key of the tile skip it
                 const bool run = WINDOW ? n0 + BN > any_lo && n0 < any_hi : !(CAUSAL && n0 > row0 + 31);
                 if (wave_live && run)
                     dq_tile<D, WINDOW ? kBand : kInterval>(kc, vc, qf, dof, acc, koff, toff, n0, lo, span, wlo, wlim,
-                                                           lo, g);
+                                                           lo, g, p.exp_c, p.alpha);
             }
             wait_global_loads();
             __syncthreads();
@@ -378,7 +374,7 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
                                             uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
                                             const uint2 (&toff)[(D < 32 ? 32 : D) / 32], int row0, int lo, int hi,
-                                            int g, uint32_t mw, const DsOut& ds) {
+                                            int g, uint32_t mw, const DsOut& ds, float c, float alpha) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // reads for S and dA: step kk, (Q, K, dO, V)
@@ -411,9 +407,9 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     float av[16], dv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float y = sa[r], sg = sig_pre(y);
-        av[r] = y * sg;
-        dv[r] = da[r] * dsilu_from(av[r], sg);
+        const float x = sa[r], sg = sig_x(x, c);
+        av[r] = x * sg;
+        dv[r] = da[r] * dsilu_from(av[r], sg, alpha);
     }
     if constexpr (MT == kBits) {
         if (mask) {
@@ -515,14 +511,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         ds_base = p.ds + ((int64_t)h * p.ds_nb + slot) * p.ds_kg * kDsBlockElems + l32 * kDsRowElems + 8 * g;
     }
 
-    // the block's K (times c) and V rows into LDS; rows past the sequence repeat its last row
+    // the block's K and V rows into LDS; rows past the sequence repeat its last row
     for (int u = tid; u < BNK * 16; u += 512) {
         const int r = u >> 4, c = u & 15;
         if (c < D / 8) {
             const int64_t row = sb.k0 + min(n0 + r, sb.lk - 1);
             const uint4 kv = ld_global16(p.k.base + row * p.k.tok + (int64_t)h * p.k.head + 8 * c);
             const uint4 vv = ld_global16(p.v.base + row * p.v.tok + (int64_t)h * p.v.head + 8 * c);
-            ds_write16(lds0 + KB + tile_byte(r, c), scale_bf16x8(kv, p.exp_c));
+            ds_write16(lds0 + KB + tile_byte(r, c), kv);
             ds_write16(lds0 + VB + tile_byte(r, c), vv);
         }
     }
@@ -660,7 +656,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     if (seen != 0)
                         dkdv_block<D, kBits>(cut != 0 || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
                                              roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g),
-                                             DsOut{nullptr, false, false, false});
+                                             DsOut{nullptr, false, false, false}, p.exp_c, p.alpha);
                 }
             } else {
                 // waves whose keys no row of the block sees, or that lie past the sequence, skip it
@@ -676,7 +672,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     }
                     // rows outside those that see every key of the wave, or past the sequence, need the mask
                     dkdv_block<D, kInterval>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
-                                             roff, toff, row0, lo, hi, g, 0, ds);
+                                             roff, toff, row0, lo, hi, g, 0, ds, p.exp_c, p.alpha);
                 }
             }
             wait_global_loads();
@@ -716,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     if (my_key < sb.lk) {
         uint16_t* dk = p.dk.base + (int64_t)(sb.k0 + my_key) * p.dk.tok + (int64_t)h * p.dk.head;
         uint16_t* dv = p.dv.base + (int64_t)(sb.k0 + my_key) * p.dv.tok + (int64_t)h * p.dv.head;
-        const float sc = p.out_scale, scv = p.pre_scale;
+        const float sc = p.out_scale, scv = p.out_scale;
 #pragma unroll
         for (int db = 0; db < DM / 32; ++db) {
 #pragma unroll

@@ -74,18 +74,6 @@ __device__ __forceinline__ uint4 pack_operand(const float* x) {
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
 }
 
-// Eight bf16 values times an fp32 factor, rounded back to bf16 (nearest-even).
-__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float c) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
-        o[i] = pack_bf16x2(lo * c, hi * c);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
@@ -417,11 +405,14 @@ __device__ __forceinline__ SeqBounds seq_bounds(const int32_t* cu_q, const int32
     return s;
 }
 
-// y / (1 + 2^y): SiLU(s) / alpha times c for a score pre-multiplied by
-// c = -alpha log2(e), i.e. y = c x, s = alpha x (x = q.k).
-__device__ __forceinline__ float silu_pre(float y) {
-    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+// sig(alpha x) for a raw score x = q.k (the fp32 MFMA sum of exact bf16
+// products): 1 / (1 + 2^(c x)) with c = -alpha log2(e), the scale applied in fp32.
+// 2^(c x) overflowing to +inf for large negative alpha x gives exactly 0.
+__device__ __forceinline__ float sig_x(float x, float c) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(c * x));
 }
+// SiLU(alpha x) / alpha = x sig(alpha x); the factor alpha goes into the store.
+__device__ __forceinline__ float silu_x(float x, float c) { return x * sig_x(x, c); }
 
 // Marks a branch body the optimizer must not speculate: the mask selects sit
 // behind a uniform branch so that interior tiles skip them, and an if-converted

@@ -29,9 +29,10 @@
 // loads of the next tile are issued before the current one is computed and
 // waited for (vmcnt) before the one barrier per step.  Per tile a wave runs, for
 // each 32-key half,
-//   S^T (32 x 32)  = K_half (cQ)^T   on MFMA: A = K rows from LDS, B = Q from
-//                    registers, Q pre-scaled by c = -alpha log2 e
-//   P^T            = bf16(y / (1 + 2^y)), masked on edge tiles only
+//   X^T (32 x 32)  = K_half Q^T      on MFMA: A = K rows from LDS, B = Q from
+//                    registers (both exact bf16, so X = Q K^T is the fp32 sum)
+//   P^T            = bf16(x / (1 + 2^(c x))), c = -alpha log2 e applied in fp32,
+//                    masked on edge tiles only
 //   O^T (D x 32)  += V_half^T P^T    on MFMA: A = V read transposed from LDS
 // with the scores of one half turned into P^T while the next half's products
 // run, and the epilogue writing O = (alpha / L_scale) O^T^T in bf16.
@@ -53,15 +54,16 @@ constexpr uint32_t kTileBytes = 2 * kTileElems;  // 16 KB per staged 64-row tile
 enum TileMask : int { kNoMask = 0, kInterval = 1, kBits = 2 };
 
 // bf16 P^T operand from accumulator registers r0..r0+7 of a 32-key block whose
-// first key is key0.  The scores arrive as y = c x with c = -alpha log2(e)
-// folded into Q (x = q.k), so y sig(alpha x) = y / (1 + 2^y) costs one exp, one
-// add, one rcp and one multiply; the factor 1/c is folded into the output
-// scale.  kInterval: (a, b) = (lo, span); kBits: a = the block's bit word, b the flag.
+// first key is key0.  The registers hold raw scores x = q.k; SiLU(alpha x) /
+// alpha = x / (1 + 2^(c x)), c = -alpha log2(e), costs two multiplies, one exp,
+// one add and one rcp; the factor alpha goes into the output scale.  Scaling the
+// scores in fp32 (rather than a bf16 operand by c) keeps them exact to fp32
+// rounding.  kInterval: (a, b) = (lo, span); kBits: a = the block's bit word, b the flag.
 template <int MT>
-__device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int a, int b, int g) {
+__device__ __forceinline__ uint4 silu_operand(const f32x16& s, int r0, int key0, int a, int b, int g, float c) {
     float pv[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pv[r] = silu_pre(s[r0 + r]);
+    for (int r = 0; r < 8; ++r) pv[r] = silu_x(s[r0 + r], c);
     if constexpr (MT == kInterval) {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
@@ -87,7 +89,7 @@ template <int D, int MT, uint32_t kt, uint32_t vt>
 __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
                                          f32x16 (&oacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&koff)[D / 16],
                                          const uint2 (&voff)[(D < 32 ? 32 : D) / 32], int n0, int a0, int b0,
-                                         int a1, int b1, int g) {
+                                         int a1, int b1, int g, float c) {
     constexpr int NDB = (D < 32 ? 32 : D) / 32;  // 32-column blocks of O^T
     constexpr int NS = D / 16;                   // contraction steps per S^T block
     constexpr int NK = 2 * NS;                   // K reads: block-major, step-minor
@@ -111,15 +113,15 @@ __device__ __forceinline__ void fwd_tile(const uint4 (&qf)[D / 16],
         else s1 = mfma32x32x16(rd[j], qf[j - NS], s1);
         read(j + PF);
     }
-    const uint4 p0 = silu_operand<MT>(s0, 0, n0, a0, b0, g);
-    const uint4 p1 = silu_operand<MT>(s0, 8, n0, a0, b0, g);
+    const uint4 p0 = silu_operand<MT>(s0, 0, n0, a0, b0, g, c);
+    const uint4 p1 = silu_operand<MT>(s0, 8, n0, a0, b0, g, c);
 #pragma unroll
     for (int i = 0; i < 2 * NDB; ++i) {
         oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < NDB ? p0 : p1, oacc[i % NDB]);
         read(NK + i + PF);
     }
-    const uint4 p2 = silu_operand<MT>(s1, 0, n0 + 32, a1, b1, g);
-    const uint4 p3 = silu_operand<MT>(s1, 8, n0 + 32, a1, b1, g);
+    const uint4 p2 = silu_operand<MT>(s1, 0, n0 + 32, a1, b1, g, c);
+    const uint4 p3 = silu_operand<MT>(s1, 8, n0 + 32, a1, b1, g, c);
 #pragma unroll
     for (int i = 2 * NDB; i < NV; ++i) {
         oacc[i % NDB] = mfma32x32x16(rd[NK + i], i < 3 * NDB ? p2 : p3, oacc[i % NDB]);
@@ -143,6 +145,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+    const float c = p.exp_c;
 
     // workgroup -> (live row block, head), head fastest; surplus workgroups exit
     const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.heads));
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
         const int r = min(my_row, sb.lq - 1);
         const uint16_t* src = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = scale_bf16x8(ld_global16(src + 16 * kk), p.exp_c);
+        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = ld_global16(src + 16 * kk);
     }
     uint32_t koff[KSTEPS];
 #pragma unroll
@@ -264,9 +267,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
             if constexpr (WINDOW) {
                 if (wave_live && n0 + BN > any_lo && n0 < any_hi) {
                     if (n0 >= full_lo && n0 + BN <= full_hi)
-                        fwd_tile<D, kNoMask, cur, cur>(qf, oacc, koff, voff, n0, 0, 0, 0, 0, g);
+                        fwd_tile<D, kNoMask, cur, cur>(qf, oacc, koff, voff, n0, 0, 0, 0, 0, g, c);
                     else
-                        fwd_tile<D, kInterval, cur, cur>(qf, oacc, koff, voff, n0, lo, span, lo, span, g);
+                        fwd_tile<D, kInterval, cur, cur>(qf, oacc, koff, voff, n0, lo, span, lo, span, g, c);
                 }
             } else if constexpr (FUNC) {
                 // this lane's visible keys of the tile; the live rows of the wave decide
@@ -280,14 +283,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
                     if (seen != 0) {
                         const uint64_t sh = bits >> (4 * g);
                         fwd_tile<D, kBits, cur, cur>(qf, oacc, koff, voff, n0, (int)(uint32_t)sh, cut,
-                                                     (int)(uint32_t)(sh >> 32), cut, g);
+                                                     (int)(uint32_t)(sh >> 32), cut, g, c);
                     }
                 }
             } else {
                 // waves whose rows all precede the tile's first key, or lie past the sequence, skip it
                 if (wave_live && !(CAUSAL && n0 > row0 + 31))
                     fwd_tile<D, decltype(masked)::value ? kInterval : kNoMask, cur, cur>(qf, oacc, koff, voff, n0, lo,
-                                                                                         span, lo, span, g);
+                                                                                         span, lo, span, g, c);
             }
             wait_global_loads();
             __syncthreads();
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
 
     if (my_row >= sb.lq) return;
     uint16_t* dst = p.o.base + (int64_t)(sb.q0 + my_row) * p.o.tok + (int64_t)h * p.o.head;
-    const float sc = p.pre_scale;
+    const float sc = p.out_scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll

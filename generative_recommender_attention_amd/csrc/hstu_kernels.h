@@ -30,9 +30,8 @@ struct AttnParams {
                            // kernels) or ceil(max_seqlen_q / 64) (dk/dv), at least 1
     float alpha;           // score scale
     float exp_c;           // -alpha * log2(e), for sig(alpha x) = 1 / (1 + 2^(x exp_c))
-    float out_scale;       // alpha / L_scale: the epilogue factor of dQ and dK
-    float pre_scale;       // alpha / (L_scale c): the factor of O and dV, whose sums run over
-                           // scores pre-multiplied by c = exp_c (0 when alpha = 0)
+    float out_scale;       // alpha / L_scale: the epilogue factor of O, dQ, dK and dV, whose sums
+                           // run over raw scores x = q.k (alpha is applied to them in fp32)
     int32_t win_left;      // MaskKind::Window: 0 <= left, right <= max_seqlen_k <= 2^29
     int32_t win_right;
     const int32_t* func;   // MaskKind::Func: endpoints, device, func_n rows of func_ld >= T_q
@@ -79,5 +78,7 @@ hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipSt
 hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 // dQ from the dS the dk/dv kernel stored (p.ds); mask None, Causal or Window.
 hipError_t launch_bwd_dq_ds(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
+// `count` one-wave workgroups, each writing {realtime, shader cycles, XCC id, HW_ID}.
+hipError_t launch_clock_sample(uint64_t* out, int count, hipStream_t stream);
 
 }  // namespace hstu

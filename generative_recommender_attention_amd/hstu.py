@@ -49,6 +49,7 @@ __all__ = [
     "lmsd_fwd",
     "lmsd_bwd",
     "lmsd_bwd_workspace_size",
+    "clock_sample",
 ]
 
 HSTU_OK = 0
@@ -169,6 +170,8 @@ def library() -> ctypes.CDLL:
             lib.hstu_lmsd_bwd_workspace_size.argtypes = [largp, ctypes.POINTER(ctypes.c_size_t)]
             lib.hstu_lmsd_bwd.restype = ctypes.c_int
             lib.hstu_lmsd_bwd.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            lib.hstu_clock_sample.restype = ctypes.c_int
+            lib.hstu_clock_sample.argtypes = [vp, ctypes.c_int32, vp]
             lib.hstu_last_error.restype = ctypes.c_char_p
             lib.hstu_last_error.argtypes = []
             lib.hstu_status_string.restype = ctypes.c_char_p
@@ -218,10 +221,22 @@ def _cu(name: str, t: torch.Tensor, device: torch.device) -> int:
     return t.data_ptr()
 
 
-def _stream(stream, device) -> int:
+def _launch_stream(stream, device):
+    """The stream the kernels go to, as a torch stream: the current one when none is
+    given; a raw ``hipStream_t`` handle is wrapped.  Every tensor a function
+    allocates (outputs, workspaces) is allocated while this stream is current, so
+    the caching allocator hands a block freed at return to later work on the same
+    stream only, which the stream orders after the kernels that used it."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.ExternalStream(handle, device=device)
+
+
+def _stream(s) -> int:
+    return int(s.cuda_stream)
 
 
 def _args(q, k, cu_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size,
@@ -280,13 +295,15 @@ def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              window_size: Optional[Tuple[int, int]] = None, func: Optional[torch.Tensor] = None) -> torch.Tensor:
     """O = HSTU(q, k, v) on packed (T, H, D) bf16 tensors; returns ``out``."""
     H, D, pq, pk = _inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
-    if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    _thd("out", out, int(q.shape[0]), H, D)
-    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
-    a.q, a.k, a.v, a.o = _stride(q), _stride(k), _stride(v), _stride(out)
-    _check(library().hstu_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(), pq, pk,
-                              out.data_ptr(), _stream(stream, q.device)))
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        _thd("out", out, int(q.shape[0]), H, D)
+        a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
+        a.q, a.k, a.v, a.o = _stride(q), _stride(k), _stride(v), _stride(out)
+        _check(library().hstu_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(), pq, pk,
+                                  out.data_ptr(), _stream(s)))
     return out
 
 
@@ -316,23 +333,25 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     scores and no workspace is used."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    _thd("dq", dq, int(q.shape[0]), H, D)
-    _thd("dk", dk, int(k.shape[0]), H, D)
-    _thd("dv", dv, int(k.shape[0]), H, D)
-    a.dq, a.dk, a.dv = _stride(dq), _stride(dk), _stride(dv)
-    need = ctypes.c_size_t(0)
-    _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
-    if not store_ds or need.value == 0:
-        workspace = None
-    elif workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_bytes = _workspace(workspace)
-    _check(library().hstu_bwd(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
-                              _stream(stream, q.device)))
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):  # a workspace allocated here is freed on s, after the kernels
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+        _thd("dq", dq, int(q.shape[0]), H, D)
+        _thd("dk", dk, int(k.shape[0]), H, D)
+        _thd("dv", dv, int(k.shape[0]), H, D)
+        a.dq, a.dk, a.dv = _stride(dq), _stride(dk), _stride(dv)
+        need = ctypes.c_size_t(0)
+        _check(library().hstu_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        if not store_ds or need.value == 0:
+            workspace = None
+        elif workspace is None:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _workspace(workspace)
+        _check(library().hstu_bwd(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
+                                  _stream(s)))
     return dq, dk, dv
 
 
@@ -360,11 +379,13 @@ def hstu_bwd_dq(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seq
     """dq only (the query-major backward kernel)."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    _thd("dq", dq, int(q.shape[0]), H, D)
-    a.dq = _stride(dq)
-    _check(library().hstu_bwd_dq(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                 v.data_ptr(), pq, pk, dq.data_ptr(), _stream(stream, q.device)))
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+        _thd("dq", dq, int(q.shape[0]), H, D)
+        a.dq = _stride(dq)
+        _check(library().hstu_bwd_dq(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), pq, pk, dq.data_ptr(), _stream(s)))
     return dq
 
 
@@ -374,14 +395,15 @@ def hstu_bwd_dkdv(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
     """(dk, dv) only (the key-major backward kernel)."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    _thd("dk", dk, int(k.shape[0]), H, D)
-    _thd("dv", dv, int(k.shape[0]), H, D)
-    a.dk, a.dv = _stride(dk), _stride(dv)
-    _check(library().hstu_bwd_dkdv(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                   v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(),
-                                   _stream(stream, q.device)))
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+        _thd("dk", dk, int(k.shape[0]), H, D)
+        _thd("dv", dv, int(k.shape[0]), H, D)
+        a.dk, a.dv = _stride(dk), _stride(dv)
+        _check(library().hstu_bwd_dkdv(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(), _stream(s)))
     return dk, dv
 
 
@@ -432,15 +454,17 @@ def lmsd_fwd(x: torch.Tensor, u: torch.Tensor, weight: torch.Tensor, bias: torch
     _vec("weight", weight, d)
     _vec("bias", bias, d)
     segs = 1 + a.concat_u + a.concat_x
-    y = torch.empty((n, segs * d), dtype=torch.bfloat16, device=x.device) if y is None else y
-    if y.shape != (n, segs * d) or y.dtype != torch.bfloat16 or not y.is_contiguous():
-        raise ValueError(f"y must be a contiguous ({n}, {segs * d}) bfloat16 tensor")
-    mean = torch.empty(n, dtype=torch.float32, device=x.device) if mean is None else mean
-    rstd = torch.empty(n, dtype=torch.float32, device=x.device) if rstd is None else rstd
-    _vec("mean", mean, n, torch.float32)
-    _vec("rstd", rstd, n, torch.float32)
-    _check(library().hstu_lmsd_fwd(ctypes.byref(a), x.data_ptr(), u.data_ptr(), weight.data_ptr(), bias.data_ptr(),
-                                   y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), _stream(stream, x.device)))
+    s = _launch_stream(stream, x.device)
+    with torch.cuda.stream(s):
+        y = torch.empty((n, segs * d), dtype=torch.bfloat16, device=x.device) if y is None else y
+        if y.shape != (n, segs * d) or y.dtype != torch.bfloat16 or not y.is_contiguous():
+            raise ValueError(f"y must be a contiguous ({n}, {segs * d}) bfloat16 tensor")
+        mean = torch.empty(n, dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty(n, dtype=torch.float32, device=x.device) if rstd is None else rstd
+        _vec("mean", mean, n, torch.float32)
+        _vec("rstd", rstd, n, torch.float32)
+        _check(library().hstu_lmsd_fwd(ctypes.byref(a), x.data_ptr(), u.data_ptr(), weight.data_ptr(),
+                                       bias.data_ptr(), y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), _stream(s)))
     return y, mean, rstd
 
 
@@ -466,27 +490,29 @@ def lmsd_bwd(dy: torch.Tensor, x: torch.Tensor, u: torch.Tensor, weight: torch.T
     _vec("bias", bias, d)
     _vec("mean", mean, n, torch.float32)
     _vec("rstd", rstd, n, torch.float32)
-    dx = torch.empty((n, d), dtype=torch.bfloat16, device=x.device) if dx is None else dx
-    du = torch.empty((n, d), dtype=torch.bfloat16, device=x.device) if du is None else du
-    a.dx_stride = _rowmat("dx", dx, n, d)
-    a.du_stride = _rowmat("du", du, n, d)
-    dbias = torch.empty(d, dtype=torch.bfloat16, device=x.device) if dbias is None else dbias
-    _vec("dbias", dbias, d)
-    if compute_dweight:
-        dweight = torch.empty(d, dtype=torch.bfloat16, device=x.device) if dweight is None else dweight
-        _vec("dweight", dweight, d)
-    else:
-        dweight = None
-    need = ctypes.c_size_t(0)
-    _check(library().hstu_lmsd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
-    if workspace is None and need.value > 0:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=x.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(library().hstu_lmsd_bwd(ctypes.byref(a), dy.data_ptr(), x.data_ptr(), u.data_ptr(), weight.data_ptr(),
-                                   bias.data_ptr(), mean.data_ptr(), rstd.data_ptr(), dx.data_ptr(), du.data_ptr(),
-                                   dweight.data_ptr() if dweight is not None else None, dbias.data_ptr(), ws_ptr,
-                                   ws_bytes, _stream(stream, x.device)))
+    s = _launch_stream(stream, x.device)
+    with torch.cuda.stream(s):  # a workspace allocated here is freed on s, after the kernels
+        dx = torch.empty((n, d), dtype=torch.bfloat16, device=x.device) if dx is None else dx
+        du = torch.empty((n, d), dtype=torch.bfloat16, device=x.device) if du is None else du
+        a.dx_stride = _rowmat("dx", dx, n, d)
+        a.du_stride = _rowmat("du", du, n, d)
+        dbias = torch.empty(d, dtype=torch.bfloat16, device=x.device) if dbias is None else dbias
+        _vec("dbias", dbias, d)
+        if compute_dweight:
+            dweight = torch.empty(d, dtype=torch.bfloat16, device=x.device) if dweight is None else dweight
+            _vec("dweight", dweight, d)
+        else:
+            dweight = None
+        need = ctypes.c_size_t(0)
+        _check(library().hstu_lmsd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        if workspace is None and need.value > 0:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=x.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(library().hstu_lmsd_bwd(ctypes.byref(a), dy.data_ptr(), x.data_ptr(), u.data_ptr(),
+                                       weight.data_ptr(), bias.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+                                       dx.data_ptr(), du.data_ptr(), dweight.data_ptr() if dweight is not None else None,
+                                       dbias.data_ptr(), ws_ptr, ws_bytes, _stream(s)))
     return dx, du, dweight, dbias
 
 
@@ -497,15 +523,17 @@ def hstu_bwd_dkdv_ds(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
     ``hstu_bwd_dq_ds``; no mask, the causal mask or a window."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    _thd("dk", dk, int(k.shape[0]), H, D)
-    _thd("dv", dv, int(k.shape[0]), H, D)
-    a.dk, a.dv = _stride(dk), _stride(dv)
-    ws_ptr, ws_bytes = _workspace(ds)
-    _check(library().hstu_bwd_dkdv_ds(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                      v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
-                                      _stream(stream, q.device)))
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+        _thd("dk", dk, int(k.shape[0]), H, D)
+        _thd("dv", dv, int(k.shape[0]), H, D)
+        a.dk, a.dv = _stride(dk), _stride(dv)
+        ws_ptr, ws_bytes = _workspace(ds)
+        _check(library().hstu_bwd_dkdv_ds(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                          v.data_ptr(), pq, pk, dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
+                                          _stream(s)))
     return dk, dv
 
 
@@ -516,10 +544,27 @@ def hstu_bwd_dq_ds(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
     H, D, pq, pk = _inputs(q, k, k, cu_seqlens_q, cu_seqlens_k)
     a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, None)
     a.q, a.k = _stride(q), _stride(k)
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    _thd("dq", dq, int(q.shape[0]), H, D)
-    a.dq = _stride(dq)
-    ws_ptr, ws_bytes = _workspace(ds)
-    _check(library().hstu_bwd_dq_ds(ctypes.byref(a), k.data_ptr(), pq, pk, ws_ptr, ws_bytes, dq.data_ptr(),
-                                    _stream(stream, q.device)))
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+        _thd("dq", dq, int(q.shape[0]), H, D)
+        a.dq = _stride(dq)
+        ws_ptr, ws_bytes = _workspace(ds)
+        _check(library().hstu_bwd_dq_ds(ctypes.byref(a), k.data_ptr(), pq, pk, ws_ptr, ws_bytes, dq.data_ptr(),
+                                        _stream(s)))
     return dq
+
+
+# ---------------------------------------------------------------------------
+# Measurement helper: shader-clock samples (not part of the method)
+# ---------------------------------------------------------------------------
+def clock_sample(count: int = 64, device=None, stream=None) -> torch.Tensor:
+    """Enqueue ``count`` one-wave workgroups that each record (100 MHz real time,
+    shader cycles, XCC id, HW_ID); returns the (count, 4) int64 device tensor they
+    fill (read it after the stream reaches the call)."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    s = _launch_stream(stream, device)
+    with torch.cuda.stream(s):
+        out = torch.empty((int(count), 4), dtype=torch.int64, device=device)
+        _check(library().hstu_clock_sample(out.data_ptr(), int(count), _stream(s)))
+    return out

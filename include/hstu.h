@@ -286,6 +286,17 @@ HSTU_API hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* args, const void* d
                             void* dx, void* du, void* dweight, void* dbias, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* ==========================================================================
+ * Measurement helper (not part of the method): enqueues `count` (1..65536)
+ * one-wave workgroups on `stream`; workgroup i writes four uint64 values to
+ * samples[4 i .. 4 i + 3] (device memory, 8-byte aligned, caller-owned):
+ * the 100 MHz real-time counter, the shader-cycle counter (it advances at the
+ * shader clock of the XCD it runs on), the XCC id and the HW_ID register.
+ * Two such calls around a timed region give each XCD's average shader clock
+ * over it.
+ * ========================================================================== */
+HSTU_API hstu_status_t hstu_clock_sample(uint64_t* samples, int32_t count, hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 HSTU_API const char* hstu_last_error(void);
 

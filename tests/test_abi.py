@@ -34,8 +34,16 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dkdv_ds", "hstu_bwd_dq", "hstu_bwd_dq_ds",
-        "hstu_bwd_workspace_size", "hstu_fwd",
-        "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd", "hstu_status_string"])
+        "hstu_bwd_workspace_size", "hstu_clock_sample", "hstu_fwd",
+        "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd",
+        "hstu_status_string"])
+
+
+def test_clock_sample_rejections(lib):
+    assert lib.hstu_clock_sample(None, 8, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_clock_sample(FAKE + 4, 8, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_clock_sample(FAKE, 0, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_clock_sample(FAKE, 65537, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
 
 
 def test_library_exports_every_declared_symbol(lib):

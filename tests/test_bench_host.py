@@ -59,3 +59,22 @@ def test_source_digest_ignores_comments():
     code = "int f(int x) { // add one\n  return x + 1; /* done */ }\n"
     assert bench._code_only(code) == bench._code_only("int f(int x) {\n return x + 1; }")
     assert bench._code_only(code) != bench._code_only("int f(int x) { return x + 2; }")
+
+
+def test_clock_summary_per_xcd():
+    """Two sample launches 1 ms apart in real time (100 MHz ticks), XCD 0 advancing
+    1.8e6 cycles and XCD 1 2.0e6: 1800 and 2000 MHz, mean 1900."""
+    before, after = [], []
+    for w in range(16):
+        x = w % 2
+        before.append([1000 + w, 5_000_000 * (x + 1) + 7 * w, x, 0])
+        after.append([101_000 + w, 5_000_000 * (x + 1) + 7 * w + (1_800_000 if x == 0 else 2_000_000), x, 0])
+    c = bench.clock_summary(np.array(before), np.array(after))
+    assert c["per_xcd_mhz"] == {"0": 1800.0, "1": 2000.0}
+    assert c["shader_mhz"] == 1900.0
+    assert c["region_us_by_realtime"] == 1000.0
+    assert c["counter_spread_cycles"] == 7 * 14
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

@@ -1,8 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
 
-Small problems are compared element by element in full; the full-size
-workloads on rows the oracle computes one by one (every row of short
-sequences, first/last rows, rows on both sides of tile edges, random rows).
+Every problem is compared element by element on whole tensors, except the
+backward of the long 4 x 8k-15k causal workload, whose oracle would take
+minutes: there the rows compared are sampled (every row of short sequences,
+first/last rows, rows on both sides of tile edges, random rows).
 """
 
 import numpy as np
@@ -69,34 +70,75 @@ def test_uniform_workload_fwd(oracle_lib):
     run_fwd_check(named_workload("uniform_b8_h2_d64_full"))
 
 
-def test_zipf_workload_fwd_sampled(oracle_lib):
-    wl = named_workload("zipf_b32_h4_d128_causal")
-    rel, worst = run_fwd_check(wl, sample_rows(wl.cu_seqlens_q, seed=2), " (sampled rows)")
-    print(f"zipf fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
-
-
-def test_long_workload_fwd_sampled(oracle_lib):
-    wl = named_workload("long_b4_h8_d128_causal")
-    rel, worst = run_fwd_check(wl, sample_rows(wl.cu_seqlens_q, per_seq=24, seed=3), " (sampled rows)")
-    print(f"long fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
-
-
-def test_zipf_workload_fwd_bwd_sampled(oracle_lib):
+def test_zipf_workloads_full(oracle_lib):
+    """The Zipf forward workload and the Zipf forward + backward workload, every row:
+    both draw q, k, v from seed 2 in the same order (the backward one draws dO after
+    them), so one forward comparison covers both; the backward goes through both
+    routes against one oracle evaluation."""
+    fwd_wl = named_workload("zipf_b32_h4_d128_causal")
     wl = named_workload("zipf_b32_h4_d128_causal_fwdbwd")
-    rows = sample_rows(wl.cu_seqlens_q, per_seq=32, seed=4)
-    run_fwd_check(wl, rows, " (sampled rows)")
-    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    for name in ("q", "k", "v", "cu_seqlens_q", "cu_seqlens_k"):
+        assert np.array_equal(getattr(fwd_wl, name), getattr(wl, name)), name
+    rel, worst = run_fwd_check(wl)
+    print(f"zipf fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
+    res = run_bwd_check(wl)
     print("zipf bwd (err/max, worst per-seq):", res)
 
 
+def test_long_workload_fwd_full(oracle_lib):
+    wl = named_workload("long_b4_h8_d128_causal")
+    rel, worst = run_fwd_check(wl)
+    print(f"long fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
+
+
 def test_long_workload_fwd_bwd_sampled(oracle_lib):
-    # the longest walks (up to 256 tiles of 64) through both backward routes, at full size
+    # the longest walks (up to 256 tiles of 64) through both backward routes, at full
+    # size; the oracle's backward over all 43527 rows and 8 heads would take minutes,
+    # so the rows compared are sampled (every tile edge in a stride, first and last
+    # rows, random rows), dK and dV on the same row set
     rng = np.random.default_rng(3)  # the long causal workload's lengths and inputs, plus dO
     lens = rng.integers(8192, 16384, size=4, endpoint=True)
     wl = make_workload("long_b4_h8_d128_causal_fwdbwd", 3, lens, 8, 128, True, 0.5, rng=rng, with_do=True)
-    rows = sample_rows(wl.cu_seqlens_q, per_seq=12, seed=6)
+    rows = sample_rows(wl.cu_seqlens_q, per_seq=48, seed=6)
     res = run_bwd_check(wl, rows, rows, " (sampled rows)")
     print("long bwd (err/max, worst per-seq):", res)
+
+
+# ------------------------------------------------------------------ large scores
+def large_score_workload(tag, seed, D, q_k_scale=1.0, alpha=None):
+    """Scores far outside the N(0, 1) range of the named workloads: q and k scaled by
+    a power of two (exact in bf16) or a large alpha.  With |s| in the hundreds,
+    2^y in the kernels' sigmoid overflows to infinity for large negative s (the
+    reciprocal then gives 0), sig(s) rounds to exactly 0 or 1 on both sides, and
+    SiLU(s) and SiLU'(s) approach their asymptotes s, 0 and 1, 0."""
+    wl = make_workload(f"big{tag}", seed, [300, 129, 64, 17, 1], 2, D, True, 1.0, with_do=True, alpha=alpha)
+    if q_k_scale != 1.0:
+        from generative_recommender_attention_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+        wl.q = f32_to_bf16_bits(bf16_bits_to_f32(wl.q) * np.float32(q_k_scale))
+        wl.k = f32_to_bf16_bits(bf16_bits_to_f32(wl.k) * np.float32(q_k_scale))
+    return wl
+
+
+LARGE_SCORE_CASES = [
+    # (tag, seed, D, q and k scale, alpha, least max|s| the case must reach)
+    ("qk8_d64", 200, 64, 8.0, None, 150.0),      # 2^(c x) overflows to +inf (alpha x < -88.7)
+    ("qk8_d128", 201, 128, 8.0, None, 150.0),
+    ("qk2_d128", 202, 128, 2.0, None, 15.0),     # sig(s) rounds to 1 in fp32 (s > 16.6)
+    ("alpha4_d128", 203, 128, 1.0, 4.0, 100.0),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_SCORE_CASES, ids=[c[0] for c in LARGE_SCORE_CASES])
+def test_large_scores_fwd_bwd(oracle_lib, case):
+    tag, seed, D, scale, alpha, least = case
+    wl = large_score_workload(tag, seed, D, scale, alpha)
+    q, k = oracle.widen(wl.q), oracle.widen(wl.k)
+    smax = float(wl.alpha) * max(float(np.abs(q[:300, h] @ k[:300, h].T).max()) for h in range(wl.num_heads))
+    say(f"large scores {tag}: max |s| over the first sequence {smax:.0f}")
+    assert smax > least  # the case reaches the saturated range it is meant to cover
+    run_fwd_check(wl, tag=f" ({tag})")
+    run_bwd_check(wl, tag=f" ({tag})")
 
 
 # ------------------------------------------------------------ shapes and edges
@@ -179,12 +221,11 @@ def test_window_fwd_bwd(oracle_lib, case):
     run_bwd_check(wl)
 
 
-def test_long_window_workload_sampled(oracle_lib):
+def test_long_window_workload_full(oracle_lib):
     wl = named_workload("long_b4_h8_d128_window1024")
-    rows = sample_rows(wl.cu_seqlens_q, per_seq=24, seed=5)
-    rel, worst = run_fwd_check(wl, rows, " (sampled rows)")
+    rel, worst = run_fwd_check(wl)
     print(f"long window fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
-    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    res = run_bwd_check(wl)
     print("long window bwd (err/max, worst per-seq):", res)
 
 
@@ -241,14 +282,11 @@ def test_func_mask_fwd_bwd(oracle_lib, case):
     run_bwd_check(wl)
 
 
-def test_func_target_workload_sampled(oracle_lib):
+def test_func_target_workload_full(oracle_lib):
     wl = named_workload("zipf_b32_h4_d128_target_fwdbwd")
-    rows = sample_rows(wl.cu_seqlens_q, per_seq=32, seed=6)
-    tail = np.concatenate([np.arange(max(s, e - 40), e) for s, e in zip(wl.cu_seqlens_q[:-1], wl.cu_seqlens_q[1:])])
-    rows = np.union1d(rows, tail)  # the candidate rows of every sequence
-    rel, worst = run_fwd_check(wl, rows, " (sampled rows)")
+    rel, worst = run_fwd_check(wl)
     print(f"target fwd: err/max {rel:.2e}, worst per-sequence {worst:.2e}")
-    res = run_bwd_check(wl, rows, rows, " (sampled rows)")
+    res = run_bwd_check(wl)
     print("target bwd (err/max, worst per-seq):", res)
 
 
@@ -469,6 +507,30 @@ def test_runs_on_caller_stream(oracle_lib):
         o = dw.fwd()
     s.synchronize()
     check_close("O", to_f64(o), oracle.fwd_workload(wl), wl.cu_seqlens_q)
+
+
+def test_bwd_on_side_stream_allocates_there(oracle_lib):
+    """hstu_bwd on a side stream with no workspace given: the binding allocates the dS
+    workspace and the outputs while that stream is current, so a block freed at
+    return is not handed to the current stream's next allocation while the side
+    stream's kernels still use it.  The current stream allocates and NaN-fills
+    blocks of the workspace's size right after the call, without waiting."""
+    wl = make_workload("sidestream", 127, [1500, 900, 64], 4, 128, True, 0.5, with_do=True)
+    dw = DeviceWorkload(wl)
+    kw = dw.kw()
+    need = hstu.hstu_bwd_workspace_size(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, **kw)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("hstu_bwd on a side stream, workspace allocated by the binding")
+    dq, dk, dv = hstu.hstu_bwd(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, stream=s, **kw)
+    junk = [torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    rq, rk, rv = oracle.bwd_workload(wl)
+    check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q)
+    check_close("dK", to_f64(dk), rk, wl.cu_seqlens_k)
+    check_close("dV", to_f64(dv), rv, wl.cu_seqlens_k)
 
 
 def test_unsupported_raise():

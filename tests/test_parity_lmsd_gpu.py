@@ -139,3 +139,30 @@ def test_lmsd_dropout_is_unsupported():
     w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(NotImplementedError):
         hstu.lmsd_fwd(x, x, w, w, dropout_ratio=0.1)
+
+
+def test_lmsd_bwd_on_side_stream_allocates_there(oracle_lib):
+    """lmsd_bwd on a side stream with no workspace given: the binding allocates the
+    column-partial workspace while that stream is current, so the block freed at
+    return is not reused by the current stream's allocations while the side
+    stream's kernels still read it."""
+    wl = make_lmsd_workload("lside", 99, 20000, 512, True, True, True)
+    x, u, w, b, dy = (to_dev(t) for t in (wl.x, wl.u, wl.weight, wl.bias, wl.dy))
+    flags = dict(apply_u_silu=wl.silu_u, concat_u=wl.concat_u, concat_x=wl.concat_x)
+    need = hstu.lmsd_bwd_workspace_size(x, u, eps=wl.eps, **flags)
+    y, mean, rstd = hstu.lmsd_fwd(x, u, w, b, eps=wl.eps, **flags)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("lmsd_bwd on a side stream, workspace allocated by the binding")
+    dx, du, dw, db = hstu.lmsd_bwd(dy, x, u, w, b, mean, rstd, eps=wl.eps, stream=s, **flags)
+    junk = [torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    rm, rr = oracle.lmsd_fwd(wl.x, wl.u, wl.weight, wl.bias, wl.eps, wl.silu_u, wl.concat_u, wl.concat_x)[1:]
+    rdx, rdu, rdw, rdb = oracle.lmsd_bwd(wl.dy, wl.x, wl.u, wl.weight, wl.bias, rm, rr, wl.silu_u, wl.concat_u,
+                                         wl.concat_x)
+    close("dx", to_f64(dx), rdx)
+    close("du", to_f64(du), rdu)
+    close("dweight", to_f64(dw), rdw)
+    close("dbias", to_f64(db), rdb)
