@@ -490,7 +490,8 @@ hstu_status_t hstu_lmsd_bwd_workspace_size(const hstu_lmsd_args_t* a, size_t* by
 
 namespace {
 
-// The LMSD backward on the caller's column-partial buffer `workspace`.
+// The LMSD backward on the column-partial buffer `workspace`, from the caller
+// (hstu_lmsd_bwd) or the library's own scratch (hstu_lmsd_bwd_noalloc).
 hstu_status_t run_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const void* x, const void* u,
                            const void* weight, const void* bias, const float* mean, const float* rstd, void* dx,
                            void* du, void* dweight, void* dbias, void* workspace, size_t workspace_bytes,
@@ -544,6 +545,24 @@ hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* a, const void* dy, const voi
                             hipStream_t stream) {
     return run_lmsd_bwd(a, dy, x, u, weight, bias, mean, rstd, dx, du, dweight, dbias, workspace, workspace_bytes,
                         stream, "hstu_lmsd_bwd");
+}
+
+hstu_status_t hstu_lmsd_bwd_noalloc(const hstu_lmsd_args_t* a, const void* dy, const void* x, const void* u,
+                                    const void* weight, const void* bias, const float* mean, const float* rstd,
+                                    void* dx, void* du, void* dweight, void* dbias, hipStream_t stream) {
+    hstu::LmsdParams p;
+    hstu_status_t st = lmsd_common(a, p);
+    if (st != HSTU_OK) return st;
+    const size_t need = lmsd_workspace(a);
+    if (need > hstu::kLmsdScratchBytes)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "the backward needs %zu bytes of scratch; the library holds %zu", need,
+                    hstu::kLmsdScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = hstu::lmsd_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(HSTU_ERR_DEVICE, "hstu_lmsd_bwd_noalloc: scratch address lookup failed: %s", hipGetErrorString(e));
+    return run_lmsd_bwd(a, dy, x, u, weight, bias, mean, rstd, dx, du, dweight, dbias, scratch,
+                        hstu::kLmsdScratchBytes, stream, "hstu_lmsd_bwd_noalloc");
 }
 
 hstu_status_t hstu_clock_sample(uint64_t* samples, int32_t count, hipStream_t stream) {

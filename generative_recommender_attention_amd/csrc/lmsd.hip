@@ -27,6 +27,8 @@
 // row per workgroup to the caller's workspace; a second kernel adds the G
 // partials column by column, spread over 16 waves per column block, in a fixed
 // order (deterministic).
+#include <mutex>
+
 #include "hstu_device.h"
 #include "lmsd_kernels.h"
 
@@ -294,6 +296,34 @@ hipError_t launch(const LmsdParams& p, bool bwd, int parts, hipStream_t stream) 
 }
 
 }  // namespace
+
+// Scratch for the column partials of hstu_lmsd_bwd_noalloc, for callers that
+// cannot allocate: one array per GPU, held until the process ends and shared by
+// every such call on that GPU.  It needs no clearing: each call's row kernel
+// writes every partial row its column sums read.  Host code must not pass the
+// array's name to a kernel (it is a host-side stand-in, not a device address):
+// lmsd_scratch() returns the device's own address from hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[kLmsdScratchBytes / sizeof(float)];
+
+hipError_t lmsd_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {  // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int lmsd_bwd_parts(int64_t n, int d) {
     const int nvec = d / 8;

@@ -40,6 +40,15 @@ constexpr int kLmsdMaxParts = 1024;
 // Workgroups (= partial rows) the backward launches for n rows of d values.
 int lmsd_bwd_parts(int64_t n, int d);
 
+// Largest d (d < 1024, d % 8 == 0) and the bytes of column partials the backward
+// can need: kLmsdMaxParts rows of [dbias | dweight], 2 d fp32 each (8,323,072 bytes).
+constexpr int kLmsdMaxD = 1016;
+constexpr size_t kLmsdScratchBytes = (size_t)kLmsdMaxParts * 2 * kLmsdMaxD * sizeof(float);
+
+// Device address, on the current device, of the library's own kLmsdScratchBytes of
+// scratch for the backward's column partials (looked up once per device).
+hipError_t lmsd_scratch(void** ptr);
+
 hipError_t launch_lmsd_fwd(const LmsdParams& p, hipStream_t stream);
 hipError_t launch_lmsd_bwd(const LmsdParams& p, int parts, hipStream_t stream);
 

@@ -49,6 +49,7 @@ __all__ = [
     "lmsd_fwd",
     "lmsd_bwd",
     "lmsd_bwd_workspace_size",
+    "lmsd_bwd_noalloc",
     "clock_sample",
 ]
 
@@ -170,6 +171,8 @@ def library() -> ctypes.CDLL:
             lib.hstu_lmsd_bwd_workspace_size.argtypes = [largp, ctypes.POINTER(ctypes.c_size_t)]
             lib.hstu_lmsd_bwd.restype = ctypes.c_int
             lib.hstu_lmsd_bwd.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            lib.hstu_lmsd_bwd_noalloc.restype = ctypes.c_int
+            lib.hstu_lmsd_bwd_noalloc.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_clock_sample.restype = ctypes.c_int
             lib.hstu_clock_sample.argtypes = [vp, ctypes.c_int32, vp]
             lib.hstu_last_error.restype = ctypes.c_char_p
@@ -514,6 +517,37 @@ def lmsd_bwd(dy: torch.Tensor, x: torch.Tensor, u: torch.Tensor, weight: torch.T
                                        dx.data_ptr(), du.data_ptr(), dweight.data_ptr() if dweight is not None else None,
                                        dbias.data_ptr(), ws_ptr, ws_bytes, _stream(s)))
     return dx, du, dweight, dbias
+
+
+def lmsd_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, u: torch.Tensor, weight: torch.Tensor,
+                     bias: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor, dx: torch.Tensor,
+                     du: torch.Tensor, dweight: Optional[torch.Tensor], dbias: torch.Tensor,
+                     dropout_ratio: float = 0.0, apply_u_silu: bool = True, concat_u: bool = True,
+                     concat_x: bool = True, eps: float = 1e-6, stream=None) -> None:
+    """lmsd_bwd for callers that cannot allocate: every output is caller-owned and the
+    column partials live in the library's own per-GPU scratch, so nothing is
+    allocated here or in the library.  ``dweight=None`` skips dweight.  Calls that
+    overlap on one GPU share that scratch and race."""
+    compute_dweight = dweight is not None
+    a = _lmsd_args(x, u, eps, dropout_ratio, apply_u_silu, concat_u, concat_x, compute_dweight)
+    n, d = a.n, a.d
+    segs = 1 + a.concat_u + a.concat_x
+    a.dy_stride = _rowmat("dy", dy, n, segs * d)
+    _vec("weight", weight, d)
+    _vec("bias", bias, d)
+    _vec("mean", mean, n, torch.float32)
+    _vec("rstd", rstd, n, torch.float32)
+    a.dx_stride = _rowmat("dx", dx, n, d)
+    a.du_stride = _rowmat("du", du, n, d)
+    _vec("dbias", dbias, d)
+    if compute_dweight:
+        _vec("dweight", dweight, d)
+    s = _launch_stream(stream, x.device)
+    _check(library().hstu_lmsd_bwd_noalloc(ctypes.byref(a), dy.data_ptr(), x.data_ptr(), u.data_ptr(),
+                                           weight.data_ptr(), bias.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+                                           dx.data_ptr(), du.data_ptr(),
+                                           dweight.data_ptr() if compute_dweight else None, dbias.data_ptr(),
+                                           _stream(s)))
 
 
 def hstu_bwd_dkdv_ds(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ds,

@@ -297,6 +297,22 @@ HSTU_API hstu_status_t hstu_lmsd_bwd(const hstu_lmsd_args_t* args, const void* d
  * ========================================================================== */
 HSTU_API hstu_status_t hstu_clock_sample(uint64_t* samples, int32_t count, hipStream_t stream);
 
+/* hstu_lmsd_bwd for callers that cannot allocate (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the column partials in a scratch array the library holds on
+ * each GPU for the life of the process (8,323,072 bytes: 1024 partial rows of
+ * 2 x 1016 fp32, the most any valid args need; args needing more, which the D
+ * limit rules out, are HSTU_ERR_INVALID_ARGUMENT).  Allocates nothing.  The
+ * array is looked up (hipGetSymbolAddress) on a device's first call, with that
+ * device current; HSTU_ERR_DEVICE if that fails.  Every call on one GPU shares
+ * its array: calls that overlap on one GPU (other streams, other threads, or
+ * before an earlier call's kernels finished on another stream) race and give
+ * wrong results; calls ordered on one stream do not. */
+HSTU_API hstu_status_t hstu_lmsd_bwd_noalloc(const hstu_lmsd_args_t* args, const void* dy, const void* x,
+                                    const void* u, const void* weight, const void* bias, const float* mean,
+                                    const float* rstd, void* dx, void* du, void* dweight, void* dbias,
+                                    hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 HSTU_API const char* hstu_last_error(void);
 

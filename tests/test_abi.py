@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dkdv_ds", "hstu_bwd_dq", "hstu_bwd_dq_ds",
         "hstu_bwd_workspace_size", "hstu_clock_sample", "hstu_fwd",
-        "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd",
+        "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_noalloc", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd",
         "hstu_status_string"])
 
 
