@@ -3,9 +3,9 @@
 
 One step = the whole path over one batch of synthetic input, launched through
 the C ABI on the current stream: hstu_fwd, then the backward as hstu_bwd runs it
--- under no mask, the causal mask or a window hstu_bwd_dkdv_ds (dK, dV, and dS
-stored in a workspace allocated before the timed region) then hstu_bwd_dq_ds;
-under the arbitrary mask, or with --recompute-dq, hstu_bwd_dq then hstu_bwd_dkdv.  Default
+-- hstu_bwd_dkdv_ds (dK, dV, and dS stored in a workspace allocated before the
+timed region) then hstu_bwd_dq_ds, or with --recompute-dq hstu_bwd_dq then
+hstu_bwd_dkdv.  Default
 workload: B=32 sequences with Zipf(1.2) lengths clipped to [16, 4096]
 (T = 23460), H=4, D=128, causal, bf16, plus an upstream gradient.
 
@@ -36,6 +36,7 @@ import numpy as np  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0
+CLOCK_WGS = 2048  # one-wave workgroups per clock sample: about 8 per CU, so most CUs appear in both
 DEFAULT_WORKLOAD = "zipf_b32_h4_d128_causal_fwdbwd"
 # Algorithmic flops per visible (query, key) pair and head, per unit of D:
 # forward: S (2) + A.V (2); dq kernel: S (2) + dO.V^T (2) + dS.K (2);
@@ -196,7 +197,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     else:
         wl = named_workload(workload)
         title = "HSTU attention fwd + bwd"
-        stored = wl.func is None
+        stored = True
         what = (f"Workload: B={wl.batch} packed sequences (T={wl.total_q}), H={wl.num_heads}, D={wl.head_dim}, "
                 f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + " +
                 ("hstu_bwd_dkdv_ds (bwd_dkdv_kernel storing dS) + hstu_bwd_dq_ds." if stored else
@@ -390,29 +391,42 @@ def cpu_model() -> str:
 
 
 def clock_summary(before, after) -> dict:
-    """Average shader clock of each XCD between two clock_sample launches (rows of
-    (real time at 100 MHz, shader cycles, XCC id, HW_ID)): per XCD, the median
-    cycle and real-time readings of its workgroups in each launch give
-    MHz = d(cycles) / d(real time) x 100.  counter_spread_cycles is the largest
-    spread of one XCD's cycle readings inside one launch (its workgroups start
-    within microseconds of each other, so a small spread shows the counter is
-    common to the XCD)."""
+    """Average shader clock between two clock_sample launches (rows of (real time at
+    100 MHz, shader cycles, XCC id, HW_ID)).  The cycle counter is per compute unit
+    (its readings on different CUs of one XCD differ by arbitrary offsets), so
+    readings are paired by CU -- the XCC id and the CU, SH and SE fields of HW_ID
+    (bits 8-15) -- and each CU seen in both launches gives d(cycles) / d(real time)
+    x 100 MHz; an XCD's clock is the median over its CUs, the chip's the mean over
+    XCDs.  counter_spread_cycles is the largest spread of one CU's readings inside
+    one launch (its workgroups start within microseconds of each other)."""
     b, a = np.asarray(before, dtype=np.int64), np.asarray(after, dtype=np.int64)
-    per, spread = {}, 0
-    for x in sorted(set(b[:, 2].tolist()) & set(a[:, 2].tolist())):
-        sb, sa = b[b[:, 2] == x], a[a[:, 2] == x]
-        spread = max(spread, int(np.ptp(sb[:, 1])), int(np.ptp(sa[:, 1])))
-        drt = float(np.median(sa[:, 0]) - np.median(sb[:, 0]))
-        dcy = float(np.median(sa[:, 1]) - np.median(sb[:, 1]))
+
+    def by_cu(s):
+        out, spread = {}, 0
+        for row in s:
+            key = (int(row[2]), (int(row[3]) >> 8) & 0xFF)
+            out.setdefault(key, []).append((int(row[0]), int(row[1])))
+        for v in out.values():
+            cy = [c for _, c in v]
+            spread = max(spread, max(cy) - min(cy))
+        return {k: min(v) for k, v in out.items()}, spread
+
+    sb, spb = by_cu(b)
+    sa, spa = by_cu(a)
+    per_xcd = {}
+    for key in sorted(set(sb) & set(sa)):
+        drt = sa[key][0] - sb[key][0]
         if drt > 0:
-            per[int(x)] = dcy / drt * 100.0
-    vals = list(per.values())
+            per_xcd.setdefault(key[0], []).append((sa[key][1] - sb[key][1]) / drt * 100.0)
+    med = {x: float(np.median(v)) for x, v in per_xcd.items()}
+    vals = list(med.values())
     region_us = float(np.median(a[:, 0]) - np.median(b[:, 0])) / 100.0
     return {"shader_mhz": round(float(np.mean(vals)), 1) if vals else None,
-            "per_xcd_mhz": {str(k): round(v, 1) for k, v in per.items()},
-            "region_us_by_realtime": round(region_us, 1), "counter_spread_cycles": spread,
-            "method": "s_memtime / s_memrealtime deltas per XCD between samples taken just before and after "
-                      "the timed steps on the same stream"}
+            "per_xcd_mhz": {str(k): round(v, 1) for k, v in sorted(med.items())},
+            "cus_paired": int(sum(len(v) for v in per_xcd.values())),
+            "region_us_by_realtime": round(region_us, 1), "counter_spread_cycles": int(max(spb, spa)),
+            "method": "s_memtime / s_memrealtime deltas per CU between samples taken just before and after "
+                      "the timed steps on the same stream; median per XCD, mean over XCDs"}
 
 
 def lmsd_bytes(n: int, d: int, segs: int) -> dict:
@@ -592,7 +606,6 @@ def main(argv=None) -> int:
     if stored:
         print(f"[bench] backward through stored dS: workspace {ws_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
     kernels = ["fwd"] + ((["bwd_dkdv_ds", "bwd_dq_ds"] if stored else ["bwd_dq", "bwd_dkdv"]) if has_bwd else [])
-    dskw = {key: val for key, val in kw.items() if key != "func"}
 
     def step(events=None):
         if events is not None:
@@ -601,10 +614,10 @@ def main(argv=None) -> int:
         if events is not None:
             events[1].record(stream)
         if stored:
-            hstu.hstu_bwd_dkdv_ds(do, q, k, v, cu_q, cu_k, ds=ws, dk=dk, dv=dv, stream=stream, **dskw)
+            hstu.hstu_bwd_dkdv_ds(do, q, k, v, cu_q, cu_k, ds=ws, dk=dk, dv=dv, stream=stream, **kw)
             if events is not None:
                 events[2].record(stream)
-            hstu.hstu_bwd_dq_ds(q, k, cu_q, cu_k, ds=ws, dq=dq, stream=stream, **dskw)
+            hstu.hstu_bwd_dq_ds(q, k, cu_q, cu_k, ds=ws, dq=dq, stream=stream, **kw)
             if events is not None:
                 events[3].record(stream)
         elif has_bwd:
@@ -622,21 +635,22 @@ def main(argv=None) -> int:
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()  # barrier: one rank
-    clk0 = hstu.clock_sample(64, dev, stream)
+    clk0 = hstu.clock_sample(CLOCK_WGS, dev, stream)
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(ev[s])
-    clk1 = hstu.clock_sample(64, dev, stream)
+    clk1 = hstu.clock_sample(CLOCK_WGS, dev, stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     clock = clock_summary(clk0.cpu().numpy(), clk1.cpu().numpy())
     print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s; shader clock {clock['shader_mhz']} MHz "
-          f"(per XCD {clock['per_xcd_mhz']}, counter spread {clock['counter_spread_cycles']} cycles, "
+          f"(per XCD {clock['per_xcd_mhz']}, {clock['cus_paired']} CUs paired, counter spread "
+          f"{clock['counter_spread_cycles']} cycles, "
           f"region {clock['region_us_by_realtime']} us by the real-time counter)", file=sys.stderr, flush=True)
     if args.clock_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.clock_out)), exist_ok=True)
         with open(args.clock_out, "w") as f:
-            json.dump(clock, f)
+            json.dump(dict(clock, samples_before=clk0.cpu().tolist(), samples_after=clk1.cpu().tolist()), f)
 
     per_kernel_ms = {}
     for i, name in enumerate(kernels):

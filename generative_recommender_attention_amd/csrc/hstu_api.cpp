@@ -192,23 +192,38 @@ hstu_status_t run_dq(const hstu_args_t* a, const void* dout, const void* q, cons
 }
 
 // Layout of stored dS for validated args (stored = false where the backward always
-// recomputes): row-block slots per head, key-group slots per row block, the
-// window's relative offset (or -1) and the key groups the dk/dv grid covers.
+// recomputes): blocks per head, key-group slots per row block of a window stored
+// relative to the row block (rel >= 0: ceil(left / 32), else -1), the causal
+// packing flag and the key groups the dk/dv grid covers.
 struct DsLayout {
     bool stored;
-    int64_t nb, kg, kgr;
+    int64_t head, kg, kgr;
     int32_t rel;
+    bool tri;
 };
+
+// Largest sum over sequences of f(n_b), f convex with f(0) = 0, over every batch of at
+// most B sequences whose row-block counts n_b = ceil(L_b / 32) satisfy n_b <= nmax and
+// sum n_b <= N, N = (T + 31 B) / 32 (sum ceil(L_b / 32) <= sum (L_b + 31) / 32): a convex
+// sum is largest at a vertex of that polytope, i.e. k = min(B, N / nmax) sequences of
+// nmax row blocks and one of the remainder.
+template <class F>
+int64_t convex_bound(int64_t T, int64_t B, int64_t maxlen, const F& f) {
+    const int64_t N = (T + 31 * B) / 32, nmax = (maxlen + 31) / 32;
+    if (nmax == 0) return 0;
+    const int64_t k = std::min<int64_t>(B, N / nmax);
+    const int64_t r = k < B ? std::min<int64_t>(N - k * nmax, nmax) : 0;
+    return k * f(nmax) + f(r);
+}
+
 DsLayout ds_layout(const hstu_args_t& a) {
-    DsLayout l{false, 0, 0, 0, -1};
+    DsLayout l{false, 0, 0, 0, -1, false};
     const hstu::MaskKind mk = mask_kind(a);
-    if (mk == hstu::MaskKind::Func || a.total_q == 0 || a.total_k == 0) return l;
+    if (a.total_q == 0 || a.total_k == 0) return l;
     l.kgr = 4 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN);
     // the dq kernel addresses a row block's groups by 32-bit byte offsets
     if (l.kgr * 2 * hstu::kDsBlockElems > (int64_t)hstu::kMaxDsRowBlockBytes) return l;
-    l.stored = true;
-    l.nb = ((int64_t)a.total_q + 31 * (int64_t)a.batch) / 32;
-    l.kg = l.kgr;
+    const int64_t B = a.batch, nb = ((int64_t)a.total_q + 31 * B) / 32;
     if (mk == hstu::MaskKind::Window) {
         // row block R (rows 32 R ..) meets key groups R - ceil(left / 32) .. R + floor((31 + right) / 32)
         auto side = [&](int32_t w) { return w < 0 || w > a.max_seqlen_k ? (int64_t)a.max_seqlen_k : (int64_t)w; };
@@ -216,8 +231,24 @@ DsLayout ds_layout(const hstu_args_t& a) {
         if (lo + hi + 1 < l.kgr) {
             l.kg = lo + hi + 1;
             l.rel = (int32_t)lo;
+            l.head = nb * l.kg;  // one slot per row-block slot (cu_q[b] + 31 b) / 32 + R
         }
     }
+    if (l.rel < 0 && mk == hstu::MaskKind::Causal) {
+        // row block R of a sequence keeps min(R + 1, nG) <= R + 1 groups: at most
+        // n (n + 1) / 2 blocks for a sequence of n row blocks
+        l.tri = true;
+        l.head = convex_bound(a.total_q, B, a.max_seqlen_q, [](int64_t n) { return n * (n + 1) / 2; });
+    } else if (l.rel < 0) {
+        // every row block keeps nG groups (no mask, a wide window, or the arbitrary mask,
+        // whose row blocks use a range of groups not known on the host): nR nG blocks per
+        // sequence, and sum_b nR_b nG_b is at most (sum_b nR_b) max nG and (sum_b nG_b) max nR
+        const int64_t nq = nb, nk = ((int64_t)a.total_k + 31 * B) / 32;
+        l.head = std::min(nq * (((int64_t)a.max_seqlen_k + 31) / 32), nk * (((int64_t)a.max_seqlen_q + 31) / 32));
+    }
+    // the kernels sum per-sequence block counts in int32
+    if (l.head >= (int64_t(1) << 31)) return l;
+    l.stored = true;
     return l;
 }
 
@@ -228,17 +259,15 @@ hstu_status_t ds_bytes(const hstu_args_t& a, size_t& bytes) {
     bytes = 0;
     const DsLayout l = ds_layout(a);
     if (!l.stored) return HSTU_OK;
-    const double approx = (double)a.num_heads * (double)l.nb * (double)l.kg * 2.0 * hstu::kDsBlockElems;
+    const double approx = (double)a.num_heads * (double)l.head * 2.0 * hstu::kDsBlockElems;
     if (approx > 9.0e18)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "stored dS would need %.3g bytes", approx);
-    bytes = (size_t)a.num_heads * (size_t)l.nb * (size_t)l.kg * 2 * hstu::kDsBlockElems;
+    bytes = (size_t)a.num_heads * (size_t)l.head * 2 * hstu::kDsBlockElems;
     return HSTU_OK;
 }
 
 // Checks a dS workspace against the args and points the parameter block at it.
 hstu_status_t bind_ds(const hstu_args_t& a, void* ds, size_t ds_bytes_given, hstu::AttnParams& p) {
-    if (mask_kind(a) == hstu::MaskKind::Func)
-        return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs the full, causal or window mask");
     if (8 * (((int64_t)a.max_seqlen_k + hstu::kBwdBlockN - 1) / hstu::kBwdBlockN) * hstu::kDsBlockElems >
         (int64_t)hstu::kMaxDsRowBlockBytes)
         return fail(HSTU_ERR_UNSUPPORTED, "stored dS needs max_seqlen_k below 2^25");
@@ -251,9 +280,10 @@ hstu_status_t bind_ds(const hstu_args_t& a, void* ds, size_t ds_bytes_given, hst
         return fail(HSTU_ERR_INVALID_ARGUMENT, "dS workspace is null or not 256-byte aligned");
     const DsLayout l = ds_layout(a);
     p.ds = static_cast<uint16_t*>(ds);
-    p.ds_nb = l.nb;
+    p.ds_head = l.head;
     p.ds_kg = (int32_t)l.kg;
     p.ds_rel = l.rel;
+    p.ds_tri = l.tri ? 1 : 0;
     p.ds_kgr = (int32_t)l.kgr;
     return HSTU_OK;
 }

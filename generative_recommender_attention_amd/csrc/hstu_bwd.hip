@@ -1,6 +1,6 @@
 // HSTU attention backward on gfx950: deterministic kernels, no atomics.  Two
 // routes: a dq kernel and a dk/dv kernel that both recompute the scores (no
-// workspace), or -- under any mask but the arbitrary one, given a workspace --
+// workspace), or -- given a workspace --
 // the dk/dv kernel storing dS and a dq kernel that reads it (described last).
 //
 // The backward receives dO and q, k, v only (HSTU Attention page, "High-level
@@ -348,10 +348,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     }
 }
 
-// Where a wave of the dk/dv kernel stores the dS of its 32 x 32 block: `p` is
-// the lane's destination (the 64-byte row of its key, element 8 g); `kdead`
-// (read when the wave-uniform `kcut` is set) whether the lane's key lies past
-// the sequence (stored as 0); nothing is stored unless the wave-uniform `on` is set.
+// Where a wave of the dk/dv kernel stores the dS of its 32 x 32 block: `p` is the
+// block (wave-uniform; lane (l32, g) writes the 64-byte row of its key l32 from
+// element 8 g); `kdead` (read when the wave-uniform `kcut` is set) whether the
+// lane's key lies past the sequence (stored as 0); nothing is stored unless the
+// wave-uniform `on` is set.
 struct DsOut {
     uint16_t* p;
     bool on, kcut, kdead;
@@ -369,7 +370,7 @@ __device__ __forceinline__ int ds_pos_row(int c) { return (c & 0x13) | ((c & 4) 
 // tests row 8 k + 4 g + j of the block (accumulator register 4 k + j) against
 // bit l32 of the LDS word at mw + 32 k + 4 j.  The bf16 dS goes to `ds` as it is
 // formed (the operand of dK^T itself is left as computed).
-template <int D, int MT>
+template <int D, int MT, int PF = 6>
 __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t drow, uint32_t krow, uint32_t vrow, uint32_t qtr,
                                             uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
@@ -379,7 +380,8 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     constexpr int NS = D / 16;
     constexpr int NA = 4 * NS;   // reads for S and dA: step kk, (Q, K, dO, V)
     constexpr int NG = 4 * NDB;  // reads for dV, dK: half, column block, (dO^T, Q^T)
-    constexpr int PF = 6;
+    // PF: LDS reads issued ahead of their products
+
     uint4 rd[NA + NG];
     auto read = [&](int r) {
         if (r < NA) {
@@ -442,17 +444,21 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     const uint4 a[2] = {pack_operand(av), pack_operand(av + 8)};
     const uint4 d[2] = {pack_operand(dv), pack_operand(dv + 8)};
     if (ds.on) {
-        // the two dS^T operand halves as they are: rows past the sequence hold 0 (masked above)
-        uint4 s0 = d[0], s1 = d[1];
-        if (ds.kcut) {
-            keep_branch();
-            if (ds.kdead) s0 = s1 = make_uint4(0, 0, 0, 0);
+        // the two dS^T operand halves as they are (rows past the sequence hold 0, masked
+        // above; keys past it are stored as 0), with streaming stores: dS is read once,
+        // by the dq kernel, and must not push the Q and dO rows that the other key
+        // blocks re-read out of the caches
+        const int l = threadIdx.x & 63;
+        uint16_t* dst = ds.p + (l & 31) * kDsRowElems + 8 * (l >> 5);
+        if (ds.kcut && ds.kdead) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst));
+            __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst + 16));
+        } else {
+            const u32x4 v0 = {d[0].x, d[0].y, d[0].z, d[0].w}, v1 = {d[1].x, d[1].y, d[1].z, d[1].w};
+            __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dst));
+            __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dst + 16));
         }
-        // streaming stores: dS is read once, by the dq kernel, and must not push the
-        // Q and dO rows that the other key blocks re-read out of the caches
-        const u32x4 v0 = {s0.x, s0.y, s0.z, s0.w}, v1 = {s1.x, s1.y, s1.z, s1.w};
-        __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(ds.p));
-        __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(ds.p + 16));
     }
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -463,13 +469,13 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     }
 }
 
-template <int D, MaskKind MK>
+template <int D, MaskKind MK, bool DS>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr bool FUNC = MK == MaskKind::Func;
-    // stored dS (no mask, causal or window: the row blocks of the walk start on multiples of 32)
-    constexpr bool DS = MK != MaskKind::Func;
+    // DS: the launch stores dS (p.ds is the workspace); the row blocks of the walk then
+    // start on multiples of 32 under every mask
     constexpr int DM = D < 32 ? 32 : D;
     constexpr int KSTEPS = D / 16;
     // [Q slot 0 | Q slot 1 | dO slot 0 | dO slot 1 | K rows of the block | V rows of the block]
@@ -503,12 +509,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     const int key0 = n0 + 32 * kw;
     const int my_key = key0 + l32;
     const bool wave_live = key0 < sb.lk;
-    // stored dS: this lane's element of the sequence's first row-block slot (block rows
-    // are keys here: lane l32 writes the row of its key); a tile adds its block index
+    // stored dS: the sequence's first block (wave-uniform); a tile adds its block's
+    // index within the sequence's share
     uint16_t* ds_base = nullptr;
-    if (DS && p.ds != nullptr) {
-        const int64_t slot = ((int64_t)sb.q0 + 31 * (int64_t)b) >> 5;
-        ds_base = p.ds + ((int64_t)h * p.ds_nb + slot) * p.ds_kg * kDsBlockElems + l32 * kDsRowElems + 8 * g;
+    const int ds_ng = (sb.lk + 31) >> 5;  // key groups of the sequence
+    if constexpr (DS) {
+        const int64_t seq0 = p.ds_rel >= 0 ? (((int64_t)sb.q0 + 31 * (int64_t)b) >> 5) * p.ds_kg
+                                           : ds_seq_base(p.cu_q, p.cu_k, b, p.ds_tri != 0);
+        ds_base = static_cast<uint16_t*>(
+            const_cast<void*>(uniform_ptr(p.ds + ((int64_t)h * p.ds_head + seq0) * kDsBlockElems)));
     }
 
     // the block's K and V rows into LDS; rows past the sequence repeat its last row
@@ -576,7 +585,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
             qlo = min(qlo, q_red[2 * w]);
             qhi = max(qhi, q_red[2 * w + 1]);
         }
-        q_begin = qhi >= qlo ? qlo : 0;
+        // stored dS: row blocks start on multiples of 32 (the extra rows see none of the keys)
+        q_begin = qhi >= qlo ? (DS ? qlo & ~31 : qlo) : 0;
         q_end = qhi >= qlo ? qhi + 1 : 0;
     }
     const int ntiles = q_end > q_begin ? (q_end - q_begin + BMQ - 1) / BMQ : 0;
@@ -653,20 +663,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     const uint64_t seen = __ballot(live && word != 0);
                     const uint64_t cut = __ballot(live && word != valid);
                     // rows past the sequence (copies of its last row) must be masked out too
-                    if (seen != 0)
+                    if (seen != 0) {
+                        // stored dS: the block is written exactly when it holds a visible pair,
+                        // the test the dq kernel repeats before reading it
+                        DsOut ds{nullptr, false, false, false};
+                        if constexpr (DS) {
+                            ds.on = true;
+                            ds.p = ds_base + (ds_rows_before(row0 >> 5, ds_ng, false) + (key0 >> 5)) * kDsBlockElems;
+                            ds.kcut = key0 + 32 > sb.lk;
+                            ds.kdead = my_key >= sb.lk;
+                        }
                         dkdv_block<D, kBits>(cut != 0 || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
-                                             roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g),
-                                             DsOut{nullptr, false, false, false}, p.exp_c, p.alpha);
+                                             roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g), ds,
+                                             p.exp_c, p.alpha);
+                    }
                 }
             } else {
                 // waves whose keys no row of the block sees, or that lie past the sequence, skip it
                 const bool run = WINDOW ? row0 + 32 > any_lo && row0 < any_hi : !(CAUSAL && row0 + 31 < key0);
                 if (wave_live && run && row0 < sb.lq) {
                     DsOut ds{nullptr, false, false, false};
-                    if (DS && ds_base != nullptr) {
+                    if constexpr (DS) {
                         ds.on = true;
-                        const int rb = row0 >> 5, goff = p.ds_rel >= 0 ? rb - p.ds_rel : 0;
-                        ds.p = ds_base + ((int64_t)rb * p.ds_kg + (key0 >> 5) - goff) * kDsBlockElems;
+                        const int rb = row0 >> 5;
+                        const int64_t blk = p.ds_rel >= 0 ? (int64_t)rb * p.ds_kg + (key0 >> 5) - (rb - p.ds_rel)
+                                                          : ds_rows_before(rb, ds_ng, p.ds_tri != 0) + (key0 >> 5);
+                        ds.p = ds_base + blk * kDsBlockElems;
                         ds.kcut = key0 + 32 > sb.lk;
                         ds.kdead = my_key >= sb.lk;
                     }
@@ -733,7 +755,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     }
 }
 
-// dq from stored dS (no mask, causal or window): one workgroup per (256-row block,
+// dq from stored dS: one workgroup per (256-row block,
 // sequence, head), 8 waves of 32 rows, one workgroup per CU.  Per 64-key tile K
 // is staged row-major in LDS (three slots, two tiles ahead, shared by the eight
 // waves) and each wave copies its rows' dS blocks into its own LDS ring of three
@@ -748,7 +770,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
 // right) row block R uses groups (row0 - left) / 32 .. (row0 + 31 + right) / 32
 // (none once row0 - left reaches the sequence's keys), the groups that hold a
 // visible pair; the dk/dv kernel wrote each of those (and possibly some blocks of
-// zeros besides).
+// zeros besides).  Under the arbitrary mask row block R uses the groups from its
+// rows' smallest to their largest visible key, and among those only the groups
+// that hold a visible pair (a ballot over its rows' visibility words per tile):
+// the blocks the dk/dv kernel computed, and so stored.
 template <int D>
 __device__ __forceinline__ void dq_ds_tile(uint32_t kt, const uint4 (&dsop)[4],
                                            f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
@@ -790,9 +815,10 @@ constexpr int NWD = BMD / 32;     // its waves
 
 template <int D, MaskKind MK>
 __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
-    static_assert(MK != MaskKind::Func, "stored dS exists for the full, causal and window masks");
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
+    constexpr bool FUNC = MK == MaskKind::Func;
+    __shared__ int wrange[FUNC ? 2 * 8 : 1];  // func: each wave's key-group range
     constexpr int DM = D < 32 ? 32 : D;
     // [K slots 0-2 | wave 0: dS slots 0-2 | wave 1 | ... | wave 7]
     __shared__ __attribute__((aligned(16))) uint16_t smem[3 * kTileElems + NWD * 3 * kDsSlotBytes / 2];
@@ -829,19 +855,46 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
         }
     };
     int gA, gB;
-    groups(row0, gA, gB);
-    gA = __builtin_amdgcn_readfirstlane(gA);
-    gB = __builtin_amdgcn_readfirstlane(gB);
-    // the workgroup walks the 64-key tiles that hold some wave's groups
     int wga = 0x7fffffff, wgb = 0;
-    for (int w = 0; w < NWD; ++w) {
-        int ga, gb;
-        groups(m0 + 32 * w, ga, gb);
-        if (ga < gb) {
-            wga = min(wga, ga);
-            wgb = max(wgb, gb);
+    int f0 = 0, f1 = 0, f2 = 0;  // func: this lane's row's first endpoints
+    if constexpr (FUNC) {
+        // the range of the row block's visible keys, reduced over its 32 rows (lanes l
+        // and l + 32 hold the same row); inside it, the dk/dv kernel wrote exactly the
+        // blocks that hold a visible pair, which the walk tests per tile below
+        const int frow = sb.q0 + min(my_row, sb.lq - 1);
+        f0 = p.func[frow];
+        if (p.func_n > 1) {
+            f1 = p.func[(int64_t)p.func_ld + frow];
+            f2 = p.func[2 * (int64_t)p.func_ld + frow];
+        }
+        int rlo = 0x7fffffff, rhi = 0;
+        if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
+        func_group_range(wave_min(rlo), wave_max(rhi), gA, gB);
+        gB = min(gB, gmax);
+        if (lane == 0) {
+            wrange[2 * wave] = gA;
+            wrange[2 * wave + 1] = gB;
+        }
+        __syncthreads();
+        for (int w = 0; w < NWD; ++w)
+            if (wrange[2 * w] < wrange[2 * w + 1]) {
+                wga = min(wga, wrange[2 * w]);
+                wgb = max(wgb, wrange[2 * w + 1]);
+            }
+    } else {
+        groups(row0, gA, gB);
+        // the workgroup walks the 64-key tiles that hold some wave's groups
+        for (int w = 0; w < NWD; ++w) {
+            int ga, gb;
+            groups(m0 + 32 * w, ga, gb);
+            if (ga < gb) {
+                wga = min(wga, ga);
+                wgb = max(wgb, gb);
+            }
         }
     }
+    gA = __builtin_amdgcn_readfirstlane(gA);
+    gB = __builtin_amdgcn_readfirstlane(gB);
     const int t0 = __builtin_amdgcn_readfirstlane(wgb > 0 ? wga >> 1 : 0);
     const int t1 = __builtin_amdgcn_readfirstlane(wgb > 0 ? (wgb + 1) >> 1 : 0);
     const int kv_end = min(sb.lk, 32 * wgb);  // K rows past it only meet zero operands
@@ -849,11 +902,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
     // G (block 0 when the wave uses none: its copies then fetch in-bounds data that
     // is never used, so that every tile issues the same four copies); each copy moves
     // 1 KB of a block as it is.
+    const int64_t seq0 = p.ds_rel >= 0 ? (((int64_t)sb.q0 + 31 * (int64_t)b) >> 5) * p.ds_kg
+                                       : ds_seq_base(p.cu_q, p.cu_k, b, p.ds_tri != 0);
     int64_t blk0 = 0;
     if (gA < gB) {
-        const int64_t slot = ((int64_t)sb.q0 + 31 * (int64_t)b) >> 5;
-        const int rb = row0 >> 5, goff = p.ds_rel >= 0 ? rb - p.ds_rel : 0;
-        blk0 = ((int64_t)h * p.ds_nb + slot + rb) * p.ds_kg - goff;
+        const int rb = row0 >> 5;
+        blk0 = (int64_t)h * p.ds_head + seq0 +
+               (p.ds_rel >= 0 ? (int64_t)rb * p.ds_kg - (rb - p.ds_rel)
+                              : ds_rows_before(rb, (sb.lk + 31) >> 5, p.ds_tri != 0));
     }
     const uint16_t* dsg = static_cast<const uint16_t*>(uniform_ptr(p.ds + blk0 * kDsBlockElems));
     const uint32_t cpy_off = 16u * (uint32_t)lane;
@@ -919,13 +975,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
             if (2 * t + 1 >= gA && 2 * t < gB) {
                 const uint32_t sl = dsl + (uint32_t)(t % 3) * kDsSlotBytes;
                 uint4 op[4];
-                if (2 * t >= gA) {
+                bool use0 = 2 * t >= gA, use1 = 2 * t + 1 < gB;
+                if constexpr (FUNC) {
+                    // a group is used only when some row of the block sees one of its keys:
+                    // the dk/dv kernel's test for storing the block (others hold no data)
+                    const bool live = my_row < sb.lq;
+                    const int row = sb.q0 + min(my_row, sb.lq - 1);
+                    if (use0)
+                        use0 = __ballot(live && func_bits32_pre(f0, f1, f2, p.func, p.func_ld, p.func_n, row, 64 * t,
+                                                                sb.lk) != 0u) != 0;
+                    if (use1)
+                        use1 = __ballot(live && func_bits32_pre(f0, f1, f2, p.func, p.func_ld, p.func_n, row,
+                                                                64 * t + 32, sb.lk) != 0u) != 0;
+                }
+                if (use0) {
                     op[0] = ds_read_tr16x2(sl + dtr.x, sl + dtr.y);
                     op[1] = ds_read_tr16x2(sl + 1024u + dtr.x, sl + 1024u + dtr.y);
                 } else {
                     op[0] = op[1] = make_uint4(0, 0, 0, 0);  // the first group is not used
                 }
-                if (2 * t + 1 < gB) {
+                if (use1) {
                     op[2] = ds_read_tr16x2(sl + 2048u + dtr.x, sl + 2048u + dtr.y);
                     op[3] = ds_read_tr16x2(sl + 3072u + dtr.x, sl + 3072u + dtr.y);
                 } else {
@@ -971,7 +1040,7 @@ hipError_t launch_dq_ds_mask(const AttnParams& p, MaskKind mask, hipStream_t str
         case MaskKind::None: return launch_dq_ds<D, MaskKind::None>(p, stream);
         case MaskKind::Causal: return launch_dq_ds<D, MaskKind::Causal>(p, stream);
         case MaskKind::Window: return launch_dq_ds<D, MaskKind::Window>(p, stream);
-        default: return hipErrorInvalidValue;
+        case MaskKind::Func: return launch_dq_ds<D, MaskKind::Func>(p, stream);
     }
 }
 
@@ -987,7 +1056,10 @@ template <int D, MaskKind MK>
 hipError_t launch_dkdv(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.items * p.heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    if (p.ds != nullptr)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -489,6 +489,24 @@ __device__ __forceinline__ void func_key_range(const int32_t* f, int ld, int N, 
     for (int n = 1; n + 1 < N; n += 2) add(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row]);
 }
 
+// func_key_range with the row's first three endpoints already in registers.
+__device__ __forceinline__ void func_key_range_pre(int f0, int f1, int f2, const int32_t* f, int ld, int N, int row,
+                                                   int lk, int& lo, int& hi) {
+    lo = 0x7fffffff;
+    hi = 0;
+    auto add = [&](int a, int b) {
+        a = max(a, 0);
+        b = min(b, lk);
+        if (b > a) {
+            lo = min(lo, a);
+            hi = max(hi, b);
+        }
+    };
+    add(0, f0);
+    if (N > 1) add(f1, f2);
+    for (int n = 3; n + 1 < N; n += 2) add(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row]);
+}
+
 // Whether row `row` sees any key of [k0, k1) (0 <= k0, k1 <= lk).
 __device__ __forceinline__ bool func_row_meets(const int32_t* f, int ld, int N, int row, int k0, int k1) {
     bool hit = min(f[row], k1) > k0;
@@ -506,6 +524,57 @@ __device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
     return x;
+}
+// The same over each half of the wave (lanes 0-31 and 32-63 separately).
+__device__ __forceinline__ int half_wave_min(int x) {
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ int half_wave_max(int x) {
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// Stored dS under the arbitrary mask: the key groups [ga, gb) of a 32-row block are
+// those from the smallest to the largest visible key of any of its rows, from the
+// block's reduced [lo, hi) (lo >= hi: no visible key, no groups).  The dk/dv kernel
+// writes every block of that range (those no visible pair falls in as zeros) and the
+// dq kernel reads exactly those, both reducing the same rows.
+__device__ __forceinline__ void func_group_range(int lo, int hi, int& ga, int& gb) {
+    ga = lo < hi ? lo >> 5 : 0;
+    gb = lo < hi ? (hi + 31) >> 5 : 0;
+}
+
+// ---- stored dS layout ----------------------------------------------------------
+// Blocks (32 rows x 32 keys) of stored dS that row blocks 0 .. R - 1 of a sequence
+// with nG key groups keep: row block R' keeps min(R' + 1, nG) of them under the
+// causal mask (tri), nG otherwise.  With R = the sequence's row-block count it is
+// the sequence's whole share.
+__device__ __forceinline__ int64_t ds_rows_before(int R, int nG, bool tri) {
+    const int64_t r = R, n = nG;
+    if (!tri) return r * n;
+    return r <= n ? r * (r + 1) / 2 : n * (n + 1) / 2 + (r - n) * n;
+}
+
+// Blocks of stored dS of the sequences before batch entry b (wave-uniform b; every
+// lane returns the same value): a lane-parallel sum over the sequences, 64 at a
+// time.  Each sum fits int32: the host sizes the workspace by a bound on the total
+// below 2^31 blocks per head.
+__device__ __forceinline__ int64_t ds_seq_base(const int32_t* cu_q, const int32_t* cu_k, int b, bool tri) {
+    const int lane = threadIdx.x & 63;
+    int64_t acc = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        const int bb = b0 + lane;
+        int cnt = 0;
+        if (bb < b) {
+            const int nR = (cu_q[bb + 1] - cu_q[bb] + 31) >> 5, nG = (cu_k[bb + 1] - cu_k[bb] + 31) >> 5;
+            cnt = (int)ds_rows_before(nR, nG, tri);
+        }
+        acc += wave_sum(cnt);
+    }
+    return acc;
 }
 
 // Row of accumulator register r (0..15) inside a 32-row block, for lane half g.

@@ -39,16 +39,21 @@ struct AttnParams {
     int32_t func_ld;
     TensorRef q, k, v, dout;
     TensorOut o, dq, dk, dv;
-    // Backward through stored dS (no mask, causal or window): the dk/dv kernel writes,
+    // Backward through stored dS (any mask): the dk/dv kernel writes,
     // and the dS-reading dq kernel reads, bf16 dS in 2 KB blocks of 32 query rows x 32
-    // keys.  Block (head h, row block R of batch entry b, key group G) sits at block
-    // index (h ds_nb + (cu_q[b] + 31 b) / 32 + R) ds_kg + G - goff(R), goff(R) = R - ds_rel
-    // when ds_rel >= 0 (a window: R's groups lie in [R - ds_rel, R - ds_rel + ds_kg)),
-    // else 0; null: the dk/dv kernel writes none.
+    // keys; null: the dk/dv kernel writes none.  Block (head h, row block R of batch
+    // entry b, key group G) sits at block index h ds_head + ds_block(...) below:
+    //  - a window stored relative to R (ds_rel >= 0): ((cu_q[b] + 31 b) / 32 + R) ds_kg
+    //    + G - (R - ds_rel): R's groups lie in [R - ds_rel, R - ds_rel + ds_kg);
+    //  - otherwise the sequences' blocks are packed one after another (base(b) = the
+    //    blocks of the sequences before b), row block after row block, and row block R
+    //    keeps the groups it has: min(R + 1, nG) under the causal mask (ds_tri; G <= R),
+    //    nG otherwise, nG = ceil(L_k / 32).
     uint16_t* ds;
-    int64_t ds_nb;         // row-block slots per head: (T_q + 31 B) / 32
-    int32_t ds_kg;         // key-group slots per row block
+    int64_t ds_head;       // blocks per head (a bound on every sequence mix the sizes allow)
+    int32_t ds_kg;         // window stored relative to R: key-group slots per row block
     int32_t ds_rel;        // ceil(left / 32) for a window stored relative to R, else -1
+    int32_t ds_tri;        // 1: causal packing (row block R keeps groups 0..R)
     int32_t ds_kgr;        // key groups the dk/dv grid covers: 4 ceil(max_seqlen_k / 128)
 };
 

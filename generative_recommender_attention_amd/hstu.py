@@ -329,10 +329,9 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
              store_ds: bool = True) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """(dq, dk, dv) of HSTU attention for upstream gradient ``dout``.
 
-    With ``store_ds`` (and any mask but the arbitrary one) the dk/dv kernel stores dS
-    in ``workspace`` (a device byte tensor of ``hstu_bwd_workspace_size`` bytes,
-    allocated here when not given) and dq is computed from it; with
-    ``store_ds=False``, or under the other masks, the dq kernel recomputes the
+    With ``store_ds`` the dk/dv kernel stores dS in ``workspace`` (a device byte
+    tensor of ``hstu_bwd_workspace_size`` bytes, allocated here when not given) and
+    dq is computed from it; with ``store_ds=False`` the dq kernel recomputes the
     scores and no workspace is used."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
@@ -552,11 +551,11 @@ def lmsd_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, u: torch.Tensor, weight:
 
 def hstu_bwd_dkdv_ds(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ds,
                      alpha=1.0, scaling_seqlen=None, causal=True, dk=None, dv=None, stream=None,
-                     window_size=None):
+                     window_size=None, func=None):
     """(dk, dv), storing dS in ``ds`` (``hstu_bwd_workspace_size`` bytes) for
-    ``hstu_bwd_dq_ds``; no mask, the causal mask or a window."""
+    ``hstu_bwd_dq_ds``, under any mask."""
     H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size)
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     s = _launch_stream(stream, q.device)
     with torch.cuda.stream(s):
         dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
@@ -572,11 +571,11 @@ def hstu_bwd_dkdv_ds(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
 
 
 def hstu_bwd_dq_ds(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ds, alpha=1.0,
-                   scaling_seqlen=None, causal=True, dq=None, stream=None, window_size=None):
+                   scaling_seqlen=None, causal=True, dq=None, stream=None, window_size=None, func=None):
     """dq from the dS that ``hstu_bwd_dkdv_ds`` stored in ``ds`` for the same
     problem (``q`` gives the shape and strides of dq only; it is not read)."""
     H, D, pq, pk = _inputs(q, k, k, cu_seqlens_q, cu_seqlens_k)
-    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, None)
+    a = _args(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
     a.q, a.k = _stride(q), _stride(k)
     s = _launch_stream(stream, q.device)
     with torch.cuda.stream(s):

@@ -169,14 +169,24 @@ HSTU_API hstu_status_t hstu_fwd(const hstu_args_t* args,
  * the scores for dQ (written to *bytes).  Reads the scalars of `args` only (the
  * pointers in it are not used).  dS (above) is the factor that dQ and dK share;
  * the workspace holds it in bf16 without the 1 / L_scale, which the dQ kernel
- * applies with alpha.  The result is H x ((T_q + 31 B) / 32) x G blocks of 2 KB
- * (a bf16 dS block of 32 query rows x 32 keys per row-block slot and key-group
- * slot, whatever the sequence lengths turn out to be) with G = 4 ceil(max_seqlen_k
- * / 128) under no mask or the causal mask, and under a window (left, right) the
- * smaller of that and ceil(left / 32) + floor((31 + right) / 32) + 1 (the key
- * groups a 32-row block meets; a side of -1 counts as max_seqlen_k).  Under the
- * arbitrary mask, with no tokens on a side, or with max_seqlen_k of 2^25 or more
- * it is 0 (those backwards always recompute). */
+ * applies with alpha, in 2 KB blocks of 32 query rows x 32 keys.  A sequence of
+ * nR = ceil(L_q / 32) row blocks and nG = ceil(L_k / 32) key groups keeps
+ * sum_R min(R + 1, nG) blocks under the causal mask (the lower triangle) and
+ * nR nG otherwise; the sequences' blocks are packed one after another, the
+ * offsets computed on the device from cu_seqlens.  The size is H times a bound
+ * that holds for every length mix the sizes allow, with N_q = (T_q + 31 B) / 32,
+ * n = ceil(max_seqlen_q / 32), k = min(B, N_q / n), r = min(N_q - k n, n):
+ *   causal:  k n (n + 1) / 2 + r (r + 1) / 2 blocks per head (a sum of
+ *            triangles is largest with as many sequences as possible at the
+ *            longest length);
+ *   no mask: min(N_q ceil(max_seqlen_k / 32), N_k ceil(max_seqlen_q / 32)).
+ * A window (left, right) keeps ceil(left / 32) + floor((31 + right) / 32) + 1
+ * key-group slots per row-block slot (N_q of them, a side of -1 counting as
+ * max_seqlen_k) when that is below 4 ceil(max_seqlen_k / 128), else the no-mask
+ * layout; the arbitrary mask uses the no-mask layout (a row block's key groups
+ * depend on the endpoints, which the host never reads).  With no tokens on a
+ * side, with max_seqlen_k of 2^25 or more or a bound of 2^31 blocks per head or
+ * more, it is 0 (those backwards always recompute). */
 HSTU_API hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* args, size_t* bytes);
 
 /* Backward, all three gradients.  With a workspace of at least
@@ -209,8 +219,9 @@ HSTU_API hstu_status_t hstu_bwd_dkdv(const hstu_args_t* args, const void* dout,
 /* hstu_bwd_dkdv that also writes the bf16 dS of every 32 x 32 (rows x keys)
  * block it computes to `ds` (hstu_bwd_workspace_size() bytes, 256-byte aligned;
  * null allowed only when that size is 0), entries outside the mask as 0.  dK
- * and dV are bit-identical to hstu_bwd_dkdv's.  Mask none, causal or window
- * (the arbitrary mask is HSTU_ERR_UNSUPPORTED). */
+ * and dV are bit-identical to hstu_bwd_dkdv's.  Under the arbitrary mask it
+ * writes exactly the blocks that hold a visible pair; the rest of the workspace
+ * keeps what it held. */
 HSTU_API hstu_status_t hstu_bwd_dkdv_ds(const hstu_args_t* args, const void* dout,
                                const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -219,8 +230,9 @@ HSTU_API hstu_status_t hstu_bwd_dkdv_ds(const hstu_args_t* args, const void* dou
 
 /* dQ = alpha / L_scale * dS K from the dS that hstu_bwd_dkdv_ds stored in `ds`
  * for the same args and cu_seqlens (enqueue it first on the same stream, or
- * order the two otherwise).  Reads k and ds only; writes dq.  Mask none,
- * causal or window. */
+ * order the two otherwise).  Reads k and ds only (and, under the arbitrary mask,
+ * func, to skip the blocks with no visible pair); writes dq.  Any mask, with the
+ * same func contents as the hstu_bwd_dkdv_ds call. */
 HSTU_API hstu_status_t hstu_bwd_dq_ds(const hstu_args_t* args, const void* k,
                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                              const void* ds, size_t ds_bytes, void* dq,

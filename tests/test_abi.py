@@ -155,20 +155,24 @@ def ws_size(lib, a):
 
 
 @pytest.mark.parametrize("over,blocks", [
-    # 2 KB blocks: H x (T_q + 31 B) / 32 row-block slots x 4 ceil(max_seqlen_k / 128) key groups
-    (dict(), 2 * 2 * 4),                                                   # causal, B = 2, T_q = 32
-    (dict(mask=0), 2 * 2 * 4),                                             # no mask
-    (dict(mask=2, window_left=-1, window_right=0), 2 * 2 * 4),            # the causal window
+    # 2 KB blocks per head (times H = 2 unless set), sequences packed one after another.
+    # Causal: row block R keeps min(R + 1, nG) groups, bounded by k n(n + 1)/2 + r(r + 1)/2 with
+    # n = ceil(max_seqlen_q / 32), N = (T_q + 31 B) / 32, k = min(B, N / n), r = min(N - k n, n).
+    # No mask: nR nG per sequence, bounded by min(N_q ceil(max_k / 32), N_k ceil(max_q / 32)).
+    (dict(), 2 * 2),                                                       # N = 2, n = 1: k = 2, r = 0
+    (dict(mask=0), 2 * 2),                                                 # min(2 x 1, 2 x 1)
+    (dict(mask=2, window_left=-1, window_right=0), 2 * 2),                # the causal window
     (dict(batch=5, total_q=300, total_k=300, max_seqlen_q=129, max_seqlen_k=129, num_heads=3),
-     3 * ((300 + 31 * 5) // 32) * 8),
-    # window: key groups relative to the row block, ceil(left/32) + floor((31 + right)/32) + 1 of them
+     3 * (2 * 15 + 10)),                                                   # N = 14, n = 5: k = 2, r = 4
+    # window: key groups relative to the row block, ceil(left/32) + floor((31 + right)/32) + 1 slots
+    # per row-block slot (N = (T_q + 31 B) / 32 of them)
     (dict(mask=2, window_left=4, window_right=0), 2 * 2 * 2),
     (dict(mask=2, window_left=40, window_right=33), 2 * 2 * 3),           # sides clamp to max_seqlen_k = 20
     (dict(mask=2, window_left=600, window_right=400, batch=5, total_q=3000, total_k=3000, max_seqlen_q=900,
-          max_seqlen_k=900), 2 * ((3000 + 31 * 5) // 32) * 32),           # 19 + 13 + 1 >= 32 groups: absolute
+          max_seqlen_k=900), 2 * 98 * 29),                                # 19 + 13 + 1 >= 32 groups: packed nR nG
     (dict(mask=2, window_left=300, window_right=0, batch=5, total_q=3000, total_k=3000, max_seqlen_q=900,
           max_seqlen_k=900), 2 * ((3000 + 31 * 5) // 32) * (10 + 0 + 1)),
-    (dict(mask=3, func_n=1, func_ld=32, func=FAKE), 0),                   # arbitrary mask: recompute only
+    (dict(mask=3, func_n=1, func_ld=32, func=FAKE), 2 * 2),              # arbitrary mask: packed nR nG
     (dict(total_k=0, max_seqlen_q=0, max_seqlen_k=0, scaling_seqlen=8), 0),  # no keys
 ])
 def test_backward_workspace_query(lib, over, blocks):
@@ -197,10 +201,12 @@ def test_backward_workspace_rejections(lib):
         hstu.HSTU_ERR_INVALID_ARGUMENT
     assert lib.hstu_bwd_dq_ds(ctypes.byref(a), FAKE, FAKE, FAKE, ws + 128, size, FAKE, None) == \
         hstu.HSTU_ERR_INVALID_ARGUMENT
-    # stored dS exists for the full, causal and window masks
+    # the arbitrary mask's workspace is checked like the others'
     f = good_args(mask=3, func_n=1, func_ld=32, func=FAKE)
-    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(f), *dkdv, ws, size, None) == hstu.HSTU_ERR_UNSUPPORTED
-    assert lib.hstu_bwd_dq_ds(ctypes.byref(f), FAKE, FAKE, FAKE, ws, size, FAKE, None) == hstu.HSTU_ERR_UNSUPPORTED
+    fsize = ws_size(lib, f)[1]
+    assert lib.hstu_bwd_dkdv_ds(ctypes.byref(f), *dkdv, ws, fsize - 2048, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_dq_ds(ctypes.byref(f), FAKE, FAKE, FAKE, None, fsize, FAKE, None) == \
+        hstu.HSTU_ERR_INVALID_ARGUMENT
 
 
 def test_binding_rejects_host_tensors():

@@ -61,19 +61,25 @@ def test_source_digest_ignores_comments():
     assert bench._code_only(code) != bench._code_only("int f(int x) { return x + 2; }")
 
 
-def test_clock_summary_per_xcd():
-    """Two sample launches 1 ms apart in real time (100 MHz ticks), XCD 0 advancing
-    1.8e6 cycles and XCD 1 2.0e6: 1800 and 2000 MHz, mean 1900."""
+def test_clock_summary_pairs_readings_by_cu():
+    """Two launches 1 ms apart (100 MHz real-time ticks); every CU's cycle counter has
+    its own offset; the CUs of XCD 0 advance 1.8e6 cycles, those of XCD 1 2.0e6, and
+    one CU of XCD 1 appears only in the first launch."""
     before, after = [], []
     for w in range(16):
-        x = w % 2
-        before.append([1000 + w, 5_000_000 * (x + 1) + 7 * w, x, 0])
-        after.append([101_000 + w, 5_000_000 * (x + 1) + 7 * w + (1_800_000 if x == 0 else 2_000_000), x, 0])
+        x, cu = w % 2, w // 2
+        hwid = cu << 8
+        off = 10_000_000 * (w + 1)  # per-CU counter offset
+        before.append([1000 + w, off, x, hwid])
+        if w != 15:
+            after.append([101_000 + w, off + (1_800_000 if x == 0 else 2_000_000), x, hwid])
+    before.append([1003, 10_000_000 + 50, 0, 0])  # a second workgroup on CU 0 of XCD 0
     c = bench.clock_summary(np.array(before), np.array(after))
     assert c["per_xcd_mhz"] == {"0": 1800.0, "1": 2000.0}
     assert c["shader_mhz"] == 1900.0
+    assert c["cus_paired"] == 15
     assert c["region_us_by_realtime"] == 1000.0
-    assert c["counter_spread_cycles"] == 7 * 14
+    assert c["counter_spread_cycles"] == 50
 
 
 def test_cpu_model_is_named():

@@ -39,10 +39,10 @@ def run_fwd_check(wl, rows=None, tag=""):
 
 
 def run_bwd_check(wl, rows_q=None, rows_k=None, tag=""):
-    """Both backward routes against one oracle evaluation: dQ from stored dS (no
-    mask, causal, window) and dQ from recomputed scores."""
+    """Both backward routes against one oracle evaluation: dQ from stored dS and dQ
+    from recomputed scores."""
     dw = DeviceWorkload(wl)
-    routes = [True, False] if wl.func is None else [False]
+    routes = [True, False]
     rq, rk, rv = oracle.bwd_workload(wl, rows_q, rows_k)
     res = []
     for store in routes:
@@ -300,15 +300,17 @@ def test_func_spelling_causal_and_window_is_bitwise_those_masks():
     causal_f = torch.from_numpy((i + 1)[None, :].astype(np.int32)).cuda()
     left, right = 70, 0
     win_f = torch.from_numpy(np.stack([np.zeros_like(i), i - left, i + right + 1]).astype(np.int32)).cuda()
-    say("func spelling causal / window (70, 0) vs those kernels")
-    # the arbitrary mask always recomputes dQ: compare with causal's recompute route
-    oc, gc = dw.fwd(causal=True), dw.bwd(causal=True, store_ds=False)
-    of, gf = dw.fwd(func=causal_f), dw.bwd(func=causal_f)
-    ow, gw = dw.fwd(window_size=(left, right)), dw.bwd(window_size=(left, right), store_ds=False)
-    ofw, gfw = dw.fwd(func=win_f), dw.bwd(func=win_f)
-    torch.cuda.synchronize()
-    assert torch.equal(oc, of) and all(torch.equal(a, b) for a, b in zip(gc, gf))
-    assert torch.equal(ow, ofw) and all(torch.equal(a, b) for a, b in zip(gw, gfw))
+    say("func spelling causal / window (70, 0) vs those kernels, both backward routes")
+    for store in (False, True):
+        # stored dS: the row blocks' key-group ranges from the endpoints are the causal and
+        # window kernels' ranges, so dQ reads the same blocks in the same order
+        oc, gc = dw.fwd(causal=True), dw.bwd(causal=True, store_ds=store)
+        of, gf = dw.fwd(func=causal_f), dw.bwd(func=causal_f, store_ds=store)
+        ow, gw = dw.fwd(window_size=(left, right)), dw.bwd(window_size=(left, right), store_ds=store)
+        ofw, gfw = dw.fwd(func=win_f), dw.bwd(func=win_f, store_ds=store)
+        torch.cuda.synchronize()
+        assert torch.equal(oc, of) and all(torch.equal(a, b) for a, b in zip(gc, gf)), store
+        assert torch.equal(ow, ofw) and all(torch.equal(a, b) for a, b in zip(gw, gfw)), store
 
 
 def test_func_invalid_arguments_raise():
