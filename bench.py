@@ -42,10 +42,10 @@ DEFAULT_WORKLOAD = "zipf_b32_h4_d128_causal_fwdbwd"
 # forward: S (2) + A.V (2); dq kernel: S (2) + dO.V^T (2) + dS.K (2);
 # dk/dv kernel: S (2) + dO.V^T (2) + A^T.dO (2) + dS^T.Q (2) (also when it stores
 # dS); dq from stored dS: dS.K (2).
-FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8, "bwd_dkdv_ds": 8, "bwd_dq_ds": 2}
+FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8, "bwd_dkdv_ds": 8, "bwd_dq_ds": 2, "bwd_fused": 10}
 USEFUL_PER_PAIR_D = {"fwd": 4, "bwd": 10}
 KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
-                 "bwd_dkdv_ds": "bwd_dkdv_kernel", "bwd_dq_ds": "bwd_dq_ds_kernel"}
+                 "bwd_dkdv_ds": "bwd_dkdv_kernel", "bwd_dq_ds": "bwd_dq_ds_kernel", "bwd_fused": "bwd_dkdv_kernel"}
 
 
 def dq_ds_bytes(wl, pairs: int) -> int:
@@ -534,6 +534,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="time the backward route without stored dS (hstu_bwd_dq + hstu_bwd_dkdv)")
+    ap.add_argument("--fused-bwd", action="store_true",
+                    help="time the fused single-pass backward with fp32-atomic dQ (hstu_bwd_fused: clear, "
+                         "pass, convert, timed together)")
     ap.add_argument("--cpu-max-pairs", type=int, default=0,
                     help="bound on the oracle sample in visible pairs per head (0: the whole workload, "
                          "about 15 s on 16 host threads for the default workload)")
@@ -601,11 +604,15 @@ def main(argv=None) -> int:
               func=torch.from_numpy(wl.func).to(dev) if wl.func is not None else None)
     stream = torch.cuda.current_stream(dev)
     ws_bytes = hstu.hstu_bwd_workspace_size(do, q, k, v, cu_q, cu_k, **kw) if has_bwd else 0
-    stored = has_bwd and ws_bytes > 0 and not args.recompute_dq
+    fused = has_bwd and args.fused_bwd
+    stored = has_bwd and ws_bytes > 0 and not args.recompute_dq and not fused
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if stored else None
     if stored:
         print(f"[bench] backward through stored dS: workspace {ws_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
-    kernels = ["fwd"] + ((["bwd_dkdv_ds", "bwd_dq_ds"] if stored else ["bwd_dq", "bwd_dkdv"]) if has_bwd else [])
+    kernels = ["fwd"] + ((["bwd_fused"] if fused else ["bwd_dkdv_ds", "bwd_dq_ds"] if stored else ["bwd_dq", "bwd_dkdv"])
+                         if has_bwd else [])
+    fws = (torch.empty(wl.total_q * wl.num_heads * wl.head_dim * 4 + 256, dtype=torch.uint8, device=dev)
+           if fused else None)
 
     def step(events=None):
         if events is not None:
@@ -613,7 +620,11 @@ def main(argv=None) -> int:
         hstu.hstu_fwd(q, k, v, cu_q, cu_k, out=o, stream=stream, **kw)
         if events is not None:
             events[1].record(stream)
-        if stored:
+        if fused:
+            hstu.hstu_bwd_fused(do, q, k, v, cu_q, cu_k, dq=dq, dk=dk, dv=dv, workspace=fws, stream=stream, **kw)
+            if events is not None:
+                events[2].record(stream)
+        elif stored:
             hstu.hstu_bwd_dkdv_ds(do, q, k, v, cu_q, cu_k, ds=ws, dk=dk, dv=dv, stream=stream, **kw)
             if events is not None:
                 events[2].record(stream)
@@ -695,7 +706,8 @@ def main(argv=None) -> int:
                    "heads": wl.num_heads, "head_dim": wl.head_dim, "mask": wl.mask_name,
                    "max_seqlen": wl.max_seqlen_q, "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful, "parallelism": "single GPU",
-                   "backward": "stored dS" if stored else "recompute" if has_bwd else None,
+                   "backward": "fused (fp32 atomic dQ)" if fused else "stored dS" if stored else
+                               "recompute" if has_bwd else None,
                    "workspace_bytes": ws_bytes if stored else 0},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_useful_tflops": round(fwd_useful_tf, 2),

@@ -391,6 +391,57 @@ hstu_status_t hstu_bwd_workspace_size(const hstu_args_t* a, size_t* bytes) {
     return ok();
 }
 
+// Bytes of the fused backward's fp32 dQ accumulator: T_q H D floats, whole 256-byte units.
+size_t fused_bytes(const hstu_args_t& a) {
+    const size_t n = (size_t)a.total_q * (size_t)a.num_heads * (size_t)a.head_dim * sizeof(float);
+    return (n + 255) / 256 * 256;
+}
+
+hstu_status_t hstu_bwd_fused_workspace_size(const hstu_args_t* a, size_t* bytes) {
+    if (a == nullptr || bytes == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "args or bytes is null");
+    hstu::AttnParams p;
+    const int32_t zero[1] = {0};
+    hstu_status_t st = check_common(a, zero, zero, p);  // scalar checks only
+    if (st != HSTU_OK) return st;
+    *bytes = fused_bytes(*a);
+    return ok();
+}
+
+hstu_status_t hstu_bwd_fused(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    hstu::AttnParams p;
+    hstu_status_t st = check_common(a, cu_seqlens_q, cu_seqlens_k, p);
+    if (st != HSTU_OK) return st;
+    const size_t need = fused_bytes(*a);
+    if (workspace_bytes < need)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (need > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is null or not 256-byte aligned");
+    Operand ops[] = {{"dout", dout, a->dout, a->total_q}, {"q", q, a->q, a->total_q},
+                     {"k", k, a->k, a->total_k},          {"v", v, a->v, a->total_k},
+                     {"dq", dq, a->dq, a->total_q},       {"dk", dk, a->dk, a->total_k},
+                     {"dv", dv, a->dv, a->total_k}};
+    for (Operand& o : ops)
+        if ((st = check_operand(*a, o)) != HSTU_OK) return st;
+    if (a->total_k > 0 && dk == dv) return fail(HSTU_ERR_INVALID_ARGUMENT, "dk and dv are the same buffer");
+    p.dout = ref(ops[0]);
+    p.q = ref(ops[1]);
+    p.k = ref(ops[2]);
+    p.v = ref(ops[3]);
+    p.dq = out(ops[4]);
+    p.dk = out(ops[5]);
+    p.dv = out(ops[6]);
+    if ((st = set_grid(p, a->max_seqlen_k, hstu::kBwdBlockN, a->max_seqlen_q, a->total_k)) != HSTU_OK) return st;
+    if (a->total_q == 0 && a->total_k == 0) return ok();
+    p.dq_acc = static_cast<float*>(workspace);
+    const int64_t nacc = (int64_t)a->total_q * a->num_heads * a->head_dim;
+    hipError_t e = hstu::launch_fill_zero(p.dq_acc, nacc, stream);
+    if (e == hipSuccess && a->total_k > 0) e = hstu::launch_bwd_dkdv(p, a->head_dim, mask_kind(*a), stream);
+    if (e == hipSuccess) e = hstu::launch_dq_convert(p, a->head_dim, a->total_q, stream);
+    return launched(e, "hstu_bwd_fused");
+}
+
 hstu_status_t hstu_bwd(const hstu_args_t* a, const void* dout, const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -60,6 +60,8 @@
 // same transposing read it uses for K.  dK and dV are those of the recompute
 // route bit for bit; dQ differs only in rounding (its dS comes from the scores
 // as the dk/dv kernel forms them).
+#include <algorithm>
+
 #include "hstu_kernels.h"
 
 namespace hstu {
@@ -356,12 +358,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
 struct DsOut {
     uint16_t* p;
     bool on, kcut, kdead;
+    uint32_t lds;  // fused backward: the block's LDS byte address instead of p
 };
 
 // Query row held at position c (0..31) of a stored dS key row, and the reverse:
 // the dk/dv lane (key, g) stores its operand half h (rows 16 h + 8 (t / 4) +
 // 4 g + t % 4, t = 0..7) at positions 16 h + 8 g + t, i.e. bits 2 and 3 trade places.
 __device__ __forceinline__ int ds_pos_row(int c) { return (c & 0x13) | ((c & 4) << 1) | ((c & 8) >> 1); }
+
+// Byte offsets of the transposing reads of lane `lane` in a stored block: keys
+// 4 g .. 4 g + 3 (.x) and 8 + 4 g .. (.y) at position l32, i.e. the dS^T operand
+// half 0 of query row ds_pos_row(l32); half 1 is 16 keys (1 KB) further.
+__device__ __forceinline__ uint2 ds_tr_offsets(int lane) {
+    const int grp = lane >> 4, j = lane & 15;
+    const int r = 4 * (grp >> 1) + (j >> 2);
+    const int c = 16 * (grp & 1) + 4 * (j & 3);
+    return make_uint2((uint32_t)(r * 64 + 2 * c), (uint32_t)((r + 8) * 64 + 2 * c));
+}
+
 
 // One 32-row block for one wave: S = Q K^T and dA = dO V^T (A operands: Q, dO
 // rows of the block; B operands: the wave's K, V rows), then dV^T += dO^T A' and
@@ -370,7 +384,7 @@ __device__ __forceinline__ int ds_pos_row(int c) { return (c & 0x13) | ((c & 4) 
 // tests row 8 k + 4 g + j of the block (accumulator register 4 k + j) against
 // bit l32 of the LDS word at mw + 32 k + 4 j.  The bf16 dS goes to `ds` as it is
 // formed (the operand of dK^T itself is left as computed).
-template <int D, int MT, int PF = 6>
+template <int D, int MT, bool TO_LDS = false, int PF = 6>
 __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t drow, uint32_t krow, uint32_t vrow, uint32_t qtr,
                                             uint32_t dtr, f32x16 (&dvacc)[(D < 32 ? 32 : D) / 32],
                                             f32x16 (&dkacc)[(D < 32 ? 32 : D) / 32], const uint32_t (&roff)[D / 16],
@@ -449,15 +463,23 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
         // by the dq kernel, and must not push the Q and dO rows that the other key
         // blocks re-read out of the caches
         const int l = threadIdx.x & 63;
-        uint16_t* dst = ds.p + (l & 31) * kDsRowElems + 8 * (l >> 5);
-        if (ds.kcut && ds.kdead) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst));
-            __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst + 16));
+        if constexpr (TO_LDS) {
+            // the fused backward keeps the block in LDS for the tile's dQ products
+            const uint32_t dst = ds.lds + 64u * (uint32_t)(l & 31) + 16u * (uint32_t)(l >> 5);
+            const bool dead = ds.kcut && ds.kdead;
+            ds_write16(dst, dead ? make_uint4(0, 0, 0, 0) : d[0]);
+            ds_write16(dst + 32u, dead ? make_uint4(0, 0, 0, 0) : d[1]);
         } else {
-            const u32x4 v0 = {d[0].x, d[0].y, d[0].z, d[0].w}, v1 = {d[1].x, d[1].y, d[1].z, d[1].w};
-            __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dst));
-            __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dst + 16));
+            uint16_t* dst = ds.p + (l & 31) * kDsRowElems + 8 * (l >> 5);
+            if (ds.kcut && ds.kdead) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst));
+                __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst + 16));
+            } else {
+                const u32x4 v0 = {d[0].x, d[0].y, d[0].z, d[0].w}, v1 = {d[1].x, d[1].y, d[1].z, d[1].w};
+                __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dst));
+                __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dst + 16));
+            }
         }
     }
 #pragma unroll
@@ -469,8 +491,15 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
     }
 }
 
-template <int D, MaskKind MK, bool DS>
+// Modes of the dk/dv kernel: recompute only; also store dS for the dq-from-dS
+// kernel; or the fused backward, which also adds each query tile's dQ into an fp32
+// accumulator with atomics (no dq kernel; dQ's summation order is not fixed).
+enum DkdvMode : int { kDkdvPlain = 0, kDkdvStoreDs = 1, kDkdvFusedDq = 2 };
+
+template <int D, MaskKind MK, int MODE>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
+    constexpr bool DS = MODE == kDkdvStoreDs;
+    constexpr bool FQ = MODE == kDkdvFusedDq;
     constexpr bool CAUSAL = MK == MaskKind::Causal;
     constexpr bool WINDOW = MK == MaskKind::Window;
     constexpr bool FUNC = MK == MaskKind::Func;
@@ -484,6 +513,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
     // (bit k of word w, row r: key n0 + 32 w + k visible to row r of the tile)
     __shared__ __attribute__((aligned(16))) uint32_t fmask[FUNC ? 2 * 256 : 4];
     __shared__ int q_red[FUNC ? 16 : 1];
+    // fused backward: the tile's eight 32 x 32 dS blocks ([row half][key sub-block], in
+    // the stored-dS block layout) and whether each was computed this step
+    __shared__ __attribute__((aligned(16))) uint16_t fq_ds[FQ ? 8 * kDsBlockElems : 8];
+    __shared__ int fq_on[FQ ? 8 : 1];
     const uint32_t lds0 = lds_addr(smem);
     constexpr uint32_t Q0 = 0, Q1 = kTileBytes, D0 = 2 * kTileBytes, D1 = 3 * kTileBytes;
     constexpr uint32_t KB = 4 * kTileBytes, VB = 6 * kTileBytes;
@@ -652,6 +685,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
             }
             const int row0 = qt0 + 32 * qh;
             const uint32_t qr = qc + 8192u * qh, dr = dc + 8192u * qh;
+            bool computed = false;  // fused backward: this wave's dS block holds data this step
+            auto fq_target = [&](DsOut& ds) {
+                ds.on = true;
+                ds.lds = lds_addr(fq_ds) + (uint32_t)(qh * 4 + kw) * (2u * kDsBlockElems);
+                ds.kcut = key0 + 32 > sb.lk;
+                ds.kdead = my_key >= sb.lk;
+            };
             if constexpr (FUNC) {
                 // the live rows of the block and the wave's live keys decide between
                 // skipping it, the unmasked code and the bit-masked code
@@ -666,23 +706,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                     if (seen != 0) {
                         // stored dS: the block is written exactly when it holds a visible pair,
                         // the test the dq kernel repeats before reading it
-                        DsOut ds{nullptr, false, false, false};
+                        DsOut ds{nullptr, false, false, false, 0};
                         if constexpr (DS) {
                             ds.on = true;
                             ds.p = ds_base + (ds_rows_before(row0 >> 5, ds_ng, false) + (key0 >> 5)) * kDsBlockElems;
                             ds.kcut = key0 + 32 > sb.lk;
                             ds.kdead = my_key >= sb.lk;
                         }
-                        dkdv_block<D, kBits>(cut != 0 || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
-                                             roff, toff, row0, 0, 0, g, lds_addr(fmask) + 4u * (wbase + 4 * g), ds,
-                                             p.exp_c, p.alpha);
+                        if constexpr (FQ) fq_target(ds);
+                        computed = true;
+                        dkdv_block<D, kBits, FQ>(cut != 0 || row0 + 32 > sb.lq, qr, dr, krow, vrow, qr, dr, dvacc,
+                                                 dkacc, roff, toff, row0, 0, 0, g,
+                                                 lds_addr(fmask) + 4u * (wbase + 4 * g), ds, p.exp_c, p.alpha);
                     }
                 }
             } else {
                 // waves whose keys no row of the block sees, or that lie past the sequence, skip it
                 const bool run = WINDOW ? row0 + 32 > any_lo && row0 < any_hi : !(CAUSAL && row0 + 31 < key0);
                 if (wave_live && run && row0 < sb.lq) {
-                    DsOut ds{nullptr, false, false, false};
+                    DsOut ds{nullptr, false, false, false, 0};
+                    if constexpr (FQ) fq_target(ds);
+                    computed = true;
                     if constexpr (DS) {
                         ds.on = true;
                         const int rb = row0 >> 5;
@@ -693,8 +737,62 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                         ds.kdead = my_key >= sb.lk;
                     }
                     // rows outside those that see every key of the wave, or past the sequence, need the mask
-                    dkdv_block<D, kInterval>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc, dkacc,
-                                             roff, toff, row0, lo, hi, g, 0, ds, p.exp_c, p.alpha);
+                    dkdv_block<D, kInterval, FQ>(row0 < wlo || row0 + 32 > whi, qr, dr, krow, vrow, qr, dr, dvacc,
+                                                 dkacc, roff, toff, row0, lo, hi, g, 0, ds, p.exp_c, p.alpha);
+                }
+            }
+            if constexpr (FQ) {
+                // dQ of the tile's rows from its dS blocks and the block's K:
+                // dQ^T (32 columns x 32 rows) = K^T dS^T over the block's 128 keys; wave w
+                // takes column block w % 4 and row half w / 4, and adds its piece to the
+                // fp32 accumulator with atomics (the other key blocks add theirs).
+                if (lane == 0) fq_on[qh * 4 + kw] = computed ? 1 : 0;
+                __syncthreads();
+                const int cb = wave & 3, hq = wave >> 2, rq0 = qt0 + 32 * hq;
+                if (32 * cb < DM && rq0 < sb.lq) {
+                    const uint2 ko = tr_offsets(32 * cb, lane);
+                    const uint2 dtr = ds_tr_offsets(lane);
+                    const uint32_t blk0 = lds_addr(fq_ds) + (uint32_t)(hq * 4) * (2u * kDsBlockElems);
+                    f32x16 qa = f32x16{};
+                    bool any = false;
+#pragma unroll
+                    for (int s8 = 0; s8 < 8; ++s8) {
+                        if (!fq_on[hq * 4 + (s8 >> 1)]) continue;
+                        any = true;
+                        const uint32_t kaddr = lds0 + KB + 4096u * (uint32_t)s8;
+                        const uint32_t daddr = blk0 + (uint32_t)(s8 >> 1) * (2u * kDsBlockElems) +
+                                               1024u * (uint32_t)(s8 & 1);
+                        qa = mfma32x32x16(ds_read_tr16x2(kaddr + ko.x, kaddr + ko.y),
+                                          ds_read_tr16x2(daddr + dtr.x, daddr + dtr.y), qa);
+                    }
+                    if (any) {
+                        // Through LDS (this tile's Q or dO slot, free once every wave has run its
+                        // block) into row-major order, so that each atomic instruction covers two
+                        // 128-byte row segments instead of 32 rows: lane (l32, g) holds row
+                        // ds_pos_row(l32), columns acc_row(r, g); column d of row i sits at
+                        // i * 32 + (d ^ ((i >> 1) & 15)) (no bank conflicts either way).
+                        const uint32_t tb = lds0 + (qh == 0 ? qc : dc) + 4096u * (uint32_t)kw;
+                        // the lane index, opaque to the compiler here, so that the addresses
+                        // below are formed in place rather than kept live across the walk
+                        int ln = lane;
+                        __asm__ volatile("" : "+v"(ln));
+                        const int wr = ds_pos_row(ln & 31), gl = ln >> 5;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int d = acc_row(r, gl);
+                            *(__attribute__((address_space(3))) float*)(uintptr_t)(
+                                tb + 4u * (uint32_t)(wr * 32 + (d ^ ((wr >> 1) & 15)))) = qa[r];
+                        }
+                        const int d = ln & 31;
+                        float* dst = p.dq_acc + ((int64_t)sb.q0 * p.heads + h) * D + 32 * cb + d;
+#pragma unroll
+                        for (int k2 = 0; k2 < 16; ++k2) {
+                            const int i = 2 * k2 + gl;
+                            const float x = *(__attribute__((address_space(3))) float*)(uintptr_t)(
+                                tb + 4u * (uint32_t)(i * 32 + (d ^ ((i >> 1) & 15))));
+                            if (rq0 + i < sb.lq && 32 * cb + d < D) atomicAdd(dst + (int64_t)(rq0 + i) * p.heads * D, x);
+                        }
+                    }
                 }
             }
             wait_global_loads();
@@ -800,16 +898,6 @@ __device__ __forceinline__ void dq_ds_tile(uint32_t kt, const uint4 (&dsop)[4],
 // One dS slot of a wave: its two key groups' 32 x 32 blocks as stored, 2 KB each
 // (64 bytes per key).
 constexpr uint32_t kDsSlotBytes = 2 * 2 * kDsBlockElems;
-// Byte offsets of the transposing reads of lane `lane` in a stored block: keys
-// 4 g .. 4 g + 3 (.x) and 8 + 4 g .. (.y) at position l32, i.e. the dS^T operand
-// half 0 of query row ds_pos_row(l32); half 1 is 16 keys (1 KB) further.
-__device__ __forceinline__ uint2 ds_tr_offsets(int lane) {
-    const int grp = lane >> 4, j = lane & 15;
-    const int r = 4 * (grp >> 1) + (j >> 2);
-    const int c = 16 * (grp & 1) + 4 * (j & 3);
-    return make_uint2((uint32_t)(r * 64 + 2 * c), (uint32_t)((r + 8) * 64 + 2 * c));
-}
-
 constexpr int BMD = kDqDsBlockM;  // dq-from-dS kernel: query rows per workgroup (32 per wave)
 constexpr int NWD = BMD / 32;     // its waves
 
@@ -1056,10 +1144,12 @@ template <int D, MaskKind MK>
 hipError_t launch_dkdv(const AttnParams& p, hipStream_t stream) {
     const int64_t grid = (int64_t)p.items * p.heads;
     if (grid == 0) return hipSuccess;
-    if (p.ds != nullptr)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    if (p.dq_acc != nullptr)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, kDkdvFusedDq>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else if (p.ds != nullptr)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, kDkdvStoreDs>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MK, kDkdvPlain>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1097,6 +1187,42 @@ hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipSt
 
 hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
     return launch_dir<true>(p, head_dim, mask, stream);
+}
+
+// The fused backward's fp32 dQ accumulator: cleared before the dk/dv kernel adds
+// into it (a kernel rather than a memset, so the call stays graph-capturable), then
+// dQ = (alpha / L_scale) acc rounded to bf16.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* p, int64_t n4) {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) p[i] = make_float4(0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, TensorOut dq, int64_t rows, int heads,
+                                                         int dim, float scale) {
+    const int per_row = heads * dim / 4;  // float4 per token
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < rows * per_row; i += (int64_t)gridDim.x * 256) {
+        const int64_t t = i / per_row;
+        const int c = (int)(i % per_row) * 4, hh = c / dim, d = c % dim;
+        const float4 v = reinterpret_cast<const float4*>(acc)[i];
+        *reinterpret_cast<uint2*>(dq.base + t * dq.tok + hh * dq.head + d) =
+            make_uint2(pack_bf16x2(v.x * scale, v.y * scale), pack_bf16x2(v.z * scale, v.w * scale));
+    }
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+    const int64_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<float4*>(p), n4);
+    return hipGetLastError();
+}
+
+hipError_t launch_dq_convert(const AttnParams& p, int head_dim, int64_t rows, hipStream_t stream) {
+    const int64_t n4 = rows * p.heads * head_dim / 4;
+    if (n4 == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(dq_convert_kernel, dim3(grid), dim3(256), 0, stream, p.dq_acc, p.dq, rows, p.heads, head_dim,
+                       p.out_scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_ds(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {

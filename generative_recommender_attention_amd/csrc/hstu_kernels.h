@@ -55,6 +55,9 @@ struct AttnParams {
     int32_t ds_rel;        // ceil(left / 32) for a window stored relative to R, else -1
     int32_t ds_tri;        // 1: causal packing (row block R keeps groups 0..R)
     int32_t ds_kgr;        // key groups the dk/dv grid covers: 4 ceil(max_seqlen_k / 128)
+    // Fused backward: fp32 (T_q, H, D) packed dQ accumulator the dk/dv kernel adds
+    // each query tile's dQ into with atomics (null: not fused).
+    float* dq_acc;
 };
 
 // Elements of one stored dS block (32 x 32 bf16, 2 KB) and of one of its rows.
@@ -83,6 +86,10 @@ hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipSt
 hipError_t launch_bwd_dkdv(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
 // dQ from the dS the dk/dv kernel stored (p.ds); mask None, Causal or Window.
 hipError_t launch_bwd_dq_ds(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream);
+// Fused backward: clear n floats (n % 4 == 0, 16-byte aligned); dq = bf16(acc * out_scale)
+// for the first `rows` tokens of p.dq_acc (packed (T, H, D) fp32).
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_dq_convert(const AttnParams& p, int head_dim, int64_t rows, hipStream_t stream);
 // `count` one-wave workgroups, each writing {realtime, shader cycles, XCC id, HW_ID}.
 hipError_t launch_clock_sample(uint64_t* out, int count, hipStream_t stream);
 

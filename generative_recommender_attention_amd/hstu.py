@@ -37,6 +37,7 @@ __all__ = [
     "hstu_bwd_dkdv",
     "hstu_bwd_dkdv_ds",
     "hstu_bwd_dq_ds",
+    "hstu_bwd_fused",
     "HSTU_OK",
     "HSTU_ERR_INVALID_ARGUMENT",
     "HSTU_ERR_UNSUPPORTED",
@@ -162,6 +163,10 @@ def library() -> ctypes.CDLL:
             lib.hstu_bwd_dkdv.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_bwd_dkdv_ds.restype = ctypes.c_int
             lib.hstu_bwd_dkdv_ds.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            lib.hstu_bwd_fused_workspace_size.restype = ctypes.c_int
+            lib.hstu_bwd_fused_workspace_size.argtypes = [argp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.hstu_bwd_fused.restype = ctypes.c_int
+            lib.hstu_bwd_fused.argtypes = [argp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
             lib.hstu_bwd_dq_ds.restype = ctypes.c_int
             lib.hstu_bwd_dq_ds.argtypes = [argp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
             largp = ctypes.POINTER(HstuLmsdArgs)
@@ -354,6 +359,39 @@ def hstu_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
         _check(library().hstu_bwd(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
                                   _stream(s)))
+    return dq, dk, dv
+
+
+def hstu_bwd_fused(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                   max_seqlen_q: int, max_seqlen_k: int, alpha: float = 1.0,
+                   scaling_seqlen: Optional[int] = None, causal: bool = True,
+                   dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                   dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                   window_size: Optional[Tuple[int, int]] = None, func: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(dq, dk, dv) through the fused single-pass backward (dQ added with fp32 atomics
+    into ``workspace``, a device byte tensor of at least T_q H D 4 bytes, allocated here
+    when not given); dQ's last bits may differ between calls."""
+    H, D, pq, pk, a = _bwd_common(dout, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, alpha, scaling_seqlen, causal, window_size, func)
+    s = _launch_stream(stream, q.device)
+    with torch.cuda.stream(s):
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+        _thd("dq", dq, int(q.shape[0]), H, D)
+        _thd("dk", dk, int(k.shape[0]), H, D)
+        _thd("dv", dv, int(k.shape[0]), H, D)
+        a.dq, a.dk, a.dv = _stride(dq), _stride(dk), _stride(dv)
+        need = ctypes.c_size_t(0)
+        _check(library().hstu_bwd_fused_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        if workspace is None and need.value > 0:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _workspace(workspace)
+        _check(library().hstu_bwd_fused(ctypes.byref(a), dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        pq, pk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
+                                        _stream(s)))
     return dq, dk, dv
 
 

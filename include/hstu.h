@@ -238,6 +238,25 @@ HSTU_API hstu_status_t hstu_bwd_dq_ds(const hstu_args_t* args, const void* k,
                              const void* ds, size_t ds_bytes, void* dq,
                              hipStream_t stream);
 
+/* The page's fused backward for D <= 128 ("Current limitations": its backward is
+ * not deterministic; Block Sparse Attention page, "Current support", backward:
+ * one pass over query x key tiles running all five products, fp32 atomics).  One
+ * key-major pass computes dK and dV as hstu_bwd_dkdv does (bit-identical) and,
+ * per 64-row query tile, that tile's dQ from its dS and the block's K, added
+ * into an fp32 accumulator with atomics; a last kernel writes dq = alpha /
+ * L_scale times the sum in bf16.  Three kernels on `stream`: clear the
+ * accumulator, the pass, the conversion.  The workspace (caller-owned device
+ * memory, 256-byte aligned, hstu_bwd_fused_workspace_size() bytes = T_q H D
+ * floats rounded up to 256 bytes, contents on entry ignored) holds the
+ * accumulator.  dQ's summation order follows the atomics', so repeated calls
+ * may differ in the last bits.  Any mask. */
+HSTU_API hstu_status_t hstu_bwd_fused_workspace_size(const hstu_args_t* args, size_t* bytes);
+HSTU_API hstu_status_t hstu_bwd_fused(const hstu_args_t* args, const void* dout,
+                             const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ==========================================================================
  * HSTU LMSD: LayerNorm, affine, times SiLU(u) (HSTU LMSD page, "Overview").
  *

@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dkdv_ds", "hstu_bwd_dq", "hstu_bwd_dq_ds",
-        "hstu_bwd_workspace_size", "hstu_clock_sample", "hstu_fwd",
+        "hstu_bwd_fused", "hstu_bwd_fused_workspace_size", "hstu_bwd_workspace_size", "hstu_clock_sample", "hstu_fwd",
         "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_noalloc", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd",
         "hstu_status_string"])
 
@@ -207,6 +207,26 @@ def test_backward_workspace_rejections(lib):
     assert lib.hstu_bwd_dkdv_ds(ctypes.byref(f), *dkdv, ws, fsize - 2048, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
     assert lib.hstu_bwd_dq_ds(ctypes.byref(f), FAKE, FAKE, FAKE, None, fsize, FAKE, None) == \
         hstu.HSTU_ERR_INVALID_ARGUMENT
+
+
+def test_fused_backward_workspace_and_rejections(lib):
+    a = good_args()  # T_q = 32, H = 2, D = 64: 4096 floats
+    need = ctypes.c_size_t(0)
+    assert lib.hstu_bwd_fused_workspace_size(ctypes.byref(a), ctypes.byref(need)) == hstu.HSTU_OK
+    assert need.value == 32 * 2 * 64 * 4
+    a3 = good_args(total_q=3, total_k=3, max_seqlen_q=3, max_seqlen_k=3, head_dim=16, num_heads=1)
+    assert lib.hstu_bwd_fused_workspace_size(ctypes.byref(a3), ctypes.byref(need)) == hstu.HSTU_OK
+    assert need.value == 256  # 48 floats, rounded up to 256 bytes
+    ws = FAKE + 4096
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, FAKE + 32, FAKE + 48)
+    assert lib.hstu_bwd_fused(ctypes.byref(a), *args, ws, 32 * 2 * 64 * 4 - 4, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_fused(ctypes.byref(a), *args, None, 32 * 2 * 64 * 4, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    assert lib.hstu_bwd_fused(ctypes.byref(a), *args, ws + 64, 32 * 2 * 64 * 4, None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    same = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, FAKE + 32, FAKE + 32)
+    st = lib.hstu_bwd_fused(ctypes.byref(a), *same, ws, 32 * 2 * 64 * 4, None)
+    assert st == hstu.HSTU_ERR_INVALID_ARGUMENT and b"same buffer" in lib.hstu_last_error()
+    assert lib.hstu_bwd_fused(ctypes.byref(good_args(head_dim=24)), *args, ws, 1 << 20, None) == \
+        hstu.HSTU_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

@@ -543,3 +543,55 @@ def test_unsupported_raise():
         hstu.hstu_fwd(q48, q48, q48, dw.cu_q, dw.cu_k, 10, 10)
     with pytest.raises(hstu.HstuError):
         hstu.hstu_fwd(dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, 11, 10)  # max_seqlen_q > max_seqlen_k
+
+
+# ------------------------------------------------------------------ fused backward (fp32 atomic dQ)
+FUSED_CASES = [
+    # (name, seed, lengths_q, lengths_k or None, H, D, mask)
+    ("edge_d16_causal", 300, EDGE_LENGTHS, None, 2, 16, True),
+    ("edge_d32_full", 301, EDGE_LENGTHS, None, 2, 32, False),
+    ("edge_d64_causal", 302, EDGE_LENGTHS, None, 1, 64, True),
+    ("edge_d128_causal", 303, EDGE_LENGTHS, None, 2, 128, True),
+    ("lq_ne_lk_full", 304, [130, 40, 7], [131, 38, 3], 3, 64, False),
+    ("window", 305, [700, 1000, 33], None, 2, 128, (256, 128)),
+    ("func", 306, [300, 5, 0, 257], [310, 9, 4, 257], 2, 128, "func"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_backward(oracle_lib, case):
+    """hstu_bwd_fused: dK and dV bit-identical to hstu_bwd_dkdv's (the same pass), dQ
+    (fp32 atomics, any summation order) within the bar of the oracle's."""
+    name, seed, lq, lk, H, D, mask = case
+    kw = {}
+    if mask == "func":
+        kw["func"] = func_random_mask(np.random.default_rng(seed), lq, lk, 3)
+        causal = False
+    elif isinstance(mask, tuple):
+        kw["window"], causal = mask, False
+    else:
+        causal = mask
+    wl = make_workload(f"fused_{name}", seed, lq, H, D, causal, 1.0, lengths_k=lk, with_do=True, **kw)
+    dw = DeviceWorkload(wl)
+    dkw = dw.kw()
+    ws = torch.full((wl.total_q * H * D * 4 + 256,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN-filled
+    say(f"hstu_bwd_fused {name}: lengths {list(wl.lengths_q)} H={H} D={D} mask={wl.mask_name}")
+    dq, dk, dv = hstu.hstu_bwd_fused(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, workspace=ws, **dkw)
+    dk_r, dv_r = hstu.hstu_bwd_dkdv(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, **dkw)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk_r) and torch.equal(dv, dv_r)
+    rq, rk, rv = oracle.bwd_workload(wl)
+    check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q)
+    check_close("dK", to_f64(dk), rk, wl.cu_seqlens_k)
+
+
+def test_fused_backward_zipf_workload_full(oracle_lib):
+    wl = named_workload("zipf_b32_h4_d128_causal_fwdbwd")
+    dw = DeviceWorkload(wl)
+    say("hstu_bwd_fused on the Zipf workload (every row)")
+    dq, dk, dv = hstu.hstu_bwd_fused(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, **dw.kw())
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.bwd_workload(wl)
+    print("fused zipf dQ (err/max, worst per-seq):", check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q))
+    check_close("dK", to_f64(dk), rk, wl.cu_seqlens_k)
+    check_close("dV", to_f64(dv), rv, wl.cu_seqlens_k)
