@@ -595,3 +595,26 @@ def test_fused_backward_zipf_workload_full(oracle_lib):
     print("fused zipf dQ (err/max, worst per-seq):", check_close("dQ", to_f64(dq), rq, wl.cu_seqlens_q))
     check_close("dK", to_f64(dk), rk, wl.cu_seqlens_k)
     check_close("dV", to_f64(dv), rv, wl.cu_seqlens_k)
+
+
+# ------------------------------------------------------------------ long walks, odd head counts
+SPLIT_CASES = [
+    # (seed, lengths, H, D, causal): blocks walking 33 to 64 key tiles next to short and
+    # empty sequences; odd H so that neighbouring work items differ in head and row block
+    (310, [4100, 100, 2049, 0, 33], 1, 128, True),
+    (311, [2500, 3000], 3, 64, False),
+    (312, [2113, 17, 4000], 2, 32, True),
+    (313, [2200, 900], 1, 16, False),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"seed{c[0]}_h{c[2]}_d{c[3]}_{'causal' if c[4] else 'full'}"
+                                                   for c in SPLIT_CASES])
+def test_split_walks_fwd(oracle_lib, case):
+    seed, lens, H, D, causal = case
+    wl = make_workload(f"split{seed}", seed, lens, H, D, causal, 0.5)
+    run_fwd_check(wl)
+    dw = DeviceWorkload(wl)
+    o1, o2 = dw.fwd(), dw.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)  # each output row is summed in one fixed order
