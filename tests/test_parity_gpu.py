@@ -618,3 +618,31 @@ def test_split_walks_fwd(oracle_lib, case):
     o1, o2 = dw.fwd(), dw.fwd()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)  # each output row is summed in one fixed order
+
+
+# ------------------------------------------------------------------ dQ from stored dS: long walks
+DQ_LONG_CASES = [
+    # (seed, lengths, H, D, causal): 256-row blocks walking 33 to 110 key tiles of stored
+    # dS beside short and empty sequences, odd and even head counts
+    (320, [4100, 100, 2049, 0, 3000], 3, 128, True),
+    (321, [2500, 2113], 2, 64, False),
+    (322, [7000], 8, 32, True),
+    (323, [2200, 17, 2600], 5, 16, True),
+]
+
+
+@pytest.mark.parametrize("case", DQ_LONG_CASES, ids=[f"seed{c[0]}_h{c[2]}_d{c[3]}_{'causal' if c[4] else 'full'}"
+                                                     for c in DQ_LONG_CASES])
+def test_dq_ds_long_walks(oracle_lib, case):
+    seed, lens, H, D, causal = case
+    wl = make_workload(f"dqlong{seed}", seed, lens, H, D, causal, 0.5, with_do=True)
+    run_bwd_check(wl)
+    dw = DeviceWorkload(wl)
+    kw = dw.kw()
+    ws = dw.workspace()
+    hstu.hstu_bwd_dkdv_ds(dw.do, dw.q, dw.k, dw.v, dw.cu_q, dw.cu_k, ds=ws, **kw)
+    dq1 = hstu.hstu_bwd_dq_ds(dw.q, dw.k, dw.cu_q, dw.cu_k, ds=ws, **kw)
+    dq2 = hstu.hstu_bwd_dq_ds(dw.q, dw.k, dw.cu_q, dw.cu_k, ds=ws, **kw)  # again, on the same dS
+    dq3 = dw.bwd()[0]  # a whole backward on a fresh workspace
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2) and torch.equal(dq1, dq3)
