@@ -133,7 +133,7 @@ def load_traffic(kernel: str, workload: str):
 
 PROFILE_COMMANDS = {
     "kt": ("rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py "
-           "--no-cpu-baseline --workload {w} --clock-out {d}/kt/clock.json"),
+           "--no-cpu-baseline --workload {w} --clock-out {d}/kt/clock.json --json-out {d}/kt/bench.json"),
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cfetch -o run -- python3 bench.py --calibrate-copy-mib 256",
@@ -220,6 +220,26 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
         short = next((k for k in kernels if k in name), name.split("(")[0][-26:])
         out.append(f"{short:26s}{int(r['Calls']):8d}{float(r['AverageNs']):11.0f}{float(r['MinNs']):11.0f}"
                    f"{float(r['MaxNs']):11.0f}{float(r['Percentage']):7.1f}%")
+    bpath = os.path.join(prof_dir, "kt", "bench.json")
+    if os.path.exists(bpath):
+        with open(bpath) as f:
+            line = json.loads(f.readline())
+        out += ["", f"The same run's bench line (HIP events on the launch stream, mean over {line['steps']} timed steps "
+                    f"after {line['warmup']} warmup steps; the trace above also counts the warmup launches):",
+                f"  value {line['value']} {line['unit']} ({line.get('frac_of_peak')} of the 2500 TFLOP/s peak), "
+                f"{line['ms_per_step']} ms per step"]
+        for kname, d in line.get("kernels", {}).items():
+            extra = f", {d['alg_gbs']} GB/s of algorithmic bytes" if "alg_gbs" in d else ""
+            out.append(f"  {kname:12s} {d['ms'] * 1e3:8.1f} us  {d['alg_tflops']:7.1f} TFLOP/s "
+                       f"({d['frac_of_peak']:.1%} of peak){extra}")
+        rl = line.get("roofline")
+        if rl:
+            tr = next((float(r["AverageNs"]) for r in stats if rl["kernel"] in r["Name"]), None)
+            out.append(f"  roofline: {rl['kernel']} {rl['achieved']} TFLOP/s = frac {rl['frac']} from the events; "
+                       + (f"{rl['alg_flops_per_launch']} flops / {tr / 1e3:.1f} us (trace average) = "
+                          f"{rl['alg_flops_per_launch'] / (tr * 1e-9) / 1e12:.1f} TFLOP/s = frac "
+                          f"{rl['alg_flops_per_launch'] / (tr * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f} from the trace"
+                          if tr else "(kernel not in the trace)"))
     with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(out) + "\n")
     if os.path.isdir(os.path.join(prof_dir, "mfma")) and not workload.startswith("lmsd_"):
@@ -545,6 +565,7 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC byte-counter calibration)")
     ap.add_argument("--clock-out", metavar="PATH", help="also write the shader-clock reading to PATH (JSON)")
+    ap.add_argument("--json-out", metavar="PATH", help="also write the JSON line to PATH")
     ap.add_argument("--oracle-configs", action="store_true",
                     help="only time the CPU oracle on every workload configuration (median of 3 runs for the "
                          "small ones, one run for the long ones) and write profiles/oracle_cpu_baseline.txt")
@@ -728,6 +749,10 @@ def main(argv=None) -> int:
                                       "at the measured clock the same CUs peak at "
                                       f"{256 * 4096 * (clock['shader_mhz'] or 0) / 1e6:.0f} TFLOP/s"}
     print(json.dumps(result))
+    if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+        with open(args.json_out, "w") as f:
+            f.write(json.dumps(result) + "\n")
     return 0
 
 
