@@ -399,15 +399,24 @@ def time_oracle_configs() -> int:
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    """The host CPU's model name with its family / model / stepping numbers (from the
+    first processor of /proc/cpuinfo; a virtual machine may report a short name), else
+    the machine type."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block ends here
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
     except OSError:
         pass
-    return platform.processor() or platform.machine()
+    name = fields.get("model name")
+    if not name:
+        return platform.processor() or platform.machine()
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{name} ({ids})" if ids else name
 
 
 def clock_summary(before, after) -> dict:
