@@ -1,4 +1,6 @@
-"""Build ``libhstu.so`` for gfx950 with hipcc (ahead of time, in-tree).
+"""Build ``libhstu.so`` for gfx950 with hipcc (ahead of time, in-tree), and its
+debug variant ``libhstu_debug.so`` (-DHSTU_DEBUG: bounds tests on the kernels'
+global indices, read back with hstu_debug_take).
 
 Usage:  python -m generative_recommender_attention_amd.build
 """
@@ -17,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "libhstu")
 LIB_PATH = os.path.join(PKG, "libhstu.so")
+DEBUG_BUILD_DIR = os.path.join(ROOT, "_build", "libhstu_debug")
+DEBUG_LIB_PATH = os.path.join(PKG, "libhstu_debug.so")
 
 SOURCES = ["hstu_api.cpp", "hstu_fwd.hip", "hstu_bwd.hip", "lmsd.hip", "clock.hip"]
 ARCH = "gfx950"
@@ -42,9 +46,11 @@ def compile_flags():
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *compile_flags(), *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    obj = os.path.join(DEBUG_BUILD_DIR if debug else BUILD_DIR, os.path.basename(src) + ".o")
+    extra = ["-DHSTU_DEBUG"] if debug else []
+    cmd = [hipcc(), *compile_flags(), *extra, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass reports the device-only feature flag as unknown; drop that line only.
     noise = "'-packed-fp32-ops' is not a recognized feature"
@@ -56,19 +62,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link ``libhstu.so`` next to this file."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+def _link(objs, path: str) -> None:
+    tmp = path + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = True, debug: bool = True) -> str:
+    """Compile every source and link ``libhstu.so`` next to this file (and, with
+    ``debug``, ``libhstu_debug.so``)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(DEBUG_BUILD_DIR, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if debug else [])
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}", file=sys.stderr)
+    if debug:
+        _link(objs[len(SOURCES):], DEBUG_LIB_PATH)
+        if verbose:
+            print(f"built {DEBUG_LIB_PATH}", file=sys.stderr)
     return LIB_PATH
 
 

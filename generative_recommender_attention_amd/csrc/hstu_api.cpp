@@ -125,6 +125,8 @@ hstu_status_t check_common(const hstu_args_t* a, const int32_t* cu_q, const int3
     p.cu_k = cu_k;
     p.batch = a->batch;
     p.heads = a->num_heads;
+    p.total_q = a->total_q;
+    p.total_k = a->total_k;
     p.alpha = a->alpha;
     p.exp_c = -a->alpha * 1.4426950408889634f;
     p.out_scale = ls >= 1 ? a->alpha / (float)ls : 0.0f;
@@ -651,6 +653,23 @@ hstu_status_t hstu_clock_sample(uint64_t* samples, int32_t count, hipStream_t st
     if (samples == nullptr || reinterpret_cast<uintptr_t>(samples) % 8 != 0)
         return fail(HSTU_ERR_INVALID_ARGUMENT, "samples is null or not 8-byte aligned");
     return launched(hstu::launch_clock_sample(samples, count, stream), "hstu_clock_sample");
+}
+
+hstu_status_t hstu_debug_take(uint32_t* sites) {
+    if (sites == nullptr) return fail(HSTU_ERR_INVALID_ARGUMENT, "sites is null");
+    *sites = 0;
+#ifdef HSTU_DEBUG
+    hipError_t e = hipDeviceSynchronize();
+    uint32_t w[3] = {0, 0, 0};
+    if (e == hipSuccess) e = hstu::debug_take_fwd(&w[0]);
+    if (e == hipSuccess) e = hstu::debug_take_bwd(&w[1]);
+    if (e == hipSuccess) e = hstu::debug_take_lmsd(&w[2]);
+    if (e != hipSuccess) return fail(HSTU_ERR_DEVICE, "hstu_debug_take: %s", hipGetErrorString(e));
+    *sites = w[0] | w[1] | w[2];
+    return ok();
+#else
+    return fail(HSTU_ERR_UNSUPPORTED, "hstu_debug_take: not a debug build (HSTU_DEBUG)");
+#endif
 }
 
 const char* hstu_last_error(void) { return g_last_error.c_str(); }

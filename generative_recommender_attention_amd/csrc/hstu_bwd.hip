@@ -200,6 +200,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
         return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
+    dbg_seq(p, sb, h);
     const int m0 = m * BM;
     if (m0 >= sb.lq) return;
 
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
         int rlo = 0x7fffffff, rhi = 0;
         if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
         const int frow = sb.q0 + min(my_row, sb.lq - 1);
+        HSTU_DCHECK(frow >= 0 && frow < p.func_ld, kDbgFunc);
         f0 = p.func[frow];
         if (p.func_n > 1) {
             f1 = p.func[(int64_t)p.func_ld + frow];
@@ -250,10 +252,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     }
     const int t0 = kv_end > kv_begin ? kv_begin / BN : 0;
     const int t1 = kv_end > kv_begin ? (kv_end + BN - 1) / BN : t0;
+    HSTU_DCHECK(t1 == t0 || (kv_begin >= 0 && kv_end <= sb.lk), kDbgTile);
 
     uint4 qf[KSTEPS], dof[KSTEPS];
     {
         const int r = min(my_row, sb.lq - 1);
+        HSTU_DCHECK(r >= 0 && r < sb.lq, kDbgRow);
         const uint16_t* qsrc = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
         const uint16_t* dsrc = p.dout.base + (int64_t)(sb.q0 + r) * p.dout.tok + (int64_t)h * p.dout.head + 8 * g;
 #pragma unroll
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnParams p) {
     }
 
     if (my_row < sb.lq) {
+        HSTU_DCHECK((int64_t)sb.q0 + my_row < p.total_q, kDbgRow);
         uint16_t* dst = p.dq.base + (int64_t)(sb.q0 + my_row) * p.dq.tok + (int64_t)h * p.dq.head;
         const float sc = p.out_scale;
 #pragma unroll
@@ -536,6 +541,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         return;
     const int b = item.b, n = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
+    dbg_seq(p, sb, h);
     const int n0 = n * BNK;
     if (n0 >= sb.lk) return;
 
@@ -558,6 +564,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         const int r = u >> 4, c = u & 15;
         if (c < D / 8) {
             const int64_t row = sb.k0 + min(n0 + r, sb.lk - 1);
+            HSTU_DCHECK(row >= sb.k0 && row < (int64_t)sb.k0 + sb.lk, kDbgRow);
             const uint4 kv = ld_global16(p.k.base + row * p.k.tok + (int64_t)h * p.k.head + 8 * c);
             const uint4 vv = ld_global16(p.v.base + row * p.v.tok + (int64_t)h * p.v.head + 8 * c);
             ds_write16(lds0 + KB + tile_byte(r, c), kv);
@@ -623,6 +630,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         q_end = qhi >= qlo ? qhi + 1 : 0;
     }
     const int ntiles = q_end > q_begin ? (q_end - q_begin + BMQ - 1) / BMQ : 0;
+    HSTU_DCHECK(ntiles == 0 || (q_begin >= 0 && q_end <= sb.lq), kDbgTile);
     // func: the words of the tile at rows qt0.. (threads 0-255, one word each: row
     // tid % 64, keys n0 + 32 (tid / 64) ..), in two halves: load_ends reads the
     // row's first endpoints, store_word turns them into the word for slot `slot`
@@ -633,6 +641,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         if constexpr (FUNC) {
             const int i = qt0 + wrow;
             if (tid < 256 && i < sb.lq) {
+                HSTU_DCHECK(sb.q0 + i >= 0 && sb.q0 + i < p.func_ld, kDbgFunc);
                 e0 = p.func[sb.q0 + i];
                 if (p.func_n > 1) {
                     e1 = p.func[(int64_t)p.func_ld + sb.q0 + i];
@@ -710,6 +719,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                         if constexpr (DS) {
                             ds.on = true;
                             ds.p = ds_base + (ds_rows_before(row0 >> 5, ds_ng, false) + (key0 >> 5)) * kDsBlockElems;
+                            HSTU_DCHECK(ds.p >= p.ds && ds.p + kDsBlockElems <= p.ds + (int64_t)p.heads * p.ds_head * kDsBlockElems,
+                                        kDbgDs);
                             ds.kcut = key0 + 32 > sb.lk;
                             ds.kdead = my_key >= sb.lk;
                         }
@@ -733,6 +744,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                         const int64_t blk = p.ds_rel >= 0 ? (int64_t)rb * p.ds_kg + (key0 >> 5) - (rb - p.ds_rel)
                                                           : ds_rows_before(rb, ds_ng, p.ds_tri != 0) + (key0 >> 5);
                         ds.p = ds_base + blk * kDsBlockElems;
+                        HSTU_DCHECK(ds.p >= p.ds && ds.p + kDsBlockElems <= p.ds + (int64_t)p.heads * p.ds_head * kDsBlockElems,
+                                    kDbgDs);
                         ds.kcut = key0 + 32 > sb.lk;
                         ds.kdead = my_key >= sb.lk;
                     }
@@ -790,7 +803,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
                             const int i = 2 * k2 + gl;
                             const float x = *(__attribute__((address_space(3))) float*)(uintptr_t)(
                                 tb + 4u * (uint32_t)(i * 32 + (d ^ ((i >> 1) & 15))));
-                            if (rq0 + i < sb.lq && 32 * cb + d < D) atomicAdd(dst + (int64_t)(rq0 + i) * p.heads * D, x);
+                            if (rq0 + i < sb.lq && 32 * cb + d < D) {
+                                HSTU_DCHECK(((int64_t)(sb.q0 + rq0 + i) * p.heads + h) * D + 32 * cb + d <
+                                                (int64_t)p.total_q * p.heads * D,
+                                            kDbgAcc);
+                                atomicAdd(dst + (int64_t)(rq0 + i) * p.heads * D, x);
+                            }
                         }
                     }
                 }
@@ -830,6 +848,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnParams p) {
         }
 
     if (my_key < sb.lk) {
+        HSTU_DCHECK((int64_t)sb.k0 + my_key < p.total_k, kDbgRow);
         uint16_t* dk = p.dk.base + (int64_t)(sb.k0 + my_key) * p.dk.tok + (int64_t)h * p.dk.head;
         uint16_t* dv = p.dv.base + (int64_t)(sb.k0 + my_key) * p.dv.tok + (int64_t)h * p.dv.head;
         const float sc = p.out_scale, scv = p.out_scale;
@@ -926,6 +945,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
         return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
+    dbg_seq(p, sb, h);
     const int m0 = m * BMD;
     if (m0 >= sb.lq) return;
 
@@ -950,6 +970,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
         // and l + 32 hold the same row); inside it, the dk/dv kernel wrote exactly the
         // blocks that hold a visible pair, which the walk tests per tile below
         const int frow = sb.q0 + min(my_row, sb.lq - 1);
+        HSTU_DCHECK(frow >= 0 && frow < p.func_ld, kDbgFunc);
         f0 = p.func[frow];
         if (p.func_n > 1) {
             f1 = p.func[(int64_t)p.func_ld + frow];
@@ -999,6 +1020,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
                (p.ds_rel >= 0 ? (int64_t)rb * p.ds_kg - (rb - p.ds_rel)
                               : ds_rows_before(rb, (sb.lk + 31) >> 5, p.ds_tri != 0));
     }
+    // the wave's groups [gA, gB) are blocks blk0 + gA .. blk0 + gB - 1
+    HSTU_DCHECK(gA >= gB || (blk0 + gA >= 0 && blk0 + gB <= (int64_t)p.heads * p.ds_head), kDbgDs);
+    HSTU_DCHECK(t1 == t0 || kv_end <= sb.lk, kDbgTile);
     const uint16_t* dsg = static_cast<const uint16_t*>(uniform_ptr(p.ds + blk0 * kDsBlockElems));
     const uint32_t cpy_off = 16u * (uint32_t)lane;
     auto copy_ds = [&](int t) {
@@ -1096,6 +1120,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(AttnParams p) {
     }
 
     if (my_row < sb.lq) {
+        HSTU_DCHECK((int64_t)sb.q0 + my_row < p.total_q, kDbgRow);
         uint16_t* dst = p.dq.base + (int64_t)(sb.q0 + my_row) * p.dq.tok + (int64_t)h * p.dq.head;
         const float sc = p.out_scale;
 #pragma unroll
@@ -1180,6 +1205,10 @@ hipError_t launch_dir(const AttnParams& p, int head_dim, MaskKind mask, hipStrea
 }
 
 }  // namespace
+
+#ifdef HSTU_DEBUG
+hipError_t debug_take_bwd(uint32_t* out) { return dbg_take(out); }
+#endif
 
 hipError_t launch_bwd_dq(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
     return launch_dir<false>(p, head_dim, mask, stream);

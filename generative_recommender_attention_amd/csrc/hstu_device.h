@@ -33,6 +33,46 @@
 
 namespace hstu {
 
+// ---- debug builds ----------------------------------------------------------------
+// Built with -DHSTU_DEBUG, the kernels test the global indices they form -- each
+// sequence's token range against the totals, the head, the rows of every tile copy,
+// load and store, the mask endpoint rows, the stored-dS blocks, the fused dQ
+// accumulator's index, the LMSD rows -- and a failed test sets its site's bit in a
+// device word that each kernel file keeps (dbg_take reads and clears it on the host).
+// A failed test neither skips the access nor stops the kernel: a trap would end the
+// process on the GPU with no report of where.  Release builds compile the tests out.
+enum DebugSite : uint32_t {
+    kDbgSeq = 1u << 0,   // a sequence's tokens outside [0, total) (cu_seqlens)
+    kDbgHead = 1u << 1,  // a head index outside [0, H)
+    kDbgRow = 1u << 2,   // a load or store row outside its sequence or the tensor
+    kDbgTile = 1u << 3,  // a tile copy from a first row at or past its valid rows, or past the sequence
+    kDbgFunc = 1u << 4,  // an endpoint row outside [0, func_ld)
+    kDbgDs = 1u << 5,    // a stored-dS block outside the workspace
+    kDbgAcc = 1u << 6,   // a fused-dQ accumulator index outside T_q H D
+    kDbgLmsd = 1u << 7,  // an LMSD row or partial row outside its buffer
+};
+#ifdef HSTU_DEBUG
+static __device__ uint32_t dbg_word;
+__device__ __forceinline__ void dbg_fail(uint32_t site) {
+    __hip_atomic_fetch_or(&dbg_word, site, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#define HSTU_DCHECK(cond, site)                   \
+    do {                                          \
+        if (!(cond)) ::hstu::dbg_fail(site);      \
+    } while (0)
+// This file's word, then 0 (the caller has synchronised the device).
+static inline hipError_t dbg_take(uint32_t* out) {
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(dbg_word), sizeof(uint32_t));
+    const uint32_t zero = 0;
+    if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &zero, sizeof(uint32_t));
+    return e;
+}
+#else
+#define HSTU_DCHECK(cond, site) \
+    do {                        \
+    } while (0)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -195,6 +235,7 @@ struct TileDma {
     // token strides up to 2^24 elements.
     __device__ __forceinline__ void issue(uint32_t tile, const uint16_t* base, int64_t tok, int row0,
                                           int valid_end) const {
+        HSTU_DCHECK(row0 >= 0 && row0 < valid_end, kDbgTile);
         const uint16_t* src = base + (int64_t)row0 * tok;
         const uint32_t dst = tile + (uint32_t)(wave * CPW) * 1024u;
         const int last = row0 + kTileRows <= valid_end ? kTileRows - 1 : valid_end - 1 - row0;
@@ -442,12 +483,14 @@ __device__ __forceinline__ uint32_t span_bits32(int a, int b, int n0) {
 // sequence with lk keys, for endpoints f[n * ld + row], n < N (N odd):
 // [0, F0) u [F1, F2) u ... , cut to [0, lk).
 __device__ __forceinline__ uint64_t func_bits64(const int32_t* f, int ld, int N, int row, int n0, int lk) {
+    HSTU_DCHECK(row >= 0 && row < ld, kDbgFunc);
     uint64_t m = span_bits64(0, f[row], n0);
     for (int n = 1; n + 1 < N; n += 2)
         m |= span_bits64(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
     return m & span_bits64(0, lk, n0);
 }
 __device__ __forceinline__ uint32_t func_bits32(const int32_t* f, int ld, int N, int row, int n0, int lk) {
+    HSTU_DCHECK(row >= 0 && row < ld, kDbgFunc);
     uint32_t m = span_bits32(0, f[row], n0);
     for (int n = 1; n + 1 < N; n += 2)
         m |= span_bits32(f[(int64_t)n * ld + row], f[(int64_t)(n + 1) * ld + row], n0);
@@ -458,6 +501,7 @@ __device__ __forceinline__ uint32_t func_bits32(const int32_t* f, int ld, int N,
 // when N > 1): only endpoints past the third are read from memory.
 __device__ __forceinline__ uint64_t func_bits64_pre(int f0, int f1, int f2, const int32_t* f, int ld, int N, int row,
                                                     int n0, int lk) {
+    HSTU_DCHECK(N <= 3 || (row >= 0 && row < ld), kDbgFunc);
     uint64_t m = span_bits64(0, f0, n0);
     if (N > 1) m |= span_bits64(f1, f2, n0);
     for (int n = 3; n + 1 < N; n += 2)
@@ -466,6 +510,7 @@ __device__ __forceinline__ uint64_t func_bits64_pre(int f0, int f1, int f2, cons
 }
 __device__ __forceinline__ uint32_t func_bits32_pre(int f0, int f1, int f2, const int32_t* f, int ld, int N, int row,
                                                     int n0, int lk) {
+    HSTU_DCHECK(N <= 3 || (row >= 0 && row < ld), kDbgFunc);
     uint32_t m = span_bits32(0, f0, n0);
     if (N > 1) m |= span_bits32(f1, f2, n0);
     for (int n = 3; n + 1 < N; n += 2)
@@ -475,6 +520,7 @@ __device__ __forceinline__ uint32_t func_bits32_pre(int f0, int f1, int f2, cons
 
 // Smallest and one past the largest visible key of row `row` (lo >= hi: none).
 __device__ __forceinline__ void func_key_range(const int32_t* f, int ld, int N, int row, int lk, int& lo, int& hi) {
+    HSTU_DCHECK(row >= 0 && row < ld, kDbgFunc);
     lo = 0x7fffffff;
     hi = 0;
     auto add = [&](int a, int b) {
@@ -492,6 +538,7 @@ __device__ __forceinline__ void func_key_range(const int32_t* f, int ld, int N, 
 // func_key_range with the row's first three endpoints already in registers.
 __device__ __forceinline__ void func_key_range_pre(int f0, int f1, int f2, const int32_t* f, int ld, int N, int row,
                                                    int lk, int& lo, int& hi) {
+    HSTU_DCHECK(N <= 3 || (row >= 0 && row < ld), kDbgFunc);
     lo = 0x7fffffff;
     hi = 0;
     auto add = [&](int a, int b) {
@@ -509,6 +556,7 @@ __device__ __forceinline__ void func_key_range_pre(int f0, int f1, int f2, const
 
 // Whether row `row` sees any key of [k0, k1) (0 <= k0, k1 <= lk).
 __device__ __forceinline__ bool func_row_meets(const int32_t* f, int ld, int N, int row, int k0, int k1) {
+    HSTU_DCHECK(row >= 0 && row < ld, kDbgFunc);
     bool hit = min(f[row], k1) > k0;
     for (int n = 1; n + 1 < N; n += 2)
         hit |= min(f[(int64_t)(n + 1) * ld + row], k1) > max(f[(int64_t)n * ld + row], k0);

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
         return;
     const int b = item.b, m = item.m;
     const SeqBounds sb = seq_bounds(p.cu_q, p.cu_k, b);
+    dbg_seq(p, sb, h);
     const int m0 = m * BM;
     const int row0 = m0 + 32 * wave;  // first row of this wave
     const int my_row = row0 + l32;
@@ -186,6 +187,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
         int rlo = 0x7fffffff, rhi = 0;
         if (my_row < sb.lq) func_key_range(p.func, p.func_ld, p.func_n, sb.q0 + my_row, sb.lk, rlo, rhi);
         const int frow = sb.q0 + min(my_row, sb.lq - 1);
+        HSTU_DCHECK(frow >= 0 && frow < p.func_ld, kDbgFunc);
         f0 = p.func[frow];
         if (p.func_n > 1) {
             f1 = p.func[(int64_t)p.func_ld + frow];
@@ -207,10 +209,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     }
     const int t0 = kv_end > kv_begin ? kv_begin / BN : 0;
     const int ntiles = kv_end > kv_begin ? (kv_end + BN - 1) / BN - t0 : 0;
+    HSTU_DCHECK(ntiles == 0 || (kv_begin >= 0 && kv_end <= sb.lk), kDbgTile);
 
     uint4 qf[KSTEPS];
     {
         const int r = min(my_row, sb.lq - 1);
+        HSTU_DCHECK(r >= 0 && r < sb.lq, kDbgRow);
         const uint16_t* src = p.q.base + (int64_t)(sb.q0 + r) * p.q.tok + (int64_t)h * p.q.head + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = ld_global16(src + 16 * kk);
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnParams p) {
     }
 
     if (my_row >= sb.lq) return;
+    HSTU_DCHECK((int64_t)sb.q0 + my_row < p.total_q, kDbgRow);
     uint16_t* dst = p.o.base + (int64_t)(sb.q0 + my_row) * p.o.tok + (int64_t)h * p.o.head;
     const float sc = p.out_scale;
 #pragma unroll
@@ -345,6 +350,10 @@ hipError_t launch_d(const AttnParams& p, MaskKind mask, hipStream_t stream) {
 }
 
 }  // namespace
+
+#ifdef HSTU_DEBUG
+hipError_t debug_take_fwd(uint32_t* out) { return dbg_take(out); }
+#endif
 
 hipError_t launch_fwd(const AttnParams& p, int head_dim, MaskKind mask, hipStream_t stream) {
     switch (head_dim) {

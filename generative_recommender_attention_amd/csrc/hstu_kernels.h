@@ -22,6 +22,8 @@ struct AttnParams {
     const int32_t* cu_k;   // (B + 1) cumulative key lengths, device
     int32_t batch;         // B
     int32_t heads;         // H
+    int32_t total_q;       // T_q, T_k: the token rows of the tensors (bounds tests of debug builds)
+    int32_t total_k;
     int32_t nblk;          // row (or key) blocks of the longest sequence
     int32_t items;         // bound on the live blocks: min(nblk B, (T + (block - 1) B) / block);
                            // the grid holds items x heads workgroups
@@ -60,6 +62,17 @@ struct AttnParams {
     float* dq_acc;
 };
 
+// Debug builds: sequence b's token ranges against the totals, and the head.
+__device__ __forceinline__ void dbg_seq(const AttnParams& p, const SeqBounds& sb, int h) {
+    HSTU_DCHECK(sb.q0 >= 0 && sb.lq >= 0 && (int64_t)sb.q0 + sb.lq <= p.total_q && sb.k0 >= 0 && sb.lk >= 0 &&
+                    (int64_t)sb.k0 + sb.lk <= p.total_k,
+                kDbgSeq);
+    HSTU_DCHECK(h >= 0 && h < p.heads, kDbgHead);
+    (void)p;
+    (void)sb;
+    (void)h;
+}
+
 // Elements of one stored dS block (32 x 32 bf16, 2 KB) and of one of its rows.
 constexpr int kDsBlockElems = 32 * 32;
 constexpr int kDsRowElems = 32;
@@ -92,5 +105,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_dq_convert(const AttnParams& p, int head_dim, int64_t rows, hipStream_t stream);
 // `count` one-wave workgroups, each writing {realtime, shader cycles, XCC id, HW_ID}.
 hipError_t launch_clock_sample(uint64_t* out, int count, hipStream_t stream);
+#ifdef HSTU_DEBUG
+// Debug builds: each kernel file's failed-bounds-test word (DebugSite bits), then 0.
+hipError_t debug_take_fwd(uint32_t* out);
+hipError_t debug_take_bwd(uint32_t* out);
+hipError_t debug_take_lmsd(uint32_t* out);
+#endif
 
 }  // namespace hstu

@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void lmsd_fwd_kernel(LmsdParams p) {
     const int64_t row = wave * RPW + lane / LPR;
     const bool live = row < p.n;
     const int64_t r = live ? row : p.n - 1;  // dead lanes recompute the last row and store nothing
+    HSTU_DCHECK(r >= 0 && r < p.n, kDbgLmsd);
     const int nvec = p.d / 8;
 
     float x[VPL][8], u[VPL][8];
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(256) void lmsd_bwd_kernel(LmsdParams p) {
         const int64_t row = grp * RPW + lane / LPR;
         const bool live = row < p.n;
         const int64_t r = live ? row : p.n - 1;
+        HSTU_DCHECK(r >= 0 && r < p.n, kDbgLmsd);
         const float mean = p.mean[r], rstd = p.rstd[r];
         const uint16_t* dyr = p.dy + r * p.dy_stride;
         float xh[VPL][8], a[VPL][8], g[VPL][8], dxh[VPL][8], uu[VPL][8];
@@ -335,6 +337,10 @@ int lmsd_bwd_parts(int64_t n, int d) {
 }
 
 hipError_t launch_lmsd_fwd(const LmsdParams& p, hipStream_t stream) { return launch(p, false, 0, stream); }
+
+#ifdef HSTU_DEBUG
+hipError_t debug_take_lmsd(uint32_t* out) { return dbg_take(out); }
+#endif
 
 // parts = 0 (no rows) runs the column sums alone, which then write zeros.
 hipError_t launch_lmsd_bwd(const LmsdParams& p, int parts, hipStream_t stream) { return launch(p, true, parts, stream); }

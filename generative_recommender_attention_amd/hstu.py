@@ -30,6 +30,8 @@ __all__ = [
     "HstuStride",
     "library",
     "library_path",
+    "select_library",
+    "debug_take",
     "hstu_fwd",
     "hstu_bwd",
     "hstu_bwd_workspace_size",
@@ -62,15 +64,28 @@ HSTU_MASK_NONE = 0
 HSTU_MASK_CAUSAL = 1
 HSTU_MASK_WINDOW = 2
 HSTU_MASK_FUNC = 3
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lock = threading.Lock()
-_lib = None
+_libs = {}
+# The debug build (bounds tests on the kernels' global indices, read back with
+# debug_take) is selected by HSTU_DEBUG=1 in the environment or select_library().
+_debug = os.environ.get("HSTU_DEBUG", "") == "1"
 
 
-def library_path() -> str:
-    return os.path.join(_PKG, "libhstu.so")
+def library_path(debug: Optional[bool] = None) -> str:
+    d = _debug if debug is None else debug
+    return os.path.join(_PKG, "libhstu_debug.so" if d else "libhstu.so")
+
+
+def select_library(debug: bool) -> bool:
+    """Route the calls of this module to the debug build (True) or the release
+    build (False); each is loaded on first use and stays loaded.  Returns the
+    previous choice."""
+    global _debug
+    prev, _debug = _debug, bool(debug)
+    return prev
 
 
 class HstuStride(ctypes.Structure):
@@ -138,15 +153,16 @@ def _status_name(s: int) -> str:
             3: "HSTU_ERR_DEVICE"}.get(s, f"status {s}")
 
 
-def library() -> ctypes.CDLL:
-    """Load ``libhstu.so`` (built in-tree); raise if it is missing."""
-    global _lib
+def library(debug: Optional[bool] = None) -> ctypes.CDLL:
+    """Load ``libhstu.so`` (or, for the debug build, ``libhstu_debug.so``; both built
+    in-tree); raise if it is missing."""
+    d = _debug if debug is None else bool(debug)
     with _lock:
-        if _lib is None:
-            path = library_path()
+        if d not in _libs:
+            path = library_path(d)
             if not os.path.exists(path):
                 raise RuntimeError(
-                    f"libhstu.so not found at {path}; build it with "
+                    f"{os.path.basename(path)} not found at {path}; build it with "
                     "`python -m generative_recommender_attention_amd.build` (there is no fallback)")
             lib = ctypes.CDLL(path)
             vp = ctypes.c_void_p
@@ -180,6 +196,8 @@ def library() -> ctypes.CDLL:
             lib.hstu_lmsd_bwd_noalloc.argtypes = [largp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.hstu_clock_sample.restype = ctypes.c_int
             lib.hstu_clock_sample.argtypes = [vp, ctypes.c_int32, vp]
+            lib.hstu_debug_take.restype = ctypes.c_int
+            lib.hstu_debug_take.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
             lib.hstu_last_error.restype = ctypes.c_char_p
             lib.hstu_last_error.argtypes = []
             lib.hstu_status_string.restype = ctypes.c_char_p
@@ -188,8 +206,8 @@ def library() -> ctypes.CDLL:
             lib.hstu_abi_version.argtypes = []
             if lib.hstu_abi_version() != ABI_VERSION:
                 raise RuntimeError(f"libhstu ABI {lib.hstu_abi_version()} != binding ABI {ABI_VERSION}")
-            _lib = lib
-        return _lib
+            _libs[d] = lib
+        return _libs[d]
 
 
 def _check(status: int) -> None:
@@ -639,3 +657,19 @@ def clock_sample(count: int = 64, device=None, stream=None) -> torch.Tensor:
         out = torch.empty((int(count), 4), dtype=torch.int64, device=device)
         _check(library().hstu_clock_sample(out.data_ptr(), int(count), _stream(s)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Debug builds: failed bounds tests of the kernels' global indices
+# ---------------------------------------------------------------------------
+DEBUG_SITES = {0: "sequence bounds", 1: "head", 2: "load/store row", 3: "tile copy rows", 4: "endpoint row",
+               5: "stored-dS block", 6: "fused dQ accumulator", 7: "LMSD row"}
+
+
+def debug_take() -> int:
+    """Bits of the bounds-test sites that failed in the debug build since the last
+    call (DEBUG_SITES names them), which are then cleared; synchronises the device.
+    Raises NotImplementedError on the release build."""
+    out = ctypes.c_uint32(0)
+    _check(library().hstu_debug_take(ctypes.byref(out)))
+    return int(out.value)

@@ -107,7 +107,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 6
+#define HSTU_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define HSTU_API __attribute__((visibility("default")))
@@ -343,6 +343,20 @@ HSTU_API hstu_status_t hstu_lmsd_bwd_noalloc(const hstu_lmsd_args_t* args, const
                                     const void* u, const void* weight, const void* bias, const float* mean,
                                     const float* rstd, void* dx, void* du, void* dweight, void* dbias,
                                     hipStream_t stream);
+
+/* ==========================================================================
+ * Debug builds (libhstu_debug.so, compiled with -DHSTU_DEBUG): the kernels test
+ * every global index they form -- each sequence's token range against T_q and
+ * T_k, the head, the rows of each tile copy, load and store, the mask endpoint
+ * rows, the stored-dS blocks, the fused dQ accumulator's index, the LMSD rows --
+ * and record a failed test as a bit per site (bit 0 sequence bounds, 1 head,
+ * 2 load/store row, 3 tile copy rows, 4 endpoint row, 5 stored-dS block,
+ * 6 fused-dQ accumulator, 7 LMSD row).  A failed test does not stop the access.
+ * hstu_debug_take synchronises the current device, writes the bits recorded
+ * since the last call to *sites and clears them.  Release builds write 0 and
+ * return HSTU_ERR_UNSUPPORTED.  Not for use while other threads launch work.
+ * ========================================================================== */
+HSTU_API hstu_status_t hstu_debug_take(uint32_t* sites);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 HSTU_API const char* hstu_last_error(void);

@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted([
         "hstu_abi_version", "hstu_bwd", "hstu_bwd_dkdv", "hstu_bwd_dkdv_ds", "hstu_bwd_dq", "hstu_bwd_dq_ds",
-        "hstu_bwd_fused", "hstu_bwd_fused_workspace_size", "hstu_bwd_workspace_size", "hstu_clock_sample", "hstu_fwd",
+        "hstu_bwd_fused", "hstu_bwd_fused_workspace_size", "hstu_bwd_workspace_size", "hstu_clock_sample",
+        "hstu_debug_take", "hstu_fwd",
         "hstu_last_error", "hstu_lmsd_bwd", "hstu_lmsd_bwd_noalloc", "hstu_lmsd_bwd_workspace_size", "hstu_lmsd_fwd",
         "hstu_status_string"])
 
@@ -296,10 +297,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """No fallback: with the library missing, the binding raises instead of computing."""
     import torch
 
-    monkeypatch.setattr(hstu, "_lib", None)
-    monkeypatch.setattr(hstu, "library_path", lambda: str(tmp_path / "libhstu.so"))
+    monkeypatch.setattr(hstu, "_libs", {})
+    monkeypatch.setattr(hstu, "library_path", lambda debug=None: str(tmp_path / "libhstu.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         hstu.library()
+    with pytest.raises(RuntimeError, match="no fallback"):
+        hstu.library(debug=True)
     q = torch.zeros(4, 1, 16, dtype=torch.bfloat16)
     with pytest.raises((RuntimeError, ValueError)):
         hstu.hstu_fwd(q, q, q, torch.tensor([0, 4], dtype=torch.int32), torch.tensor([0, 4], dtype=torch.int32), 4, 4)
@@ -314,3 +317,21 @@ def test_product_path_does_not_import_the_oracle():
         text = path.read_text(errors="replace")
         assert "import oracle" not in text and "from oracle" not in text, path
         assert "hstu_oracle" not in text and "lmsd_oracle" not in text, path
+
+
+def test_debug_take_on_the_release_build(lib):
+    assert lib.hstu_debug_take(None) == hstu.HSTU_ERR_INVALID_ARGUMENT
+    out = ctypes.c_uint32(7)
+    assert lib.hstu_debug_take(ctypes.byref(out)) == hstu.HSTU_ERR_UNSUPPORTED
+    assert out.value == 0 and b"debug build" in lib.hstu_last_error()
+
+
+def test_debug_build_exports_the_same_abi():
+    path = hstu.library_path(debug=True)
+    if not os.path.exists(path):
+        pytest.skip("libhstu_debug.so is not built")
+    dlib = hstu.library(debug=True)
+    for name in declared_symbols():
+        assert hasattr(dlib, name), name
+    assert dlib.hstu_abi_version() == hstu.ABI_VERSION
+    assert dlib.hstu_debug_take(None) == hstu.HSTU_ERR_INVALID_ARGUMENT
