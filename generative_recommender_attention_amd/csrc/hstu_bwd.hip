@@ -1,7 +1,9 @@
-// HSTU attention backward on gfx950: deterministic kernels, no atomics.  Two
-// routes: a dq kernel and a dk/dv kernel that both recompute the scores (no
-// workspace), or -- given a workspace --
-// the dk/dv kernel storing dS and a dq kernel that reads it (described last).
+// HSTU attention backward on gfx950.  Three routes: a dq kernel and a dk/dv kernel
+// that both recompute the scores (no workspace); given a workspace, the dk/dv
+// kernel storing dS and a dq kernel that reads it (described last) -- both of
+// these deterministic, with no atomics; and the fused backward, one dk/dv pass
+// that also adds each query tile's dQ into an fp32 accumulator with atomics (the
+// HSTU page's form for D <= 128, whose dQ summation order is not fixed).
 //
 // The backward receives dO and q, k, v only (HSTU Attention page, "High-level
 // functions"), so both kernels recompute the scores.  With s = alpha q_i.k_j,
