@@ -85,10 +85,13 @@
  * -- Execution ------------------------------------------------------------------
  *   Each call validates, enqueues its kernels on `stream` (0 = the null stream)
  *   and returns; results are ready when the stream reaches that point.  Calls
- *   are thread-safe and keep no state between them, so they can be captured in
+ *   are thread-safe and keep no state between them (two exceptions, stated
+ *   where they are declared: hstu_lmsd_bwd_noalloc's per-GPU array, and the
+ *   debug build's record of failed bounds tests), so they can be captured in
  *   a HIP graph.  An asynchronous device fault shows up at the caller's next
- *   synchronisation, not in the returned status.  Both backward kernels are
- *   deterministic: the same inputs give bit-identical gradients.
+ *   synchronisation, not in the returned status.  hstu_bwd, on either route,
+ *   and its parts are deterministic: the same inputs give bit-identical
+ *   gradients; hstu_bwd_fused's dQ is added with atomics in arrival order.
  *
  * -- Errors -----------------------------------------------------------------------
  *   Every entry point returns an hstu_status_t; on failure nothing has been
