@@ -202,6 +202,19 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
                 f"mask {wl.mask_name}, bf16, seeded synthetic inputs; one bench step = hstu_fwd + " +
                 ("hstu_bwd_dkdv_ds (bwd_dkdv_kernel storing dS) + hstu_bwd_dq_ds." if stored else
                  "hstu_bwd_dq + hstu_bwd_dkdv."))
+    # a run of the fused backward (bench.py --fused-bwd) gets its own summary file
+    suffix, kt_cmd = "", PROFILE_COMMANDS["kt"].format(d=prof_dir, w=workload)
+    bpath0 = os.path.join(prof_dir, "kt", "bench.json")
+    if os.path.exists(bpath0):
+        with open(bpath0) as f:
+            backward = (json.loads(f.readline()).get("config") or {}).get("backward") or ""
+        if backward.startswith("fused"):
+            suffix, kt_cmd = "_fused", kt_cmd + " --fused-bwd"
+            title = "HSTU attention fwd + fused bwd"
+            what = what.split("one bench step")[0] + ("one bench step = hstu_fwd + hstu_bwd_fused (fill_zero_kernel, "
+                                                      "bwd_dkdv_kernel with the fp32-atomic dQ phase, "
+                                                      "dq_convert_kernel).")
+            kernels = kernels + ["fill_zero_kernel", "dq_convert_kernel"]
     stats = rows("kt", "*kernel_stats.csv")
     clock_note = []
     cpath = os.path.join(prof_dir, "kt", "clock.json")
@@ -213,7 +226,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
                       "and after them.", ""]
     out = [f"# rocprofv3 kernel trace: {title}, workload {workload}", "", what, "",
            "Command (GPU box, from the repository root):",
-           "    " + PROFILE_COMMANDS["kt"].format(d=prof_dir, w=workload), ""] + clock_note + [
+           "    " + kt_cmd, ""] + clock_note + [
            f"{'kernel':26s}{'calls':>8s}{'avg ns':>11s}{'min ns':>11s}{'max ns':>11s}{'share':>8s}"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"]
@@ -240,8 +253,11 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
                           f"{rl['alg_flops_per_launch'] / (tr * 1e-9) / 1e12:.1f} TFLOP/s = frac "
                           f"{rl['alg_flops_per_launch'] / (tr * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f} from the trace"
                           if tr else "(kernel not in the trace)"))
-    with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}_kernel_trace.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"hstu_kernels_{workload}{suffix}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(out) + "\n")
+    if suffix:
+        print(f"wrote the kernel-trace summary for {workload}{suffix}")
+        return
     if os.path.isdir(os.path.join(prof_dir, "mfma")) and not workload.startswith("lmsd_"):
         avg_ns = {k: float(r["AverageNs"]) for r in stats for k in kernels if k in r["Name"]}
         ctr = {}
@@ -706,7 +722,9 @@ def main(argv=None) -> int:
     dominant = max(per_kernel_ms, key=per_kernel_ms.get)
     alg_flops = FLOPS_PER_PAIR_D[dominant] * unit_pd
     achieved = alg_flops / (per_kernel_ms[dominant] * 1e-3) / 1e12
-    traffic = load_traffic(KERNEL_SYMBOL[dominant], wl.name)
+    # the PMC counters behind profiles/traffic.json were taken on the default (stored-dS) route; the dk/dv
+    # kernel of the other routes runs in another mode, so they report no traffic
+    traffic = load_traffic(KERNEL_SYMBOL[dominant], wl.name) if stored or dominant == "fwd" else None
 
     detail = {}
     for name in kernels:
