@@ -2,9 +2,12 @@
 of 256, H = 16, D = 128, so every (T, H, D) tensor holds 2^32 bf16 elements (8 GiB)
 and the kernels form element offsets up to 2^32 and byte offsets up to 8 GiB
 (32-bit offset arithmetic anywhere would show here).  The forward and the
-stored-dS backward run on the whole tensors (~75 GiB of device memory in all);
-sequences at the start, middle and end of the buffers are compared with the fp64
-oracle, each as its own problem, to the bar of tests/hip_cases.py.
+stored-dS backward run on the whole tensors, then the fused backward (its fp32 dQ
+accumulator holds 16 GiB; its dK and dV must equal the stored route's bit for bit
+over the whole tensors) and a forward under a token window (64, 0) -- ~120 GiB of
+device memory in all.  Sequences at the start, middle and end of the buffers are
+compared with the fp64 oracle, each as its own problem, to the bar of
+tests/hip_cases.py.
 
 Inputs are drawn on the device by torch's seeded generator (bf16 normals times 0.5,
 an exact scaling); the oracle reads the same bits, copied back per sequence."""
@@ -22,7 +25,7 @@ from hip_cases import check_close, say, to_f64
 pytestmark = pytest.mark.gpu
 
 T, B, L, H, D = 1 << 21, 8192, 256, 16, 128
-NEED_BYTES = 100 << 30  # inputs, outputs, workspace and headroom
+NEED_BYTES = 140 << 30  # inputs, outputs, workspaces and headroom
 SAMPLED = [0, 1, B // 2, B - 2, B - 1]
 
 
@@ -52,6 +55,14 @@ def test_tensors_past_4gib_fwd_bwd(oracle_lib):
     dq, dk, dv = hstu.hstu_bwd(do, q, k, v, cu, cu, workspace=ws, **kw)
     torch.cuda.synchronize()
     del ws
+    say("large tensors: hstu_bwd_fused")
+    fdq, fdk, fdv = hstu.hstu_bwd_fused(do, q, k, v, cu, cu, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(fdk, dk) and torch.equal(fdv, dv)  # the same pass computes them
+    del fdk, fdv
+    say("large tensors: hstu_fwd under the window (64, 0)")
+    ow = hstu.hstu_fwd(q, k, v, cu, cu, **dict(kw, causal=False), window_size=(64, 0))
+    torch.cuda.synchronize()
 
     cu1 = np.array([0, L], dtype=np.int32)
     bits = lambda t, r0: t[r0:r0 + L].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -62,5 +73,7 @@ def test_tensors_past_4gib_fwd_bwd(oracle_lib):
         ro = oracle_lib.fwd(cu1, cu1, qs, ks, vs, alpha, L, (-1, 0))
         rq = oracle_lib.bwd_dq(cu1, cu1, dos, qs, ks, vs, alpha, L, (-1, 0))
         rk, rv = oracle_lib.bwd_dkdv(cu1, cu1, dos, qs, ks, vs, alpha, L, (-1, 0))
-        for name, got, ref in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        rw = oracle_lib.fwd(cu1, cu1, qs, ks, vs, alpha, L, (64, 0))
+        for name, got, ref in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv),
+                               ("fused dQ", fdq, rq), ("window O", ow, rw)):
             check_close(f"{name} of sequence {b}", to_f64(got[r0:r0 + L]), ref, cu1)
