@@ -646,3 +646,32 @@ def test_dq_ds_long_walks(oracle_lib, case):
     dq3 = dw.bwd()[0]  # a whole backward on a fresh workspace
     torch.cuda.synchronize()
     assert torch.equal(dq1, dq2) and torch.equal(dq1, dq3)
+
+
+# ------------------------------------------------------------------ closed forms at full size
+def test_closed_forms_on_the_zipf_workload(oracle_lib):
+    """Properties the method fixes at any size (HSTU page, "Overview" equations), on the
+    Zipf forward + backward workload's shapes: with Q = 0 every score is 0 and
+    SiLU(0) = 0, so O, dK and dV are exactly 0 on both backward routes, while dQ =
+    alpha SiLU'(0) / L_s sum_j (dO_i . v_j) k_j (SiLU'(0) = 1/2) meets the bar against
+    the oracle; with V = 1 every column of O is the same masked SiLU row sum, so all
+    columns of O are bit-identical."""
+    wl = named_workload("zipf_b32_h4_d128_causal_fwdbwd")
+    dw = DeviceWorkload(wl)
+    v1 = torch.ones_like(dw.v)
+    say("closed forms: Zipf workload with V = 1")
+    o1 = hstu.hstu_fwd(dw.q, dw.k, v1, dw.cu_q, dw.cu_k, **dw.kw())
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o1[:, :, :1].expand_as(o1))
+    dw.q.zero_()
+    say("closed forms: Zipf workload with Q = 0")
+    o = dw.fwd()
+    assert torch.all(o == 0)
+    zero_q = np.zeros_like(wl.q)
+    rq = oracle_lib.bwd_dq(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.do, zero_q, wl.k, wl.v, float(wl.alpha),
+                           wl.scaling_seqlen, wl.mask_spec)
+    for store in (True, False):
+        dq, dk, dv = dw.bwd(store_ds=store)
+        torch.cuda.synchronize()
+        assert torch.all(dk == 0) and torch.all(dv == 0), store
+        check_close(f"dQ with Q = 0 ({'stored dS' if store else 'recompute'})", to_f64(dq), rq, wl.cu_seqlens_q)
