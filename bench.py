@@ -133,14 +133,14 @@ def load_traffic(kernel: str, workload: str):
 
 PROFILE_COMMANDS = {
     "kt": ("rocprofv3 --kernel-trace --stats -T --output-format csv -d {d}/kt -o run -- python3 bench.py "
-           "--no-cpu-baseline --workload {w} --clock-out {d}/kt/clock.json --json-out {d}/kt/bench.json"),
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}",
+           "--no-cpu-baseline --no-reference-gemm --workload {w} --clock-out {d}/kt/clock.json --json-out {d}/kt/bench.json"),
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-reference-gemm --workload {w}",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-reference-gemm --workload {w}",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cfetch -o run -- python3 bench.py --calibrate-copy-mib 256",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cwrite -o run -- python3 bench.py --calibrate-copy-mib 256",
     "mfma": ("rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS "
              "SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv "
-             "-d {d}/mfma -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --workload {w}"),
+             "-d {d}/mfma -o run -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-reference-gemm --workload {w}"),
 }
 MFMA_FLOPS = 2 * 32 * 32 * 16  # one v_mfma_f32_32x32x16_bf16 (the only MFMA the attention kernels issue)
 ALG_TENSORS = {"fwd_kernel": 4, "bwd_dq_kernel": 5, "bwd_dkdv_kernel": 6}  # (T, H, D) bf16 tensors read + written
@@ -435,6 +435,43 @@ def cpu_model() -> str:
     return f"{name} ({ids})" if ids else name
 
 
+def reference_gemm(dev, stream, n: int = 8192, reps: int = 10) -> dict:
+    """What a plain dense bf16 GEMM reaches on this board, timed in the same process
+    after the attention steps: torch.mm (the ROCm BLAS library's kernel) on two
+    n x n N(0,1) bf16 matrices, with the shader clock over its timed launches.  A
+    context figure for the roofline (the chip runs near its board power limit under
+    matrix-core load, far below the 2.4 GHz the published peak assumes); it is not
+    part of the attention path."""
+    import torch
+
+    from generative_recommender_attention_amd import hstu
+
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clk0 = hstu.clock_sample(CLOCK_WGS, dev, stream)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record(stream)
+    clk1 = hstu.clock_sample(CLOCK_WGS, dev, stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    mhz = clock_summary(clk0.cpu().numpy(), clk1.cpu().numpy())["shader_mhz"]
+    print(f"[bench] reference GEMM: torch.mm bf16 {n}^3 {ms:.3f} ms = {tf:.1f} TFLOP/s at {mhz} MHz",
+          file=sys.stderr, flush=True)
+    return {"what": f"torch.mm bf16 {n}x{n}x{n}, N(0,1) operands (ROCm BLAS library kernel), "
+                    "same process, after the timed steps; not part of the attention path",
+            "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "shader_mhz": mhz}
+
+
 def clock_summary(before, after) -> dict:
     """Average shader clock between two clock_sample launches (rows of (real time at
     100 MHz, shader cycles, XCC id, HW_ID)).  The cycle counter is per compute unit
@@ -577,6 +614,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference-gemm", action="store_true",
+                    help="skip the plain bf16 GEMM timed after the steps as a context figure")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="time the backward route without stored dS (hstu_bwd_dq + hstu_bwd_dkdv)")
     ap.add_argument("--fused-bwd", action="store_true",
@@ -766,6 +805,12 @@ def main(argv=None) -> int:
                      "traffic": traffic, "alg_flops_per_launch": alg_flops,
                      "avg_launch_ms": round(per_kernel_ms[dominant], 5)},
     }
+    if not args.no_reference_gemm:
+        ref = reference_gemm(dev, stream)
+        ref["attention_step_frac"] = round(value / ref["tflops"], 4)
+        ref["fwd_frac"] = round(fwd_useful_tf / ref["tflops"], 4)
+        ref["dominant_kernel_frac"] = round(achieved / ref["tflops"], 4)
+        result["reference_gemm"] = ref
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_max_pairs)

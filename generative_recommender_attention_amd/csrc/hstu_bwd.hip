@@ -480,14 +480,17 @@ __device__ __forceinline__ void dkdv_block(bool mask, uint32_t qrow, uint32_t dr
             uint16_t* dst = ds.p + (l & 31) * kDsRowElems + 8 * (l >> 5);
             if (ds.kcut && ds.kdead) {
                 const u32x4 z = {0u, 0u, 0u, 0u};
-                __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst));
-                __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst + 16));
+                __builtin_nontemporal_store(z, (global_u32x4*)dst);
+                __builtin_nontemporal_store(z, (global_u32x4*)(dst + 16));
             } else {
                 const u32x4 v0 = {d[0].x, d[0].y, d[0].z, d[0].w}, v1 = {d[1].x, d[1].y, d[1].z, d[1].w};
-                __builtin_nontemporal_store(v0, reinterpret_cast<u32x4*>(dst));
-                __builtin_nontemporal_store(v1, reinterpret_cast<u32x4*>(dst + 16));
+                __builtin_nontemporal_store(v0, (global_u32x4*)dst);
+                __builtin_nontemporal_store(v1, (global_u32x4*)(dst + 16));
             }
         }
+        // keep the stores ahead of the dV / dK products, so that they drain while
+        // those run instead of in front of the tile's closing wait
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < NG; ++j) {

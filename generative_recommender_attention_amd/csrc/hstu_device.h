@@ -139,6 +139,11 @@ __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt
 // stay in registers.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+// The same vector in the global address space: stores through it compile to
+// global_store (counted by vmcnt only), where a generic pointer gives flat_store,
+// which also counts in lgkmcnt and so holds up every later wait on LDS reads until
+// the store has reached memory.
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
 
