@@ -435,7 +435,55 @@ def cpu_model() -> str:
     return f"{name} ({ids})" if ids else name
 
 
-def reference_gemm(dev, stream, n: int = 8192, reps: int = 10) -> dict:
+def board_power(fn, seconds: float, device_index: int = 0) -> dict:
+    """Run fn() back to back for about `seconds` while another thread polls
+    `amd-smi metric -p -c` (socket power and the GFX clock the firmware reports);
+    returns the median of the samples taken after the first second (the readings
+    lag the load by up to ~1 s).  Measurement only."""
+    import subprocess
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            t = time.perf_counter()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", str(device_index), "--json"],
+                                   capture_output=True, text=True, timeout=20)
+                d = json.loads(r.stdout)
+                g = d[0] if isinstance(d, list) else d.get("gpu_data", [d])[0]
+                pw = g["power"]["socket_power"]["value"]
+                clk = g["clock"]["gfx_0"]["clk"]["value"]
+                samples.append((t, float(pw), float(clk)))
+            except Exception:  # tool missing or output changed: no sample
+                if stop.wait(0.5):
+                    break
+
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stop.set()
+    th.join(timeout=30)
+    use = [(p, c) for t, p, c in samples if t0 + 1.0 <= t <= t1]
+    if not use:
+        return {"samples": 0, "launches": n, "seconds": round(t1 - t0, 2)}
+    return {"socket_w": float(np.median([p for p, _ in use])), "gfx_mhz": float(np.median([c for _, c in use])),
+            "samples": len(use), "launches": n, "seconds": round(t1 - t0, 2)}
+
+
+def reference_gemm(dev, stream, n: int = 8192, reps: int = 10, power_seconds: float = 0.0) -> dict:
     """What a plain dense bf16 GEMM reaches on this board, timed in the same process
     after the attention steps: torch.mm (the ROCm BLAS library's kernel) on two
     n x n N(0,1) bf16 matrices, with the shader clock over its timed launches.  A
@@ -466,10 +514,13 @@ def reference_gemm(dev, stream, n: int = 8192, reps: int = 10) -> dict:
     mhz = clock_summary(clk0.cpu().numpy(), clk1.cpu().numpy())["shader_mhz"]
     print(f"[bench] reference GEMM: torch.mm bf16 {n}^3 {ms:.3f} ms = {tf:.1f} TFLOP/s at {mhz} MHz",
           file=sys.stderr, flush=True)
-    return {"what": f"torch.mm bf16 {n}x{n}x{n}, N(0,1) operands (ROCm BLAS library kernel), "
-                    "same process, after the timed steps; not part of the attention path",
-            "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "shader_mhz": mhz}
+    out = {"what": f"torch.mm bf16 {n}x{n}x{n}, N(0,1) operands (ROCm BLAS library kernel), "
+                   "same process, after the timed steps; not part of the attention path",
+           "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "shader_mhz": mhz}
+    if power_seconds > 0:
+        out["board_power"] = board_power(lambda: torch.mm(a, b, out=c), power_seconds, dev.index or 0)
+    return out
 
 
 def clock_summary(before, after) -> dict:
@@ -628,6 +679,9 @@ def main(argv=None) -> int:
                     help="only write profiles/ from the rocprofv3 outputs under DIR (see PROFILE_COMMANDS)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC byte-counter calibration)")
+    ap.add_argument("--power-seconds", type=float, default=0.0,
+                    help="after the timed steps, loop the step (then the reference GEMM) this many seconds each "
+                         "while polling board power and clock with amd-smi; adds a 'board_power' object")
     ap.add_argument("--clock-out", metavar="PATH", help="also write the shader-clock reading to PATH (JSON)")
     ap.add_argument("--json-out", metavar="PATH", help="also write the JSON line to PATH")
     ap.add_argument("--oracle-configs", action="store_true",
@@ -805,8 +859,12 @@ def main(argv=None) -> int:
                      "traffic": traffic, "alg_flops_per_launch": alg_flops,
                      "avg_launch_ms": round(per_kernel_ms[dominant], 5)},
     }
+    if args.power_seconds > 0:
+        print(f"[bench] board power over {args.power_seconds} s of back-to-back steps", file=sys.stderr, flush=True)
+        result["board_power"] = board_power(step, args.power_seconds, dev.index or 0)
+        print(f"[bench] board power: {result['board_power']}", file=sys.stderr, flush=True)
     if not args.no_reference_gemm:
-        ref = reference_gemm(dev, stream)
+        ref = reference_gemm(dev, stream, power_seconds=args.power_seconds)
         ref["attention_step_frac"] = round(value / ref["tflops"], 4)
         ref["fwd_frac"] = round(fwd_useful_tf / ref["tflops"], 4)
         ref["dominant_kernel_frac"] = round(achieved / ref["tflops"], 4)
